@@ -1,0 +1,192 @@
+/*
+ * tls.h -- C ABI of the MI355X (gfx950) two-level sparse-attention decode
+ * library (libtls.so).
+ *
+ * The operation is one decode step of AsyncTLS two-level sparse attention
+ * (pages "AsyncTLS: Efficient Generative LLM Inference with Asynchronous
+ * Two-level Sparse Attention", section 2 "Methodology"):
+ *   stage 1 (section 2A, coarse block filtering): per-block key max/min
+ *     summaries scored with the Quest upper bound, evaluated as the GEMM
+ *     [q+, q-] . [Kmax; Kmin]; the top-Kb blocks are kept;
+ *   stage 2 (section 2A, fine token selection): inside the kept blocks, tokens
+ *     are scored on a few label channels of an INT4 key cache (Double-Sparsity
+ *     style); the top-Kt tokens are kept;
+ *   attention over only the kept tokens (section 2A);
+ *   staggered offload (section 2B): block selection for the next step
+ *     overlaps the current step, and only the blocks missing from the device
+ *     (T_t = M_t minus the resident set) are copied from pinned host memory.
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are passed as device pointers to 16-bit bf16 values.
+ *   - Every pointer argument is a device pointer unless stated otherwise.
+ *     All buffers belong to the caller; the library keeps no pointer after a
+ *     call returns, except the offload context (documented there).
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without synchronising. A fault inside a kernel surfaces at
+ *     the caller's next synchronisation, as usual for HIP.
+ *   - Return value: TLS_OK (0) or a negative TLS_ERR_* code; tls_last_error()
+ *     then returns a message for the calling thread. Argument errors are
+ *     detected before anything is enqueued.
+ *   - One selection is made per (batch b, kv head h) pair, shared by the
+ *     G = num_q_heads / num_kv_heads query heads g = h*G .. h*G+G-1; the heads
+ *     of a group are combined by taking the maximum of their scores.
+ *   - Index outputs are sets, written in ascending order. Ties in a top-k go to
+ *     the lower index.
+ *   - Workspaces: `ws` must be at least tls_workspace_size(shape, which) bytes
+ *     (256-byte aligned). Its contents on entry do not matter.
+ *
+ * Layouts (row-major)
+ *   q          [B, Hq, D]            bf16
+ *   kv         [B, Hkv, N, row]      bf16; row = D + DV (K then V) or, when
+ *                                    v_is_k_prefix, row = D and V[t] = K[t, 0:DV]
+ *   label_ch   [Hkv, r]              int32, ascending channel numbers
+ *   summ       [B, Hkv, NB, 2, D]    bf16; [.., 0, :] = Kmax, [.., 1, :] = Kmin
+ *   codes      [B, Hkv, N, r/2]      uint8; channel i in byte i/2, low nibble for
+ *                                    even i, two's-complement 4-bit code in [-7, 7]
+ *   scale      [B, Hkv, N]           float; dequantised key = code * scale
+ *   block_idx  [B, Hkv, Kb']         int32, Kb' = min(Kb, NB)
+ *   token_idx  [B, Hkv, Kt']         int32, Kt' = min(Kt, Kb' * bs); a pair with
+ *                                    fewer valid candidates (partial last block)
+ *                                    is padded with -1 after its ascending entries
+ *   out        [B, Hq, DV]           float
+ *   lse        [B, Hq]               float, natural-log log-sum-exp of the scaled
+ *                                    logits over the kept tokens
+ *   with NB = ceil(N / bs).
+ */
+#ifndef TLS_H
+#define TLS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TLS_OK = 0,
+  TLS_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape      */
+  TLS_ERR_UNSUPPORTED = -2, /* valid shape that no compiled kernel covers       */
+  TLS_ERR_WORKSPACE = -3,   /* workspace smaller than tls_workspace_size()      */
+  TLS_ERR_HIP = -4,         /* a HIP runtime call failed (message has the name) */
+  TLS_ERR_STATE = -5        /* offload context used out of order                */
+};
+
+enum { TLS_WS_BLOCKS = 0, TLS_WS_TOKENS = 1, TLS_WS_DECODE = 2 };
+
+typedef struct tls_shape {
+  int32_t batch;         /* B                                                    */
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads                       */
+  int32_t num_kv_heads;  /* Hkv                                                  */
+  int32_t head_dim_qk;   /* D: 128 (GQA/MHA) or 576 (MLA latent + rope); any     */
+                         /*    multiple of 32 up to 576                          */
+  int32_t head_dim_v;    /* DV: a multiple of 8, at most 512                     */
+  int32_t v_is_k_prefix; /* 1: no separate V, V[t] = K[t, 0:DV] (MLA)            */
+  int64_t ctx_len;       /* N: cached tokens of every sequence, >= 1             */
+  int32_t block_size;    /* bs: tokens per block, 1..64                          */
+  int32_t num_label_ch;  /* r: label channels, even, 2..32                       */
+  int32_t top_kb;        /* Kb >= 1; values above NB keep every block            */
+  int32_t top_kt;        /* Kt >= 1; values above Kb'*bs keep every candidate    */
+  float sm_scale;        /* softmax scale applied to q.k (e.g. 1/sqrt(D))        */
+} tls_shape_t;
+
+/* Bytes of workspace needed by tls_select_blocks (TLS_WS_BLOCKS),
+ * tls_select_tokens (TLS_WS_TOKENS) or tls_sparse_decode (TLS_WS_DECODE) for
+ * this shape; 0 if the shape is invalid. */
+size_t tls_workspace_size(const tls_shape_t *shape, int which);
+
+/* Block summaries and the INT4 label cache (section 2A: the block-level index
+ * and the token-level index; run once per cache, not per step).
+ *   kv [B,Hkv,N,row] -> summ [B,Hkv,NB,2,D], codes [B,Hkv,N,r/2], scale [B,Hkv,N].
+ * Kmax/Kmin are exact per-channel extremes over the valid tokens of a block.
+ * Label cache per token: a = max |K[t, c_i]| over the label channels; a == 0
+ * gives scale 0 and codes 0, otherwise scale = float(a/7) and
+ * code_i = clamp(rint(K[t,c_i] / scale), -7, 7), both divisions in double. */
+int tls_build_summaries(const tls_shape_t *shape, const void *kv, const int32_t *label_ch, void *summ,
+                        uint8_t *codes, float *scale, void *stream);
+
+/* Stage 1 (section 2A, coarse block filtering).
+ *   s[g, j] = sum_c max(q_gc Kmax_jc, q_gc Kmin_jc) = [q_g+, q_g-] . [Kmax_j; Kmin_j]
+ *   S[j] = max over the G heads of the pair;  block_idx = top-Kb' of S.
+ * block_score_opt: NULL, or [B,Hkv,NB] float receiving S. */
+int tls_select_blocks(const tls_shape_t *shape, const void *q, const void *summ, int32_t *block_idx,
+                      float *block_score_opt, void *ws, size_t ws_bytes, void *stream);
+
+/* Stage 2 (section 2A, fine token selection) inside the blocks of block_idx
+ * (ascending, Kb' per pair).
+ *   a[g, t] = scale_t * sum_i q[g, c_i] * code[t, i]  (q is not quantised)
+ *   A[t] = max over the G heads;  token_idx = top-Kt' of A over the valid
+ *   tokens (t < N) of the kept blocks. */
+int tls_select_tokens(const tls_shape_t *shape, const void *q, const int32_t *label_ch, const uint8_t *codes,
+                      const float *scale, const int32_t *block_idx, int32_t *token_idx, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Attention over the kept tokens only (section 2A), split over the token
+ * list and merged with log-sum-exp.
+ *   out[b, g] = sum_t softmax_t(sm_scale * q_g . K[t]) V[t] over t in token_idx
+ * kv_cache: with slot_map == NULL, the full cache [B,Hkv,N,row]. Otherwise a
+ *   resident cache [B,Hkv,slots_per_pair,bs,row] addressed through
+ *   slot_map [B,Hkv,NB] (int32 slot of each block, -1 = not resident); every
+ *   block holding a kept token must be resident.
+ * Entries -1 in token_idx are skipped. lse_opt: NULL or [B,Hq] float. */
+int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_cache, const int32_t *slot_map,
+                      int32_t slots_per_pair, const int32_t *token_idx, float *out, float *lse_opt, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Staggered offload (section 2B). The full cache stays in pinned host memory;
+ * the device holds a resident cache of 2*Kb' block slots per pair plus a slot
+ * map. At step t the token stage and the attention use the blocks chosen at
+ * step t-1, while stage 1 for step t runs on a side stream; then only the
+ * blocks of T_t = M_t \ C_t (C_t: resident blocks) are copied host -> device.
+ * When slots run out, resident blocks outside M_{t-1} and M_t are evicted,
+ * least recently selected first, lower block index first on equal steps.
+ */
+typedef struct tls_offload tls_offload_t;
+
+/* Create an offload context.
+ *   host_kv      [B,Hkv,N,row] bf16 in pinned host memory (hipHostMalloc),
+ *                borrowed until tls_offload_destroy; N must be a multiple of bs.
+ *   dev_cache    [B,Hkv,2*Kb',bs,row] bf16 device memory, borrowed.
+ *   dev_slot_map two device buffers of [B,Hkv,NB] int32 each, borrowed
+ *                (dev_slot_map[0] and dev_slot_map[1]); step t reads buffer t%2
+ *                and the prefetch of step t writes buffer (t+1)%2.
+ *   initial_blocks [B,Hkv,Kb'] int32 host array: M_{-1}, ascending. These
+ *                blocks are copied synchronously, slots assigned in order.
+ * On success *out receives the context. The call synchronises the device. */
+int tls_offload_create(const tls_shape_t *shape, const void *host_kv, void *dev_cache, int32_t *dev_slot_map0,
+                       int32_t *dev_slot_map1, const int32_t *initial_blocks, tls_offload_t **out);
+
+/* Slot map (device pointer) that step `step` must pass to tls_sparse_decode. */
+const int32_t *tls_offload_slot_map(const tls_offload_t *ctx, int32_t step);
+
+/* Incremental prefetch for step `step` (0, 1, 2, ... in order).
+ *   dev_block_idx  M_t [B,Hkv,Kb'] int32 device buffer written by
+ *                  tls_select_blocks on `side` (a hipStream_t) before this call.
+ * The call enqueues a copy of M_t to host on `side`, waits for it on the
+ * calling thread (the calling thread blocks; run it on a helper thread to keep
+ * the main stream busy), computes T_t and the evictions, enqueues one
+ * host->device copy per transferred block and the next slot map on `side`, and
+ * records `copies_done` (a hipEvent_t) on `side`. Step step+1 must wait for
+ * that event before reading the resident cache. n_copied_opt (host, may be
+ * NULL) receives |T_t| summed over all pairs. */
+int tls_prefetch_delta(tls_offload_t *ctx, int32_t step, const int32_t *dev_block_idx, void *side,
+                       void *copies_done, int64_t *n_copied_opt);
+
+/* Host view of the last transfer (for checking): per pair the count |T_t|
+ * and the transferred blocks ascending (host arrays [B*Hkv] and [B*Hkv, Kb']). */
+int tls_offload_last_delta(const tls_offload_t *ctx, int32_t *counts, int32_t *blocks);
+
+void tls_offload_destroy(tls_offload_t *ctx);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *tls_last_error(void);
+
+/* Library version string. */
+const char *tls_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLS_H */

@@ -1,0 +1,78 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/tls.h declares, sizes workspaces, and rejects bad arguments
+before touching the device."""
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+import two_level_sparse_amd as T
+import workload as W
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not T.LIB_PATH.exists():
+        from two_level_sparse_amd import build
+        build.build()
+    return T.load_library()
+
+
+def declared_functions():
+    hdr = (ROOT / "include" / "tls.h").read_text()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    return sorted(set(re.findall(r"\b(tls_[a-z_0-9]+)\s*\(", hdr)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    raw = C.CDLL(str(T.LIB_PATH))
+    for n in names:
+        assert hasattr(raw, n), n
+    assert sorted(T.EXPORTED) == names
+    assert T.tls_version().startswith("tls-gfx950")
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_workspace_sizes(lib, name):
+    s = W.CONFIGS[name]
+    sh = T.shape_of(s)
+    assert T.tls_workspace_size(sh, T.TLS_WS_BLOCKS) >= s.pairs * s.NB * 4
+    assert T.tls_workspace_size(sh, T.TLS_WS_TOKENS) >= s.pairs * min(s.Kb, s.NB) * s.bs * 4
+    dec = T.tls_workspace_size(sh, T.TLS_WS_DECODE)
+    assert dec >= s.Hq * s.B * (s.DV + 2) * 4
+    assert T.tls_workspace_size(sh, 7) == 0
+
+
+def test_invalid_shapes_give_zero_workspace(lib):
+    s = W.CONFIGS["c2_32k_gqa"]
+    for bad in (dict(Hq=30), dict(N=0), dict(bs=0), dict(r=3), dict(Kb=0), dict(Kt=0)):
+        assert T.tls_workspace_size(T.shape_of(s.with_(**bad)), T.TLS_WS_BLOCKS) == 0, bad
+    # valid but not compiled: bs > 64, G > 128
+    assert T.tls_workspace_size(T.shape_of(s.with_(bs=128)), T.TLS_WS_BLOCKS) == 0
+    assert T.tls_workspace_size(T.shape_of(s.with_(Hq=8 * 256)), T.TLS_WS_BLOCKS) == 0
+
+
+def test_argument_errors_before_any_device_work(lib):
+    s = W.CONFIGS["c1_8k_gqa8"]
+    sh = T.shape_of(s)
+    rc = lib.tls_select_blocks(C.byref(sh), None, None, None, None, None, 0, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"NULL" in lib.tls_last_error()
+    rc = lib.tls_select_tokens(C.byref(sh), 16, 16, 16, 16, 16, 16, None, 0, None)
+    assert rc == T.TLS_ERR_WORKSPACE
+    rc = lib.tls_sparse_decode(C.byref(T.shape_of(s.with_(D=96, DV=96))), 16, 16, None, 0, 16, 16, None, 16, 1 << 30,
+                               None)
+    assert rc == T.TLS_ERR_UNSUPPORTED
+    rc = lib.tls_sparse_decode(C.byref(sh), 8, 16, None, 0, 16, 16, None, 16, 1 << 30, None)
+    assert rc == T.TLS_ERR_INVALID_ARG   # q not 16-byte aligned
+    rc = lib.tls_select_blocks(None, 16, 16, 16, None, 16, 1 << 30, None)
+    assert rc == T.TLS_ERR_INVALID_ARG
+    h = C.c_void_p()
+    rc = lib.tls_offload_create(C.byref(sh), None, None, None, None, None, C.byref(h))
+    assert rc == T.TLS_ERR_INVALID_ARG and h.value is None
+    rc = lib.tls_prefetch_delta(None, 0, None, None, None, None)
+    assert rc == T.TLS_ERR_INVALID_ARG

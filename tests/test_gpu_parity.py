@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every stage is compared on identical inputs (the oracle's block sets feed the
+GPU token stage, the oracle's token sets feed the GPU attention), then the
+whole GPU chain is checked against oracle attention on the GPU's own sets.
+Summaries, INT4 codes and scales must be bit-exact; index sets follow the
+1e-5 relative band rule; outputs must be within 2e-3 max-abs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as W
+from gpu_common import GpuRun, band_check, check_all, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import two_level_sparse_amd as T
+    T.load_library()   # fails loudly when the HIP library is missing
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def inputs(s, int_range=None, seed=0):
+    rng = np.random.default_rng(seed)
+    if int_range is None:
+        q = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+        k = rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32)
+        oc = rng.permutation(s.D)[: s.n_outlier]
+        k[..., oc] *= 8
+        kv = W.f32_to_bf16_bits(k)
+    else:
+        q = W.f32_to_bf16_bits(rng.integers(-int_range, int_range + 1, (s.B, s.Hq, s.D)).astype(np.float32))
+        kv = W.f32_to_bf16_bits(rng.integers(-int_range, int_range + 1, (s.B, s.Hkv, s.N, s.row)).astype(np.float32))
+    lab = np.stack([np.sort(rng.choice(s.D, s.r, replace=False)) for _ in range(s.Hkv)]).astype(np.int32)
+    return q, kv, lab
+
+
+SMALL = {
+    "gqa8_ragged": W.small_shape(B=2, Hq=16, Hkv=2, N=1000, bs=64, Kb=5, Kt=200),
+    "gqa4": W.small_shape(B=3, Hq=16, Hkv=4, N=4096, bs=64, Kb=8, Kt=300),
+    "mha": W.small_shape(B=2, Hq=3, Hkv=3, N=2500, bs=64, Kb=6, Kt=128),
+    "g12": W.small_shape(B=1, Hq=24, Hkv=2, N=3000, bs=64, Kb=7, Kt=333),
+    "g32_d64_bs16": W.small_shape(B=2, Hq=64, Hkv=2, D=64, DV=64, N=777, bs=16, r=8, Kb=10, Kt=50),
+    "d256_bs32": W.small_shape(B=2, Hq=8, Hkv=1, D=256, DV=256, N=1500, bs=32, r=32, Kb=9, Kt=100),
+    "mla_small": W.small_shape(B=2, Hq=128, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=2048, bs=64, r=32,
+                               Kb=8, Kt=256, n_outlier=0),
+    "select_all": W.small_shape(B=1, Hq=8, Hkv=2, N=900, bs=64, Kb=1000, Kt=100000),
+    "k_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1024, bs=64, Kb=1, Kt=1),
+    "many_splits": W.small_shape(B=1, Hq=8, Hkv=1, N=65536, bs=64, Kb=200, Kt=9000),
+    "bs1": W.small_shape(B=1, Hq=4, Hkv=1, N=300, bs=1, D=64, DV=64, r=8, Kb=40, Kt=17),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes(name):
+    s = SMALL[name]
+    log(f"[gpu] small shape {name}: {s}")
+    q, kv, lab = inputs(s, seed=hash(name) % 1000)
+    st = check_all(s, q, kv, lab)
+    log(f"[gpu] {name}: {st}")
+
+
+def test_select_all_equals_dense_attention():
+    """Kb >= NB and Kt >= N: the GPU step equals dense attention over the whole cache."""
+    s = SMALL["select_all"]
+    q, kv, lab = inputs(s, seed=5)
+    run = GpuRun(s, q, kv, lab)
+    gb, _ = run.blocks()
+    assert np.all(gb == np.arange(s.NB))
+    gt = run.tokens()
+    assert np.all(gt == np.arange(s.N))
+    out, lse = run.attend()
+    for p in range(s.pairs):
+        b, h = divmod(p, s.Hkv)
+        o_ref, l_ref = oracle.attend_pair(s, q[b, h * s.G:(h + 1) * s.G], kv[b, h], np.arange(s.N))
+        assert np.max(np.abs(out[p] - o_ref)) <= 2e-3
+        assert np.max(np.abs(lse[p] - l_ref)) <= 2e-3
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_integer_ties_are_broken_by_lower_index(seed):
+    """Integer q and K make fp32 scores exact and force many exact ties: the GPU
+    sets must then equal the oracle's exactly (lower index wins)."""
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=2048, bs=16, D=32, DV=32, r=4, Kb=37, Kt=150)
+    q, kv, lab = inputs(s, int_range=1, seed=seed)
+    st = check_all(s, q, kv, lab, expect_exact=True)
+    log(f"[gpu] integer ties seed {seed}: {st}")
+
+
+def test_deterministic():
+    s = SMALL["gqa4"]
+    q, kv, lab = inputs(s, seed=9)
+    run = GpuRun(s, q, kv, lab)
+    a = [run.blocks()[0], run.tokens(), run.attend()[0]]
+    b = [run.blocks()[0], run.tokens(), run.attend()[0]]
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_workspace_too_small_is_rejected():
+    import two_level_sparse_amd as T
+    s = SMALL["gqa4"]
+    q, kv, lab = inputs(s, seed=1)
+    run = GpuRun(s, q, kv, lab)
+    d = run.dec
+    with pytest.raises(T.TlsError) as e:
+        T.tls_select_tokens(d.shape, run.qd, run.cache.label_ch, run.cache.codes, run.cache.scale, d.block_idx,
+                            d.token_idx, d.ws[T.TLS_WS_TOKENS], 16)
+    assert e.value.code == T.TLS_ERR_WORKSPACE
+
+
+def test_graph_replay_matches_eager():
+    """The three calls captured in a HIP graph: every replay equals the eager step."""
+    s = SMALL["gqa4"]
+    q, kv, lab = inputs(s, seed=4)
+    run = GpuRun(s, q, kv, lab)
+    d = run.dec
+    d.step(run.qd, run.cache)
+    torch.cuda.synchronize()
+    ref = [to_np(d.block_idx), to_np(d.token_idx), to_np(d.out)]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            d.step(run.qd, run.cache)
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(4):
+        d.out.zero_(); d.token_idx.fill_(-7); d.block_idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(d.block_idx), ref[0])
+        np.testing.assert_array_equal(to_np(d.token_idx), ref[1])
+        np.testing.assert_array_equal(to_np(d.out), ref[2])
+
+
+# ------------------------------------------------------- full workloads ---
+
+def full_inputs(s):
+    q = W.gen_q(s)
+    kv = W.gen_kv(s)
+    lab = W.label_channels(s, kv[0])
+    return q, kv, lab
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("c1_8k_gqa8", None),
+    ("c2_32k_gqa", [0, 7, 13, 31]),
+    ("c3_128k_gqa", [0, 21, 42, 63]),
+    ("c4_64k_mla", [0, 9, 15]),
+])
+def test_full_workloads_sampled(name, pairs):
+    """BASELINE-size workloads in the launch configuration the benchmark uses;
+    the oracle checks the sampled (batch, kv-head) pairs."""
+    s = W.CONFIGS[name]
+    log(f"[gpu] full workload {name}: generating inputs")
+    q, kv, lab = full_inputs(s)
+    log(f"[gpu] full workload {name}: running")
+    st = check_all(s, q, kv, lab, pairs=pairs)
+    log(f"[gpu] {name}: {st}")
+    del kv

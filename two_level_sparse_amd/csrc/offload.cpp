@@ -1,0 +1,234 @@
+// offload.cpp -- staggered incremental prefetch of KV blocks from pinned host
+// memory (AsyncTLS pages, section 2B "Asynchronous Offloading Engine").
+//
+// The device keeps, per (batch, kv head) pair, a resident cache of
+// cap = 2*Kb' block slots and a slot map [NB] (-1 = not resident). The blocks
+// chosen at step t-1 (M_{t-1}) are resident while step t runs; stage 1 for
+// step t produces M_t on a side stream, and this engine then
+//   1. copies M_t to the host and waits for it (the calling thread blocks),
+//   2. forms T_t = M_t \ C_t (C_t: resident blocks),
+//   3. if the free slots do not suffice, evicts resident blocks outside
+//      M_{t-1} and M_t, least recently selected first (lower block first on
+//      equal steps), so the blocks step t reads are never touched,
+//   4. enqueues one host->device copy per block of T_t into its slot and the
+//      slot map of step t+1 (double-buffered: step t reads map t%2, this call
+//      writes map (t+1)%2), and records `copies_done` on the side stream.
+// Capacity 2*Kb' is the least that always fits M_{t-1} u M_t.
+//
+// Ordering contract (the caller's streams): the side-stream work of step t
+// (stage 1 and this call) must start after the main stream finished step
+// t-1's attention, and step t+1's main-stream work must wait for
+// `copies_done` of step t. Then no slot or map entry that a running kernel
+// reads is ever written.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/tls.h"
+#include "tls_api_internal.h"
+
+using namespace tls;
+
+struct tls_offload {
+  Derived d;
+  const uint16_t* host_kv = nullptr;
+  uint16_t* dev_cache = nullptr;
+  int32_t* dev_map[2] = {nullptr, nullptr};
+  int cap = 0;
+  size_t block_elems = 0;
+  std::vector<int32_t> slot_of;     // [pairs*NB] slot or -1
+  std::vector<int64_t> last_sel;    // [pairs*NB] last step the block was selected (-1: prologue)
+  std::vector<int32_t> slot_owner;  // [pairs*cap] block or -1
+  std::vector<int32_t> prev;        // [pairs*kb] M_{t-1}
+  std::vector<uint32_t> mark;       // [NB] scratch stamps
+  uint32_t stamp = 0;
+  int32_t* host_M = nullptr;        // pinned staging of M_t
+  int32_t* host_map[2] = {nullptr, nullptr};  // pinned staging of the slot maps
+  std::vector<int32_t> last_counts, last_blocks;
+  int32_t next_step = 0;
+};
+
+static void free_ctx(tls_offload* c) {
+  if (!c) return;
+  if (c->host_M) (void)hipHostFree(c->host_M);
+  for (int i = 0; i < 2; ++i)
+    if (c->host_map[i]) (void)hipHostFree(c->host_map[i]);
+  delete c;
+}
+
+extern "C" {
+
+int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_cache, int32_t* dev_slot_map0,
+                       int32_t* dev_slot_map1, const int32_t* initial_blocks, tls_offload_t** out) {
+  clear_error();
+  if (!out) return set_error(TLS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!host_kv || !dev_cache || !dev_slot_map0 || !dev_slot_map1 || !initial_blocks)
+    return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (d.N % d.bs != 0) return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_len to be a multiple of block_size");
+  tls_offload* c = new tls_offload;
+  c->d = d;
+  c->host_kv = (const uint16_t*)host_kv;
+  c->dev_cache = (uint16_t*)dev_cache;
+  c->dev_map[0] = dev_slot_map0;
+  c->dev_map[1] = dev_slot_map1;
+  c->cap = 2 * d.kb;
+  c->block_elems = (size_t)d.bs * d.row;
+  c->slot_of.assign((size_t)d.pairs * d.NB, -1);
+  c->last_sel.assign((size_t)d.pairs * d.NB, -2);
+  c->slot_owner.assign((size_t)d.pairs * c->cap, -1);
+  c->prev.assign(initial_blocks, initial_blocks + (size_t)d.pairs * d.kb);
+  c->mark.assign((size_t)d.NB, 0u);
+  c->last_counts.assign(d.pairs, 0);
+  c->last_blocks.assign((size_t)d.pairs * d.kb, -1);
+  hipError_t e = hipHostMalloc((void**)&c->host_M, (size_t)d.pairs * d.kb * sizeof(int32_t), hipHostMallocDefault);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i)
+    e = hipHostMalloc((void**)&c->host_map[i], (size_t)d.pairs * d.NB * sizeof(int32_t), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    free_ctx(c);
+    return hip_error(e, "hipHostMalloc(offload staging)");
+  }
+  // Prologue: M_{-1} goes to slots 0..kb-1 of each pair, copied synchronously.
+  for (int p = 0; p < d.pairs; ++p) {
+    for (int i = 0; i < d.kb; ++i) {
+      const int32_t blk = initial_blocks[(size_t)p * d.kb + i];
+      if (blk < 0 || blk >= d.NB || (i > 0 && blk <= initial_blocks[(size_t)p * d.kb + i - 1])) {
+        free_ctx(c);
+        return set_error(TLS_ERR_INVALID_ARG, "initial_blocks must be ascending block numbers in [0, NB)");
+      }
+      c->slot_of[(size_t)p * d.NB + blk] = i;
+      c->slot_owner[(size_t)p * c->cap + i] = blk;
+      c->last_sel[(size_t)p * d.NB + blk] = -1;
+      e = hipMemcpy(c->dev_cache + ((size_t)p * c->cap + i) * c->block_elems,
+                    c->host_kv + ((size_t)p * d.N + (size_t)blk * d.bs) * d.row, c->block_elems * 2,
+                    hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        free_ctx(c);
+        return hip_error(e, "hipMemcpy(initial blocks)");
+      }
+    }
+  }
+  std::memcpy(c->host_map[0], c->slot_of.data(), c->slot_of.size() * sizeof(int32_t));
+  for (int i = 0; i < 2 && e == hipSuccess; ++i)
+    e = hipMemcpy(c->dev_map[i], c->host_map[0], c->slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_ctx(c);
+    return hip_error(e, "initial slot map upload");
+  }
+  *out = c;
+  return TLS_OK;
+}
+
+const int32_t* tls_offload_slot_map(const tls_offload_t* ctx, int32_t step) {
+  if (!ctx || step < 0) return nullptr;
+  return ctx->dev_map[step & 1];
+}
+
+int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_idx, void* side, void* copies_done,
+                       int64_t* n_copied_opt) {
+  clear_error();
+  if (!c || !dev_block_idx || !copies_done) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
+  if (step != c->next_step)
+    return set_error(TLS_ERR_STATE, "prefetch for step %d, expected step %d", step, c->next_step);
+  const Derived& d = c->d;
+  hipStream_t st = (hipStream_t)side;
+  hipError_t e = hipMemcpyAsync(c->host_M, dev_block_idx, (size_t)d.pairs * d.kb * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_error(e, "copy of M_t to host");
+
+  int64_t total = 0;
+  std::vector<std::pair<int64_t, int32_t>> evict;
+  std::vector<int32_t> free_slots;
+  for (int p = 0; p < d.pairs; ++p) {
+    const int32_t* cur = c->host_M + (size_t)p * d.kb;
+    int32_t* prv = c->prev.data() + (size_t)p * d.kb;
+    int32_t* slot_of = c->slot_of.data() + (size_t)p * d.NB;
+    int64_t* last = c->last_sel.data() + (size_t)p * d.NB;
+    int32_t* owner = c->slot_owner.data() + (size_t)p * c->cap;
+    // mark M_{t-1} u M_t
+    if (++c->stamp == 0) {
+      std::fill(c->mark.begin(), c->mark.end(), 0u);
+      c->stamp = 1;
+    }
+    const uint32_t s = c->stamp;
+    for (int i = 0; i < d.kb; ++i) {
+      if (cur[i] < 0 || cur[i] >= d.NB) return set_error(TLS_ERR_STATE, "M_t holds an invalid block number");
+      c->mark[prv[i]] = s;
+      c->mark[cur[i]] = s;
+    }
+    // T_t = M_t \ C_t (ascending, as M_t is)
+    int32_t* T = c->last_blocks.data() + (size_t)p * d.kb;
+    int nT = 0;
+    for (int i = 0; i < d.kb; ++i)
+      if (slot_of[cur[i]] < 0) T[nT++] = cur[i];
+    for (int i = nT; i < d.kb; ++i) T[i] = -1;
+    c->last_counts[p] = nT;
+    total += nT;
+    // free slots, then evictions if they do not suffice
+    free_slots.clear();
+    for (int sl = 0; sl < c->cap; ++sl)
+      if (owner[sl] < 0) free_slots.push_back(sl);
+    const int need = nT - (int)free_slots.size();
+    if (need > 0) {
+      evict.clear();
+      for (int sl = 0; sl < c->cap; ++sl) {
+        const int32_t blk = owner[sl];
+        if (blk >= 0 && c->mark[blk] != s) evict.emplace_back(last[blk], blk);
+      }
+      if ((int)evict.size() < need) return set_error(TLS_ERR_STATE, "not enough evictable slots");
+      std::partial_sort(evict.begin(), evict.begin() + need, evict.end());
+      for (int k = 0; k < need; ++k) {
+        const int32_t blk = evict[k].second;
+        const int32_t sl = slot_of[blk];
+        slot_of[blk] = -1;
+        owner[sl] = -1;
+        free_slots.push_back(sl);
+      }
+      std::sort(free_slots.begin(), free_slots.end());
+    }
+    // copies of T_t into the lowest free slots
+    for (int i = 0; i < nT; ++i) {
+      const int32_t blk = T[i], sl = free_slots[i];
+      slot_of[blk] = sl;
+      owner[sl] = blk;
+      e = hipMemcpyAsync(c->dev_cache + ((size_t)p * c->cap + sl) * c->block_elems,
+                         c->host_kv + ((size_t)p * d.N + (size_t)blk * d.bs) * d.row, c->block_elems * 2,
+                         hipMemcpyHostToDevice, st);
+      if (e != hipSuccess) return hip_error(e, "block copy");
+    }
+    for (int i = 0; i < d.kb; ++i) {
+      last[cur[i]] = step;
+      prv[i] = cur[i];
+    }
+  }
+  const int nxt = (step + 1) & 1;
+  std::memcpy(c->host_map[nxt], c->slot_of.data(), c->slot_of.size() * sizeof(int32_t));
+  e = hipMemcpyAsync(c->dev_map[nxt], c->host_map[nxt], c->slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice,
+                     st);
+  if (e == hipSuccess) e = hipEventRecord((hipEvent_t)copies_done, st);
+  if (e != hipSuccess) return hip_error(e, "slot map upload");
+  c->next_step = step + 1;
+  if (n_copied_opt) *n_copied_opt = total;
+  return TLS_OK;
+}
+
+int tls_offload_last_delta(const tls_offload_t* c, int32_t* counts, int32_t* blocks) {
+  if (!c || !counts || !blocks) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
+  std::memcpy(counts, c->last_counts.data(), c->last_counts.size() * sizeof(int32_t));
+  std::memcpy(blocks, c->last_blocks.data(), c->last_blocks.size() * sizeof(int32_t));
+  return TLS_OK;
+}
+
+void tls_offload_destroy(tls_offload_t* c) {
+  if (c) (void)hipDeviceSynchronize();
+  free_ctx(c);
+}
+
+}  // extern "C"

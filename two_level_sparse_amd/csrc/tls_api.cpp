@@ -1,0 +1,201 @@
+// tls_api.cpp -- the C ABI of libtls (declared in include/tls.h): argument
+// checks, workspace sizing and kernel dispatch. No allocation happens here;
+// every buffer comes from the caller.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/tls.h"
+#include "tls_api_internal.h"
+#include "tls_launch.h"
+
+namespace tls {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(TLS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int derive(const tls_shape_t* s, Derived* d) {
+  if (!s) return set_error(TLS_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->num_kv_heads < 1 || s->num_q_heads < 1)
+    return set_error(TLS_ERR_INVALID_ARG, "batch and head counts must be >= 1");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return set_error(TLS_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", s->num_q_heads,
+                     s->num_kv_heads);
+  if (s->head_dim_qk < 1 || s->head_dim_v < 1) return set_error(TLS_ERR_INVALID_ARG, "head dims must be >= 1");
+  if (s->ctx_len < 1) return set_error(TLS_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  if (s->block_size < 1) return set_error(TLS_ERR_INVALID_ARG, "block_size must be >= 1");
+  if (s->num_label_ch < 2 || s->num_label_ch % 2 != 0)
+    return set_error(TLS_ERR_INVALID_ARG, "num_label_ch must be even and >= 2");
+  if (s->top_kb < 1 || s->top_kt < 1) return set_error(TLS_ERR_INVALID_ARG, "top_kb and top_kt must be >= 1");
+  if (!std::isfinite(s->sm_scale)) return set_error(TLS_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (s->v_is_k_prefix && s->head_dim_v > s->head_dim_qk)
+    return set_error(TLS_ERR_INVALID_ARG, "v_is_k_prefix needs head_dim_v <= head_dim_qk");
+  if (s->num_label_ch > s->head_dim_qk)
+    return set_error(TLS_ERR_INVALID_ARG, "num_label_ch exceeds head_dim_qk");
+
+  d->B = s->batch;
+  d->Hq = s->num_q_heads;
+  d->Hkv = s->num_kv_heads;
+  d->G = d->Hq / d->Hkv;
+  d->D = s->head_dim_qk;
+  d->DV = s->head_dim_v;
+  d->row = s->v_is_k_prefix ? d->D : d->D + d->DV;
+  d->v_off = s->v_is_k_prefix ? 0 : d->D;
+  d->N = s->ctx_len;
+  d->bs = s->block_size;
+  d->r = s->num_label_ch;
+  d->NB = (d->N + d->bs - 1) / d->bs;
+  d->kb = (int)(s->top_kb < d->NB ? s->top_kb : d->NB);
+  const int64_t cand = (int64_t)d->kb * d->bs;
+  d->kt = (int)(s->top_kt < cand ? s->top_kt : cand);
+  d->pairs = d->B * d->Hkv;
+  d->sm = s->sm_scale;
+
+  if (d->G > 128) return set_error(TLS_ERR_UNSUPPORTED, "more than 128 query heads per kv head");
+  if (d->D % 32 != 0 || d->D > 576) return set_error(TLS_ERR_UNSUPPORTED, "head_dim_qk must be a multiple of 32, <= 576");
+  if (d->DV % 8 != 0 || d->DV > 512) return set_error(TLS_ERR_UNSUPPORTED, "head_dim_v must be a multiple of 8, <= 512");
+  if (d->bs > 64) return set_error(TLS_ERR_UNSUPPORTED, "block_size above 64");
+  if (d->r > 32) return set_error(TLS_ERR_UNSUPPORTED, "more than 32 label channels");
+  if (d->NB > 16384) return set_error(TLS_ERR_UNSUPPORTED, "more than 16384 blocks per sequence");
+  if (cand > 16384) return set_error(TLS_ERR_UNSUPPORTED, "more than 16384 candidate tokens (Kb*bs)");
+  if (d->N > (int64_t)0x7FFFFFFF) return set_error(TLS_ERR_UNSUPPORTED, "ctx_len above 2^31-1");
+  return TLS_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_bytes(const Derived& d, int which) {
+  switch (which) {
+    case TLS_WS_BLOCKS: return round_up((size_t)d.pairs * d.NB * sizeof(float));
+    case TLS_WS_TOKENS: return round_up((size_t)d.pairs * d.kb * d.bs * sizeof(float));
+    case TLS_WS_DECODE: {
+      DecodePlan pl;
+      plan_decode(d.pairs, d.G, d.D, d.DV, d.kt, &pl);
+      return round_up(pl.part_bytes);
+    }
+    default: return 0;
+  }
+}
+
+}  // namespace tls
+
+using namespace tls;
+
+extern "C" {
+
+const char* tls_last_error(void) { return g_err; }
+
+const char* tls_version(void) { return "tls-gfx950 0.1"; }
+
+size_t tls_workspace_size(const tls_shape_t* shape, int which) {
+  Derived d;
+  if (derive(shape, &d) != TLS_OK) return 0;
+  return ws_bytes(d, which);
+}
+
+int tls_build_summaries(const tls_shape_t* shape, const void* kv, const int32_t* label_ch, void* summ,
+                        uint8_t* codes, float* scale, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!kv || !label_ch || !summ || !codes || !scale) return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(kv, 4) || !aligned(summ, 4) || !aligned(scale, 4) || !aligned(label_ch, 4))
+    return set_error(TLS_ERR_INVALID_ARG, "kv, summ, scale and label_ch must be 4-byte aligned");
+  BuildArgs a{(const uint16_t*)kv, label_ch, (uint16_t*)summ, codes, scale, d.pairs, d.Hkv, d.D, d.row, d.bs, d.r,
+              d.N, d.NB};
+  hipError_t e = launch_build(a, (hipStream_t)stream);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "build_summaries launch");
+}
+
+int tls_select_blocks(const tls_shape_t* shape, const void* q, const void* summ, int32_t* block_idx,
+                      float* block_score_opt, void* ws, size_t ws_len, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!q || !summ || !block_idx) return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(q, 16) || !aligned(summ, 16))
+    return set_error(TLS_ERR_INVALID_ARG, "q and summ must be 16-byte aligned");
+  float* S = block_score_opt;
+  if (!S) {
+    if (!ws || ws_len < ws_bytes(d, TLS_WS_BLOCKS))
+      return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_BLOCKS));
+    S = (float*)ws;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB};
+  hipError_t e = launch_score_blocks(sa, st);
+  if (e != hipSuccess) return hip_error(e, "score_blocks launch");
+  TopkArgs ta{S, d.pairs, (int)d.NB, d.kb, nullptr, 0, 1, d.N, block_idx, d.kb};
+  e = launch_topk(ta, st);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "topk(blocks) launch");
+}
+
+int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* label_ch, const uint8_t* codes,
+                      const float* scale, const int32_t* block_idx, int32_t* token_idx, void* ws, size_t ws_len,
+                      void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!q || !label_ch || !codes || !scale || !block_idx || !token_idx)
+    return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!ws || ws_len < ws_bytes(d, TLS_WS_TOKENS))
+    return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_TOKENS));
+  hipStream_t st = (hipStream_t)stream;
+  float* A = (float*)ws;
+  TokenScoreArgs sa{(const uint16_t*)q, label_ch, codes, scale, block_idx, A, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.bs,
+                    d.r, d.kb, d.N};
+  hipError_t e = launch_score_tokens(sa, st);
+  if (e != hipSuccess) return hip_error(e, "score_tokens launch");
+  TopkArgs ta{A, d.pairs, d.kb * d.bs, d.kt, block_idx, d.kb, d.bs, d.N, token_idx, d.kt};
+  e = launch_topk(ta, st);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "topk(tokens) launch");
+}
+
+int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,
+                      int32_t slots_per_pair, const int32_t* token_idx, float* out, float* lse_opt, void* ws,
+                      size_t ws_len, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!q || !kv_cache || !token_idx || !out) return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(q, 16) || !aligned(kv_cache, 16))
+    return set_error(TLS_ERR_INVALID_ARG, "q and kv_cache must be 16-byte aligned");
+  if (slot_map && slots_per_pair < 1) return set_error(TLS_ERR_INVALID_ARG, "slots_per_pair must be >= 1");
+  const bool dims_ok = (d.D == 64 && d.DV == 64) || (d.D == 128 && d.DV == 128) || (d.D == 256 && d.DV == 256) ||
+                       (d.D == 576 && d.DV == 512);
+  if (!dims_ok)
+    return set_error(TLS_ERR_UNSUPPORTED, "attention is compiled for (D,DV) in {(64,64),(128,128),(256,256),(576,512)}");
+  DecodePlan pl;
+  plan_decode(d.pairs, d.G, d.D, d.DV, d.kt, &pl);
+  if (!ws || ws_len < ws_bytes(d, TLS_WS_DECODE))
+    return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
+  DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, (float*)ws, out, lse_opt,
+               d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
+               slot_map ? slots_per_pair : 0, d.N, d.NB, d.sm};
+  hipError_t e = launch_decode(a, pl, (hipStream_t)stream);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "sparse_decode launch");
+}
+
+}  // extern "C"

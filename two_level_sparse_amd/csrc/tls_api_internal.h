@@ -1,0 +1,25 @@
+// tls_api_internal.h -- shape derivation and error plumbing shared by the C ABI
+// translation units (tls_api.cpp, offload.cpp). Internal.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tls.h"
+
+namespace tls {
+
+struct Derived {
+  int B, Hq, Hkv, G, D, DV, row, v_off, bs, r, kb, kt, pairs;
+  int64_t N, NB;
+  float sm;
+};
+
+int derive(const tls_shape_t* s, Derived* d);
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+int hip_error(hipError_t e, const char* what);
+bool aligned(const void* p, size_t a);
+size_t ws_bytes(const Derived& d, int which);
+
+}  // namespace tls

@@ -1,0 +1,76 @@
+// tls_launch.h -- host-side launchers of the gfx950 kernels (internal).
+// The C ABI in include/tls.h validates arguments, then calls these.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tls {
+
+struct BuildArgs {
+  const uint16_t* kv;
+  const int32_t* label_ch;
+  uint16_t* summ;
+  uint8_t* codes;
+  float* scale;
+  int pairs, Hkv, D, row, bs, r;
+  int64_t N, NB;
+};
+hipError_t launch_build(const BuildArgs& a, hipStream_t st);
+
+struct BlockScoreArgs {
+  const uint16_t* q;
+  const uint16_t* summ;
+  float* S;  // [pairs, NB]
+  int pairs, Hq, Hkv, G, D;
+  int64_t NB;
+};
+hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st);
+
+struct TokenScoreArgs {
+  const uint16_t* q;
+  const int32_t* label_ch;
+  const uint8_t* codes;
+  const float* scale;
+  const int32_t* block_idx;  // [pairs, kb]
+  float* A;                  // [pairs, kb*bs]
+  int pairs, Hq, Hkv, G, D, bs, r, kb;
+  int64_t N;
+};
+hipError_t launch_score_tokens(const TokenScoreArgs& a, hipStream_t st);
+
+// Exact top-k per row of `scores` ([rows, n] float). With block_idx == NULL the
+// selected ids are the column numbers; otherwise column c is token
+// block_idx[row*kb + c/bs]*bs + c%bs and is valid only when that token < N.
+struct TopkArgs {
+  const float* scores;
+  int rows;
+  int n;
+  int K;
+  const int32_t* block_idx;
+  int kb, bs;
+  int64_t N;
+  int32_t* out;  // [rows, out_len], -1 padded
+  int out_len;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* slot_map;  // NULL = identity
+  const int32_t* token_idx;
+  float* part;              // partial results
+  float* out;
+  float* lse;               // may be NULL
+  int pairs, B, Hq, Hkv, G, D, DV, row, v_off, bs, kt, slots;
+  int64_t N, NB;
+  float sm_scale;
+};
+struct DecodePlan {
+  int HT, nht, tps, nsplit;
+  size_t part_bytes;
+};
+bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t st);
+
+}  // namespace tls
