@@ -1,0 +1,214 @@
+"""Benchmark of the two-level sparse-attention decode step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3_128k_gqa]
+
+A step is one whole decode step over one batch: block selection (summary
+GEMM + top-Kb), token selection (INT4 label scores + top-Kt) and attention over
+the kept tokens, for every (batch, kv head) pair, with inputs resident in HBM.
+The default workload is the 128k-context GQA decode (batch 8, 64 query heads on
+8 kv heads, head dim 128, block 64, Kb=128, Kt=4096, 16 INT4 label channels).
+
+Cold measurement: R copies of the cache live at distinct device addresses and
+the steps rotate over them, so no step finds its bytes in the 256 MB Infinity
+Cache left there by the previous step (R * touched bytes >= 1 GiB).
+
+Prints one JSON line: queries/sec (= batch / step time), the HBM roofline of
+the dominant kernel (attention; its launches timed with HIP events on the
+stream they run on) and the fp64 oracle timed on host cores over a bounded
+sample of pairs as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import workload as W  # noqa: E402
+
+METRIC = "sparse-attn decode queries/sec at 32k/128k ctx; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def algorithmic_bytes(s):
+    """Bytes the selection must touch per step (summaries, label cache of the
+    candidates, gathered K/V rows, q, out) and the attention kernel's share."""
+    kb = min(s.Kb, s.NB)
+    kt = min(s.Kt, kb * s.bs)
+    summ = s.pairs * s.NB * 2 * s.D * 2
+    label = s.pairs * kb * s.bs * (s.r // 2 + 4)
+    rows = s.pairs * kt * s.row * 2
+    q = s.B * s.Hq * s.D * 2
+    out = s.B * s.Hq * s.DV * 4
+    return dict(summaries=summ, label=label, kv_rows=rows, q=q, out=out, total=summ + label + rows + q + out,
+                attention=rows + q + out + s.B * s.Hq * 4)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(s, q, kv, lab, budget_s=15.0):
+    """The fp64 oracle (O3..O9 of one step; summaries/label cache prebuilt,
+    untimed) on a bounded sample of pairs, scaled to queries/sec of a full step."""
+    import oracle
+    nth = oracle.num_threads()
+    n = min(s.pairs, max(1, nth))
+    pairs = np.arange(n, dtype=np.int32)
+    built = oracle.decode(s, q, kv, lab, pairs=pairs)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.decode(s, q, kv, lab, pairs=pairs, built=built)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 2 * budget_s:
+            break
+    per_sample = el / reps
+    step_s = per_sample * s.pairs / n
+    return {"value": s.B / step_s, "unit": "queries/s", "cores": nth, "kind": "oracle",
+            "sample": f"{n} of {s.pairs} (batch, kv-head) pairs of one step, {reps} repetitions, "
+                      f"{per_sample * 1e3:.1f} ms each, scaled by {s.pairs}/{n}; summaries and label cache "
+                      f"prebuilt (untimed); fp64 C oracle with OpenMP over pairs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3_128k_gqa", choices=[k for k in W.CONFIGS if not W.CONFIGS[k].steps])
+    ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for 1 GiB)")
+    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this operator is built and "
+              f"timed on a single MI355X; see the design notes for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import two_level_sparse_amd as T
+    from two_level_sparse_amd.runtime import Cache, Decoder, bf16
+
+    T.load_library()
+    s = W.CONFIGS[args.config]
+    ab = algorithmic_bytes(s)
+    touched = ab["total"]
+    R = args.rotate or max(1, math.ceil((1 << 30) / touched))
+    log(f"[bench] {s.name}: generating inputs (rotation over {R} cache copies)")
+    q0 = W.gen_q(s)
+    kv = W.gen_kv(s)
+    lab = W.label_channels(s, kv[0])
+    base = Cache(s, kv, lab).build()
+    torch.cuda.synchronize()
+    caches = [base]
+    for r in range(1, R):
+        c = Cache.__new__(Cache)
+        c.s, c.shape = s, base.shape
+        c.kv = base.kv.clone()
+        c.label_ch = base.label_ch
+        c.summ, c.codes, c.scale = base.summ.clone(), base.codes.clone(), base.scale.clone()
+        caches.append(c)
+    qs = [bf16(q0)] + [bf16(W.gen_q(s.with_(seed=s.seed + 100 * r))) for r in range(1, R)]
+    dec = Decoder(s)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    graphs = None
+    if args.graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                dec.step(qs[r], caches[r])  # warm the allocator/kernels outside capture
+                with torch.cuda.graph(g, stream=side):
+                    dec.step(qs[r], caches[r])
+            graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+
+    def one_step(i, ev=None):
+        r = i % R
+        if graphs is not None:
+            graphs[r].replay()
+            return
+        dec.select_blocks(qs[r], caches[r])
+        dec.select_tokens(qs[r], caches[r])
+        if ev is not None:
+            ev[0].record(stream)
+        dec.decode(qs[r], caches[r].kv)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        one_step(i, None if graphs is not None else evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    step_s = ms_step / 1e3
+
+    dec_ms = None
+    if graphs is None:
+        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    roof = None
+    if dec_ms:
+        ach = ab["attention"] / (dec_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_attend (tls_sparse_decode)", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"]}
+
+    res = {
+        "metric": METRIC,
+        "value": round(s.B / step_s, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name}: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim {s.D}/{s.DV}, "
+                               f"context {s.N}, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, {s.r} INT4 label channels",
+                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs)},
+        "hbm": {"algorithmic_bytes_per_step": ab["total"],
+                "achieved_GBps": round(ab["total"] / step_s / 1e9, 1),
+                "frac_of_peak": round(ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline")
+        res["cpu_baseline"] = cpu_baseline(s, q0, kv, lab, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,7 +15,9 @@
 //     one token per load (16 bytes), so a wave load covers 64/(DV/8) full rows;
 //     the probabilities cross from the MFMA layout through LDS.
 // The 4 waves merge their (m, l, o) in LDS; one partial per workgroup goes to
-// the workspace. k_merge combines the splits per head and writes out and lse.
+// the workspace. The last workgroup to finish a (pair, head tile) -- found
+// with an atomic counter in the workspace, which it resets to zero -- merges
+// the splits and writes out and lse, so one launch covers the whole call.
 #include "tls_dev.h"
 #include "tls_launch.h"
 
@@ -25,9 +27,10 @@ template <int D, int DV, int HT>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map,
                                                 const int32_t* __restrict__ token_idx, float* __restrict__ part,
-                                                int Hq, int Hkv, int G, int row, int v_off, int64_t N, int bs,
-                                                int64_t NB, int slots, int kt, int tps, int nsplit, int nht,
-                                                float qk_scale) {
+                                                int* __restrict__ counters, float* __restrict__ out,
+                                                float* __restrict__ lse, int Hq, int Hkv, int G, int row, int v_off,
+                                                int64_t N, int bs, int64_t NB, int slots, int kt, int tps,
+                                                int nsplit, int nht, float qk_scale) {
   constexpr int KSTEPS = D / 32;
   constexpr int CPR = DV / 8;    // 16-byte chunks per value row
   constexpr int RPI = 64 / CPR;  // value rows per wave load
@@ -80,9 +83,13 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
     int tok = tq < t_end ? tix[tq] : -1;
     int prow = 0;  // row of the token inside this pair's cache
     if (tok >= 0 && tok < N) {
-      const int slot = smap ? smap[tok / bs] : 0;
-      if (slot < 0 || slot >= slots) tok = -1;  // not resident: never read outside the cache
-      else prow = smap ? slot * bs + tok % bs : tok;
+      if (smap) {
+        const int slot = smap[tok / bs];
+        if (slot < 0 || slot >= slots) tok = -1;  // not resident: never read outside the cache
+        else prow = slot * bs + tok % bs;
+      } else {
+        prow = tok;
+      }
     } else {
       tok = -1;
     }
@@ -202,31 +209,37 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
     }
     dst[e] = val;
   }
-}
 
-// One workgroup per query head: combine the splits.
-template <int DV>
-__global__ __launch_bounds__(DV < 64 ? 64 : DV) void k_merge(const float* __restrict__ part, float* __restrict__ out,
-                                                             float* __restrict__ lse, int Hq, int Hkv, int G, int HT,
-                                                             int nht, int nsplit) {
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int h = hq / G, g = hq % G;
-  const int p = b * Hkv + h, ht = g / HT, hh = g % HT;
-  const float* base = part + (((int64_t)p * nht + ht) * nsplit) * HT * (DV + 2) + hh * (DV + 2);
+  // ---- the last workgroup of this (pair, head tile) merges the splits ----
+  __shared__ int last_flag;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last_flag = atomicAdd(&counters[p * nht + ht], 1) == nsplit - 1;
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();  // acquire: the other workgroups' partials are visible
+  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * (DV + 2);
   const int64_t sstride = (int64_t)HT * (DV + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride]);
-  float L = 0.0f, O = 0.0f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = base[s * sstride];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    L += base[s * sstride + 1] * w;
-    if (c < DV) O += base[s * sstride + 2 + c] * w;
+  for (int e = threadIdx.x; e < HT * DV; e += 256) {
+    const int hh = e / DV, c = e % DV;
+    const int g = ht * HT + hh;
+    if (g >= G) continue;
+    const float* ph = base + hh * (DV + 2);
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ph[sp * sstride]);
+    float L = 0.0f, O = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float ms = ph[sp * sstride];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      L += ph[sp * sstride + 1] * w;
+      O += ph[sp * sstride + 2 + c] * w;
+    }
+    const int64_t oh = (int64_t)b * Hq + (int64_t)h * G + g;
+    out[oh * DV + c] = L > 0.0f ? O / L : 0.0f;
+    if (lse && c == 0) lse[oh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
-  if (c < DV) out[((int64_t)b * Hq + hq) * DV + c] = L > 0.0f ? O / L : 0.0f;
-  if (lse && c == 0) lse[(int64_t)b * Hq + hq] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (threadIdx.x == 0) counters[p * nht + ht] = 0;  // ready for the next call
 }
 
 bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
@@ -245,7 +258,8 @@ bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
   plan->nht = nht;
   plan->tps = tps;
   plan->nsplit = nsplit;
-  plan->part_bytes = (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
+  plan->cnt_bytes = (((size_t)pairs * nht * sizeof(int)) + 255) & ~(size_t)255;
+  plan->part_bytes = plan->cnt_bytes + (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
   (void)D;
   return true;
 }
@@ -253,14 +267,11 @@ bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
 template <int D, int DV, int HT>
 static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_attend<D, DV, HT>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, a.part, a.Hq,
-                     a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
-                     a.sm_scale * kLog2e);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 mgrid((unsigned)a.Hq, (unsigned)a.B);
-  hipLaunchKernelGGL(k_merge<DV>, mgrid, dim3(DV < 64 ? 64 : DV), 0, st, a.part, a.out, a.lse, a.Hq, a.Hkv, a.G, pl.HT,
-                     pl.nht, pl.nsplit);
+  int* counters = reinterpret_cast<int*>(a.part);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part) + pl.cnt_bytes);
+  hipLaunchKernelGGL((k_attend<D, DV, HT>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, part,
+                     counters, a.out, a.lse, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                     pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -191,7 +191,7 @@ int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_ca
   plan_decode(d.pairs, d.G, d.D, d.DV, d.kt, &pl);
   if (!ws || ws_len < ws_bytes(d, TLS_WS_DECODE))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
-  DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, (float*)ws, out, lse_opt,
+  DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, ws, out, lse_opt,
                d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
                slot_map ? slots_per_pair : 0, d.N, d.NB, d.sm};
   hipError_t e = launch_decode(a, pl, (hipStream_t)stream);

@@ -61,7 +61,8 @@ class Decoder:
         self.ws_sizes = {w: tls_workspace_size(self.shape, w) for w in (TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE)}
         if min(self.ws_sizes.values()) == 0:
             raise ValueError(f"invalid shape for libtls: {s}")
-        self.ws = {w: torch.empty(n, dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
+        # zero-filled: the decode workspace begins with self-resetting split counters
+        self.ws = {w: torch.zeros(n, dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
 
     def select_blocks(self, q, cache, stream=None, keep_scores=False, block_idx=None):
         bi = self.block_idx if block_idx is None else block_idx
