@@ -33,10 +33,8 @@
  *   - Index outputs are sets, written in ascending order. Ties in a top-k go to
  *     the lower index.
  *   - Workspaces: `ws` must be at least tls_workspace_size(shape, which) bytes
- *     (256-byte aligned). The TLS_WS_BLOCKS and TLS_WS_TOKENS workspaces may
- *     hold anything on entry. The TLS_WS_DECODE workspace starts with split
- *     counters: zero-fill it once before its first use; every call leaves it
- *     zeroed again. Calls that share one workspace must not overlap in time.
+ *     (256-byte aligned). Their contents on entry do not matter. Calls that
+ *     share one workspace must not overlap in time.
  *
  * Layouts (row-major)
  *   q          [B, Hq, D]            bf16

@@ -80,7 +80,8 @@ def test_select_all_equals_dense_attention():
     gb, _ = run.blocks()
     assert np.all(gb == np.arange(s.NB))
     gt = run.tokens()
-    assert np.all(gt == np.arange(s.N))
+    assert np.all(gt[:, : s.N] == np.arange(s.N))
+    assert np.all(gt[:, s.N:] == -1)          # Kt' = NB*bs > N: padded after the valid tokens
     out, lse = run.attend()
     for p in range(s.pairs):
         b, h = divmod(p, s.Hkv)
@@ -93,7 +94,7 @@ def test_select_all_equals_dense_attention():
 def test_integer_ties_are_broken_by_lower_index(seed):
     """Integer q and K make fp32 scores exact and force many exact ties: the GPU
     sets must then equal the oracle's exactly (lower index wins)."""
-    s = W.small_shape(B=2, Hq=8, Hkv=2, N=2048, bs=16, D=32, DV=32, r=4, Kb=37, Kt=150)
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=2048, bs=16, D=64, DV=64, r=4, Kb=37, Kt=150)
     q, kv, lab = inputs(s, int_range=1, seed=seed)
     st = check_all(s, q, kv, lab, expect_exact=True)
     log(f"[gpu] integer ties seed {seed}: {st}")

@@ -6,35 +6,39 @@
 // the gathered K/V rows, so each gathered row is read once per head tile.
 //
 // k_attend: workgroup = 4 wavefronts = one (pair, head tile, token split).
-// Each wave takes 16-token tiles of the split in turn:
+// A wave owns batches of TB 16-token tiles:
+//   - lane l resolves token l of the batch (one index load per lane, slot map
+//     applied), and the rows' K fragments (and, for GQA, the V chunks) of all
+//     TB tiles are requested before any arithmetic, so a wave keeps
+//     TB * 16 rows in flight;
 //   - q.K^T on MFMA (16x16x32 bf16): A = the tile's query heads (rows, zero
-//     padded to 16), B = the 16 gathered key rows (columns); each lane loads
-//     16-byte fragments of one token row;
+//     padded to 16), B = the 16 gathered key rows (columns);
 //   - online softmax per head in the exp2 domain (scale folded with log2 e);
-//   - P.V on the vector ALU: each lane owns 8 consecutive value channels of
-//     one token per load (16 bytes), so a wave load covers 64/(DV/8) full rows;
-//     the probabilities cross from the MFMA layout through LDS.
-// The 4 waves merge their (m, l, o) in LDS; one partial per workgroup goes to
-// the workspace. The last workgroup to finish a (pair, head tile) -- found
-// with an atomic counter in the workspace, which it resets to zero -- merges
-// the splits and writes out and lse, so one launch covers the whole call.
+//   - P.V on the vector ALU: a lane owns 8 consecutive value channels of one
+//     token per 16-byte load, so one wave load covers 64/(DV/8) whole rows; the
+//     probabilities cross from the MFMA layout through LDS.
+// The 4 waves merge their (m, l, o) in LDS and the workgroup writes one
+// partial. k_merge then combines the splits of every head. (A fused
+// last-workgroup merge would need an agent-scope release per workgroup, which
+// on this part writes back the XCD's whole L2; a second launch is cheaper.)
 #include "tls_dev.h"
 #include "tls_launch.h"
 
 namespace tls {
 
-template <int D, int DV, int HT>
+template <int D, int DV, int HT, int TB, bool PRE>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map,
                                                 const int32_t* __restrict__ token_idx, float* __restrict__ part,
-                                                int* __restrict__ counters, float* __restrict__ out,
-                                                float* __restrict__ lse, int Hq, int Hkv, int G, int row, int v_off,
-                                                int64_t N, int bs, int64_t NB, int slots, int kt, int tps,
-                                                int nsplit, int nht, float qk_scale) {
+                                                int Hq, int Hkv, int G, int row, int v_off, int64_t N, int bs,
+                                                int64_t NB, int slots, int kt, int tps, int nsplit, int nht,
+                                                float qk_scale) {
   constexpr int KSTEPS = D / 32;
   constexpr int CPR = DV / 8;    // 16-byte chunks per value row
   constexpr int RPI = 64 / CPR;  // value rows per wave load
-  static_assert(D % 32 == 0 && 64 % CPR == 0 && CPR <= 64, "unsupported head dims");
+  constexpr int VL = 16 / RPI;   // value loads per 16-token tile
+  constexpr int BT = TB * 16;    // tokens per wave batch
+  static_assert(D % 32 == 0 && 64 % CPR == 0 && CPR <= 64 && BT <= 64, "unsupported shape");
 
   __shared__ float p_lds[4][16][16];  // [wave][token][head]
   __shared__ float c_lds[4][16];      // [wave][head] rescale factors
@@ -47,19 +51,25 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   const int n = lane & 15, kq = lane >> 4;
   const int chunk = lane % CPR, rsub = lane / CPR;
 
-  // Query fragments of this lane's MFMA row (head ht*HT + n).
+  // Query fragments of this lane's MFMA row (head ht*HT + n): in registers,
+  // or (without row prefetch, i.e. the wide MLA rows) in LDS to free registers.
   const int g_row = ht * HT + n;
   const bool row_ok = n < HT && g_row < G;
-  u32x4 qf[KSTEPS];
+  __shared__ u32x4 q_lds[PRE ? 1 : KSTEPS][64];
+  u32x4 qf[PRE ? KSTEPS : 1];
   {
     const uint16_t* qrow = q + ((int64_t)b * Hq + (int64_t)h * G + (row_ok ? g_row : 0)) * D;
+    if constexpr (PRE) {
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) qf[k] = row_ok ? ld16(qrow + k * 32 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < KSTEPS; ++k) qf[k] = row_ok ? ld16(qrow + k * 32 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      for (int k = wave; k < KSTEPS; k += 4) q_lds[k][lane] = row_ok ? ld16(qrow + k * 32 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
   }
 
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
-  const int ntiles = t_end > t_begin ? (t_end - t_begin + 15) / 16 : 0;
   const int32_t* tix = token_idx + (int64_t)p * kt;
   const uint16_t* kvp = kv + (slot_map ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
   const int32_t* smap = slot_map ? slot_map + (int64_t)p * NB : nullptr;
@@ -76,75 +86,116 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
 
-  for (int tile = wave; tile < ntiles; tile += 4) {
-    const int t0 = t_begin + tile * 16;
-    // ---- scores of the 16 tokens (MFMA) ----
-    const int tq = t0 + n;
-    int tok = tq < t_end ? tix[tq] : -1;
-    int prow = 0;  // row of the token inside this pair's cache
-    if (tok >= 0 && tok < N) {
-      if (smap) {
-        const int slot = smap[tok / bs];
-        if (slot < 0 || slot >= slots) tok = -1;  // not resident: never read outside the cache
-        else prow = slot * bs + tok % bs;
-      } else {
-        prow = tok;
+  for (int base = t_begin + wave * BT; base < t_end; base += 4 * BT) {
+    // ---- resolve the batch's tokens: lane l -> token base + l ----
+    int my_tok = -1, my_row = 0;
+    if (lane < BT && base + lane < t_end) {
+      const int tok = tix[base + lane];
+      if (tok >= 0 && tok < N) {
+        if (smap) {
+          const int slot = smap[tok / bs];
+          if (slot >= 0 && slot < slots) {  // a block that is not resident is never read
+            my_tok = tok;
+            my_row = slot * bs + tok % bs;
+          }
+        } else {
+          my_tok = tok;
+          my_row = tok;
+        }
       }
-    } else {
-      tok = -1;
     }
-    const uint16_t* krow = kvp + (int64_t)prow * row;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // ---- request every row of the batch (PRE) ----
+    u32x4 kf[PRE ? TB : 1][KSTEPS];
+    int ktok[TB];
+    const uint16_t* krow[TB];
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) {
-      u32x4 kf = tok >= 0 ? ld16(krow + k * 32 + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
-      z = mfma16x16x32(qf[k], kf, z);
+    for (int j = 0; j < TB; ++j) {
+      ktok[j] = __shfl(my_tok, 16 * j + n, 64);
+      const int r = __shfl(my_row, 16 * j + n, 64);
+      krow[j] = kvp + (int64_t)r * row + 8 * kq;
+      if constexpr (PRE) {
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) kf[j][k] = ktok[j] >= 0 ? ld16(krow[j] + k * 32) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
-    // ---- online softmax (lane holds heads 4*kq+i of token n) ----
-    float pr[4], corr[4];
+    u32x4 vf[PRE ? TB : 1][VL];
+    if constexpr (PRE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float zi = tok >= 0 ? z[i] * qk_scale : -INFINITY;
-      const float tmax = max16(zi);
-      const float m_new = fmaxf(m_run[i], tmax);
-      const float ref = m_new == -INFINITY ? 0.0f : m_new;
-      corr[i] = exp2f(m_run[i] - ref);
-      pr[i] = exp2f(zi - ref);
-      l_run[i] = l_run[i] * corr[i] + pr[i];
-      m_run[i] = m_new;
-    }
-    *reinterpret_cast<f32x4*>(&p_lds[wave][n][4 * kq]) = f32x4{pr[0], pr[1], pr[2], pr[3]};
-    if (n == 0) *reinterpret_cast<f32x4*>(&c_lds[wave][4 * kq]) = f32x4{corr[0], corr[1], corr[2], corr[3]};
-    wave_lds_sync();
-    // ---- P.V (vector ALU) ----
+      for (int j = 0; j < TB; ++j)
 #pragma unroll
-    for (int hh = 0; hh < HT; ++hh) {
-      const float c = c_lds[wave][hh];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= c;
+        for (int v = 0; v < VL; ++v) {
+          const int tt = 16 * j + v * RPI + rsub;
+          const int vt = __shfl(my_tok, tt, 64);
+          const int vr = __shfl(my_row, tt, 64);
+          vf[j][v] = vt >= 0 ? ld16(kvp + (int64_t)vr * row + v_off + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 #pragma unroll
-    for (int r0 = 0; r0 < 16; r0 += RPI) {
-      const int tt = r0 + rsub;
-      const int tv = __shfl(tok, tt, 64);      // lane tt resolved this token above
-      const int pv = __shfl(prow, tt, 64);
-      if (tv >= 0) {
-        const u32x4 w = ld16(kvp + (int64_t)pv * row + v_off + chunk * 8);
-        float v[8];
+    for (int j = 0; j < TB; ++j) {
+      // ---- scores of the 16 tokens (MFMA) ----
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) {
+        u32x4 kk;
+        u32x4 qq;
+        if constexpr (PRE) {
+          kk = kf[j][k];
+          qq = qf[k];
+        } else {
+          kk = ktok[j] >= 0 ? ld16(krow[j] + k * 32) : u32x4{0u, 0u, 0u, 0u};
+          qq = q_lds[k][lane];
+        }
+        z = mfma16x16x32(qq, kk, z);
+      }
+      // ---- online softmax (lane holds heads 4*kq+i of token n) ----
+      float pr[4], corr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zi = ktok[j] >= 0 ? z[i] * qk_scale : -INFINITY;
+        const float tmax = max16(zi);
+        const float m_new = fmaxf(m_run[i], tmax);
+        const float ref = m_new == -INFINITY ? 0.0f : m_new;
+        corr[i] = exp2f(m_run[i] - ref);
+        pr[i] = exp2f(zi - ref);
+        l_run[i] = l_run[i] * corr[i] + pr[i];
+        m_run[i] = m_new;
+      }
+      *reinterpret_cast<f32x4*>(&p_lds[wave][n][4 * kq]) = f32x4{pr[0], pr[1], pr[2], pr[3]};
+      if (n == 0) *reinterpret_cast<f32x4*>(&c_lds[wave][4 * kq]) = f32x4{corr[0], corr[1], corr[2], corr[3]};
+      wave_lds_sync();
+      // ---- P.V (vector ALU) ----
+#pragma unroll
+      for (int hh = 0; hh < HT; ++hh) {
+        const float c = c_lds[wave][hh];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] *= c;
+      }
+#pragma unroll
+      for (int v = 0; v < VL; ++v) {
+        const int tt = v * RPI + rsub;
+        u32x4 w;
+        if constexpr (PRE) {
+          w = vf[j][v];
+        } else {
+          const int vt = __shfl(my_tok, 16 * j + tt, 64);
+          const int vr = __shfl(my_row, 16 * j + tt, 64);
+          w = vt >= 0 ? ld16(kvp + (int64_t)vr * row + v_off + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float vv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[2 * e] = bf_lo(w[e]);
-          v[2 * e + 1] = bf_hi(w[e]);
+          vv[2 * e] = bf_lo(w[e]);
+          vv[2 * e + 1] = bf_hi(w[e]);
         }
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
           const float ph = p_lds[wave][tt][hh];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(ph, v[e], acc[hh][e]);
+          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(ph, vv[e], acc[hh][e]);
         }
       }
+      wave_lds_sync();
     }
-    wave_lds_sync();
   }
 
   // ---- per-wave totals ----
@@ -167,13 +218,11 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   __syncthreads();
   // ---- merge the 4 waves ----
   float f[HT];
-  float mstar[HT];
 #pragma unroll
   for (int hh = 0; hh < HT; ++hh) {
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
-    mstar[hh] = ms;
     const float mw = ml_lds[wave][hh][0];
     f[hh] = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
   }
@@ -190,18 +239,22 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
     }
     __syncthreads();
   }
-  // ---- write the workgroup partial: per head (m, l, o[DV]) ----
+  // ---- the workgroup partial: per head (m, l, o[DV]) ----
   float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + 2);
   for (int e = threadIdx.x; e < HT * (DV + 2); e += 256) {
     const int hh = e / (DV + 2), c = e % (DV + 2);
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
     float val;
     if (c == 0) {
-      val = mstar[hh];
+      val = ms;
     } else if (c == 1) {
       float l = 0.0f;
+#pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float mw = ml_lds[w][hh][0];
-        l += mw == -INFINITY ? 0.0f : ml_lds[w][hh][1] * exp2f(mw - mstar[hh]);
+        l += mw == -INFINITY ? 0.0f : ml_lds[w][hh][1] * exp2f(mw - ms);
       }
       val = l;
     } else {
@@ -209,69 +262,75 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
     }
     dst[e] = val;
   }
+}
 
-  // ---- the last workgroup of this (pair, head tile) merges the splits ----
-  __shared__ int last_flag;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last_flag = atomicAdd(&counters[p * nht + ht], 1) == nsplit - 1;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();  // acquire: the other workgroups' partials are visible
-  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * (DV + 2);
+// One workgroup per (query head, batch): combine the splits.
+template <int DV>
+__global__ __launch_bounds__(DV < 64 ? 64 : DV) void k_merge(const float* __restrict__ part, float* __restrict__ out,
+                                                             float* __restrict__ lse, int Hq, int Hkv, int G, int HT,
+                                                             int nht, int nsplit) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int h = hq / G, g = hq % G;
+  const int p = b * Hkv + h, ht = g / HT, hh = g % HT;
+  const float* base = part + (((int64_t)p * nht + ht) * nsplit) * HT * (DV + 2) + hh * (DV + 2);
   const int64_t sstride = (int64_t)HT * (DV + 2);
-  for (int e = threadIdx.x; e < HT * DV; e += 256) {
-    const int hh = e / DV, c = e % DV;
-    const int g = ht * HT + hh;
-    if (g >= G) continue;
-    const float* ph = base + hh * (DV + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ph[sp * sstride]);
-    float L = 0.0f, O = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ms = ph[sp * sstride];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      L += ph[sp * sstride + 1] * w;
-      O += ph[sp * sstride + 2 + c] * w;
-    }
-    const int64_t oh = (int64_t)b * Hq + (int64_t)h * G + g;
-    out[oh * DV + c] = L > 0.0f ? O / L : 0.0f;
-    if (lse && c == 0) lse[oh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride]);
+  float L = 0.0f, O = 0.0f;
+  const int c = threadIdx.x;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = base[s * sstride];
+    const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    L += base[s * sstride + 1] * w;
+    if (c < DV) O += base[s * sstride + 2 + c] * w;
   }
-  if (threadIdx.x == 0) counters[p * nht + ht] = 0;  // ready for the next call
+  if (c < DV) out[((int64_t)b * Hq + hq) * DV + c] = L > 0.0f ? O / L : 0.0f;
+  if (lse && c == 0) lse[(int64_t)b * Hq + hq] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Launch shape: head tiles of HT <= 16 heads; each wave batches TB 16-token
+// tiles, as many as fit a budget of about 160 VGPRs for the P.V accumulators
+// (HT*8) plus the prefetched K fragments and V chunks of the batch; splits are
+// sized for about 1024 workgroups. The 576-dim (MLA) rows are not prefetched.
+static constexpr int head_tile(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
+static constexpr bool prefetch_rows(int D) { return D <= 256; }
+static constexpr int tiles_per_batch(int D, int DV, int HT) {
+  if (!prefetch_rows(D)) return 1;
+  const int per_tile = (D / 32) * 4 + (16 / (64 / (DV / 8))) * 4;
+  const int room = 160 - HT * 8 - (D / 32) * 4;
+  return room >= 4 * per_tile ? 4 : room >= 2 * per_tile ? 2 : 1;
 }
 
 bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
-  int HT = 1;
-  while (HT < G && HT < 16) HT <<= 1;
+  const int HT = head_tile(G);
   const int nht = (G + HT - 1) / HT;
-  // Aim for about 1024 workgroups; splits are whole multiples of 64 tokens
-  // (4 waves x 16-token tiles).
+  const int wg_tokens = 4 * 16 * tiles_per_batch(D, DV, HT);
   const int units = pairs * nht;
-  int want = (1024 + units - 1) / units;
+  const int want = (1024 + units - 1) / units;
   int tps = (kt + want - 1) / want;
-  tps = ((tps + 63) / 64) * 64;
-  if (tps < 64) tps = 64;
+  tps = ((tps + wg_tokens - 1) / wg_tokens) * wg_tokens;
+  if (tps < wg_tokens) tps = wg_tokens;
   const int nsplit = (kt + tps - 1) / tps;
   plan->HT = HT;
   plan->nht = nht;
   plan->tps = tps;
   plan->nsplit = nsplit;
-  plan->cnt_bytes = (((size_t)pairs * nht * sizeof(int)) + 255) & ~(size_t)255;
-  plan->part_bytes = plan->cnt_bytes + (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
-  (void)D;
+  plan->part_bytes = (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
   return true;
 }
 
 template <int D, int DV, int HT>
 static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
-  int* counters = reinterpret_cast<int*>(a.part);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.part) + pl.cnt_bytes);
-  hipLaunchKernelGGL((k_attend<D, DV, HT>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, part,
-                     counters, a.out, a.lse, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+  constexpr int TB = tiles_per_batch(D, DV, HT);
+  hipLaunchKernelGGL((k_attend<D, DV, HT, TB, prefetch_rows(D)>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
+                     (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
                      pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid((unsigned)a.Hq, (unsigned)a.B);
+  hipLaunchKernelGGL(k_merge<DV>, mgrid, dim3(DV < 64 ? 64 : DV), 0, st, (const float*)a.part, a.out, a.lse, a.Hq,
+                     a.Hkv, a.G, pl.HT, pl.nht, pl.nsplit);
   return hipGetLastError();
 }
 

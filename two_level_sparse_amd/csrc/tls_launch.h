@@ -59,7 +59,7 @@ struct DecodeArgs {
   const uint16_t* kv;
   const int32_t* slot_map;  // NULL = identity
   const int32_t* token_idx;
-  void* part;               // workspace: split counters, then partial results
+  void* part;               // workspace: partial results of the splits
   float* out;
   float* lse;               // may be NULL
   int pairs, B, Hq, Hkv, G, D, DV, row, v_off, bs, kt, slots;
@@ -68,8 +68,7 @@ struct DecodeArgs {
 };
 struct DecodePlan {
   int HT, nht, tps, nsplit;
-  size_t cnt_bytes;   // split counters at the start of the workspace
-  size_t part_bytes;  // whole workspace
+  size_t part_bytes;  // partial results (m, l, o) per split
 };
 bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t st);
