@@ -88,6 +88,7 @@ def main():
     ap.add_argument("--config", default="c3_128k_gqa", choices=[k for k in W.CONFIGS if not W.CONFIGS[k].steps])
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for 1 GiB)")
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--chunks", type=int, default=1, help="batch chunks pipelined on separate streams")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -99,7 +100,7 @@ def main():
     import torch
 
     import two_level_sparse_amd as T
-    from two_level_sparse_amd.runtime import Cache, Decoder, bf16
+    from two_level_sparse_amd.runtime import Cache, Decoder, PipelinedDecoder, bf16
 
     T.load_library()
     s = W.CONFIGS[args.config]
@@ -121,7 +122,7 @@ def main():
         c.summ, c.codes, c.scale = base.summ.clone(), base.codes.clone(), base.scale.clone()
         caches.append(c)
     qs = [bf16(q0)] + [bf16(W.gen_q(s.with_(seed=s.seed + 100 * r))) for r in range(1, R)]
-    dec = Decoder(s)
+    dec = PipelinedDecoder(s, args.chunks) if args.chunks > 1 else Decoder(s)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -140,10 +141,15 @@ def main():
         stream.wait_stream(side)
         torch.cuda.synchronize()
 
+    pipelined = args.chunks > 1
+
     def one_step(i, ev=None):
         r = i % R
         if graphs is not None:
             graphs[r].replay()
+            return
+        if pipelined:
+            dec.step(qs[r], caches[r])
             return
         dec.select_blocks(qs[r], caches[r])
         dec.select_tokens(qs[r], caches[r])
@@ -165,7 +171,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        one_step(i, None if graphs is not None else evs[i])
+        one_step(i, None if (graphs is not None or pipelined) else evs[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -173,7 +179,7 @@ def main():
     step_s = ms_step / 1e3
 
     dec_ms = None
-    if graphs is None:
+    if graphs is None and not pipelined:
         dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     roof = None
     if dec_ms:
@@ -197,7 +203,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{s.name}: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim {s.D}/{s.DV}, "
                                f"context {s.N}, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, {s.r} INT4 label channels",
-                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs)},
+                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs), "chunks": args.chunks},
         "hbm": {"algorithmic_bytes_per_step": ab["total"],
                 "achieved_GBps": round(ab["total"] / step_s / 1e9, 1),
                 "frac_of_peak": round(ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, 4)},

@@ -117,8 +117,11 @@ def test_workspace_too_small_is_rejected():
     run = GpuRun(s, q, kv, lab)
     d = run.dec
     with pytest.raises(T.TlsError) as e:
-        T.tls_select_tokens(d.shape, run.qd, run.cache.label_ch, run.cache.codes, run.cache.scale, d.block_idx,
-                            d.token_idx, d.ws[T.TLS_WS_TOKENS], 16)
+        T.tls_sparse_decode(d.shape, run.qd, run.cache.kv, None, 0, d.token_idx, d.out, d.lse,
+                            d.ws[T.TLS_WS_DECODE], 16)
+    assert e.value.code == T.TLS_ERR_WORKSPACE
+    with pytest.raises(T.TlsError) as e:
+        T.tls_select_blocks(d.shape, run.qd, run.cache.summ, d.block_idx, None, d.ws[T.TLS_WS_BLOCKS], 16)
     assert e.value.code == T.TLS_ERR_WORKSPACE
 
 

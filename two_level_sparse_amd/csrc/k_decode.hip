@@ -6,11 +6,11 @@
 // the gathered K/V rows, so each gathered row is read once per head tile.
 //
 // k_attend: workgroup = 4 wavefronts = one (pair, head tile, token split).
-// A wave owns batches of TB 16-token tiles:
-//   - lane l resolves token l of the batch (one index load per lane, slot map
-//     applied), and the rows' K fragments (and, for GQA, the V chunks) of all
-//     TB tiles are requested before any arithmetic, so a wave keeps
-//     TB * 16 rows in flight;
+// A wave owns 64-token chunks of the split:
+//   - lane l resolves token l of the chunk (one index load per lane, slot map
+//     applied); the chunk is then streamed as four 16-token tiles whose K
+//     fragments and V chunks are loaded one tile ahead (double-buffered), with
+//     invalid tokens pointed at a real row and masked, so no load is guarded;
 //   - q.K^T on MFMA (16x16x32 bf16): A = the tile's query heads (rows, zero
 //     padded to 16), B = the 16 gathered key rows (columns);
 //   - online softmax per head in the exp2 domain (scale folded with log2 e);
@@ -26,7 +26,7 @@
 
 namespace tls {
 
-template <int D, int DV, int HT, int TB, bool PRE>
+template <int D, int DV, int HT, bool PRE, bool SMAP>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map,
                                                 const int32_t* __restrict__ token_idx, float* __restrict__ part,
@@ -37,8 +37,7 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   constexpr int CPR = DV / 8;    // 16-byte chunks per value row
   constexpr int RPI = 64 / CPR;  // value rows per wave load
   constexpr int VL = 16 / RPI;   // value loads per 16-token tile
-  constexpr int BT = TB * 16;    // tokens per wave batch
-  static_assert(D % 32 == 0 && 64 % CPR == 0 && CPR <= 64 && BT <= 64, "unsupported shape");
+  static_assert(D % 32 == 0 && 64 % CPR == 0 && CPR <= 64, "unsupported shape");
 
   __shared__ float p_lds[4][16][16];  // [wave][token][head]
   __shared__ float c_lds[4][16];      // [wave][head] rescale factors
@@ -52,7 +51,7 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   const int chunk = lane % CPR, rsub = lane / CPR;
 
   // Query fragments of this lane's MFMA row (head ht*HT + n): in registers,
-  // or (without row prefetch, i.e. the wide MLA rows) in LDS to free registers.
+  // or (for the wide MLA rows, which are not prefetched) in LDS.
   const int g_row = ht * HT + n;
   const bool row_ok = n < HT && g_row < G;
   __shared__ u32x4 q_lds[PRE ? 1 : KSTEPS][64];
@@ -71,8 +70,8 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
   const int32_t* tix = token_idx + (int64_t)p * kt;
-  const uint16_t* kvp = kv + (slot_map ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
-  const int32_t* smap = slot_map ? slot_map + (int64_t)p * NB : nullptr;
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
+  const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
 
   float m_run[4], l_run[4];
 #pragma unroll
@@ -86,13 +85,16 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
 
-  for (int base = t_begin + wave * BT; base < t_end; base += 4 * BT) {
-    // ---- resolve the batch's tokens: lane l -> token base + l ----
+  // Each wave takes 64-token chunks of the split: lane l resolves token
+  // chunk + l (index, then slot map) once; invalid tokens point at row 0 and
+  // are masked afterwards, so every row load is unconditional.
+  for (int c0 = t_begin + 64 * wave; c0 < t_end; c0 += 256) {
     int my_tok = -1, my_row = 0;
-    if (lane < BT && base + lane < t_end) {
-      const int tok = tix[base + lane];
+    {
+      const int pos = c0 + lane;
+      const int tok = pos < t_end ? tix[pos] : -1;
       if (tok >= 0 && tok < N) {
-        if (smap) {
+        if constexpr (SMAP) {
           const int slot = smap[tok / bs];
           if (slot >= 0 && slot < slots) {  // a block that is not resident is never read
             my_tok = tok;
@@ -104,45 +106,42 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
         }
       }
     }
-    // ---- request every row of the batch (PRE) ----
-    u32x4 kf[PRE ? TB : 1][KSTEPS];
-    int ktok[TB];
-    const uint16_t* krow[TB];
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      ktok[j] = __shfl(my_tok, 16 * j + n, 64);
-      const int r = __shfl(my_row, 16 * j + n, 64);
-      krow[j] = kvp + (int64_t)r * row + 8 * kq;
+    const int ntile = min(4, (t_end - c0 + 15) / 16);
+
+    u32x4 kbuf[2][PRE ? KSTEPS : 1], vbuf[2][PRE ? VL : 1];
+    int ktk[2] = {-1, -1};
+    auto issue = [&](int j, int slot) {
+      ktk[slot] = __shfl(my_tok, 16 * j + n, 64);
       if constexpr (PRE) {
+        const uint16_t* kr = kvp + (int64_t)__shfl(my_row, 16 * j + n, 64) * row + 8 * kq;
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) kf[j][k] = ktok[j] >= 0 ? ld16(krow[j] + k * 32) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    u32x4 vf[PRE ? TB : 1][VL];
-    if constexpr (PRE) {
-#pragma unroll
-      for (int j = 0; j < TB; ++j)
+        for (int k = 0; k < KSTEPS; ++k) kbuf[slot][k] = ld16(kr + k * 32);
 #pragma unroll
         for (int v = 0; v < VL; ++v) {
           const int tt = 16 * j + v * RPI + rsub;
-          const int vt = __shfl(my_tok, tt, 64);
-          const int vr = __shfl(my_row, tt, 64);
-          vf[j][v] = vt >= 0 ? ld16(kvp + (int64_t)vr * row + v_off + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
+          vbuf[slot][v] = ld16(kvp + (int64_t)__shfl(my_row, tt, 64) * row + v_off + chunk * 8);
         }
-    }
+      }
+    };
+    issue(0, 0);
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      if (j >= ntile) break;
+      const int cur = j & 1;
+      if (j + 1 < ntile) issue(j + 1, cur ^ 1);
+      const bool tok_ok = ktk[cur] >= 0;
       // ---- scores of the 16 tokens (MFMA) ----
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = nullptr;
+      if constexpr (!PRE) kr = kvp + (int64_t)__shfl(my_row, 16 * j + n, 64) * row + 8 * kq;
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
-        u32x4 kk;
-        u32x4 qq;
+        u32x4 kk, qq;
         if constexpr (PRE) {
-          kk = kf[j][k];
+          kk = kbuf[cur][k];
           qq = qf[k];
         } else {
-          kk = ktok[j] >= 0 ? ld16(krow[j] + k * 32) : u32x4{0u, 0u, 0u, 0u};
+          kk = ld16(kr + k * 32);
           qq = q_lds[k][lane];
         }
         z = mfma16x16x32(qq, kk, z);
@@ -151,7 +150,7 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
       float pr[4], corr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float zi = ktok[j] >= 0 ? z[i] * qk_scale : -INFINITY;
+        const float zi = tok_ok ? z[i] * qk_scale : -INFINITY;
         const float tmax = max16(zi);
         const float m_new = fmaxf(m_run[i], tmax);
         const float ref = m_new == -INFINITY ? 0.0f : m_new;
@@ -164,23 +163,23 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
       if (n == 0) *reinterpret_cast<f32x4*>(&c_lds[wave][4 * kq]) = f32x4{corr[0], corr[1], corr[2], corr[3]};
       wave_lds_sync();
       // ---- P.V (vector ALU) ----
+      // rescale only when some head's running max moved (wave-uniform test)
+      if (__ballot(corr[0] != 1.0f || corr[1] != 1.0f || corr[2] != 1.0f || corr[3] != 1.0f)) {
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh) {
-        const float c = c_lds[wave][hh];
+        for (int hh = 0; hh < HT; ++hh) {
+          const float c = c_lds[wave][hh];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] *= c;
+          for (int e = 0; e < 8; ++e) acc[hh][e] *= c;
+        }
       }
 #pragma unroll
       for (int v = 0; v < VL; ++v) {
         const int tt = v * RPI + rsub;
+        const int vt = __shfl(my_tok, 16 * j + tt, 64);
         u32x4 w;
-        if constexpr (PRE) {
-          w = vf[j][v];
-        } else {
-          const int vt = __shfl(my_tok, 16 * j + tt, 64);
-          const int vr = __shfl(my_row, 16 * j + tt, 64);
-          w = vt >= 0 ? ld16(kvp + (int64_t)vr * row + v_off + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
+        if constexpr (PRE) w = vbuf[cur][v];
+        else w = ld16(kvp + (int64_t)__shfl(my_row, 16 * j + tt, 64) * row + v_off + chunk * 8);
+        if (vt < 0) w = u32x4{0u, 0u, 0u, 0u};  // masked token: its row may hold anything
         float vv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -264,73 +263,96 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   }
 }
 
-// One workgroup per (query head, batch): combine the splits.
-template <int DV>
-__global__ __launch_bounds__(DV < 64 ? 64 : DV) void k_merge(const float* __restrict__ part, float* __restrict__ out,
-                                                             float* __restrict__ lse, int Hq, int Hkv, int G, int HT,
-                                                             int nht, int nsplit) {
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int h = hq / G, g = hq % G;
-  const int p = b * Hkv + h, ht = g / HT, hh = g % HT;
-  const float* base = part + (((int64_t)p * nht + ht) * nsplit) * HT * (DV + 2) + hh * (DV + 2);
+// One workgroup per (pair, head tile): the split weights 2^(m_s - M) / L of
+// every head are formed once in LDS, then each output channel is one pass of
+// independent loads over the splits.
+constexpr int kMaxSplits = 64;
+template <int DV, int HT>
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
+                                               float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
+  __shared__ float m_lds[kMaxSplits][HT];
+  __shared__ float w_lds[kMaxSplits][HT];
+  const int ht = blockIdx.x, p = blockIdx.y;
+  const int b = p / Hkv, h = p % Hkv;
+  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * (DV + 2);
   const int64_t sstride = (int64_t)HT * (DV + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride]);
-  float L = 0.0f, O = 0.0f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = base[s * sstride];
-    const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-    L += base[s * sstride + 1] * w;
-    if (c < DV) O += base[s * sstride + 2 + c] * w;
+  for (int e = threadIdx.x; e < nsplit * HT; e += 256) {
+    const int s = e / HT, hh = e % HT;
+    m_lds[s][hh] = base[s * sstride + hh * (DV + 2)];
   }
-  if (c < DV) out[((int64_t)b * Hq + hq) * DV + c] = L > 0.0f ? O / L : 0.0f;
-  if (lse && c == 0) lse[(int64_t)b * Hq + hq] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  __syncthreads();
+  if (threadIdx.x < HT) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, m_lds[s][hh]);
+    float L = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = m_lds[s][hh];
+      const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+      L += base[s * sstride + hh * (DV + 2) + 1] * w;
+      w_lds[s][hh] = w;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int s = 0; s < nsplit; ++s) w_lds[s][hh] *= inv;
+    const int g = ht * HT + hh;
+    if (lse && g < G) lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < HT * DV; e += 256) {
+    const int hh = e / DV, c = e % DV;
+    const int g = ht * HT + hh;
+    if (g >= G) continue;
+    const float* src = base + hh * (DV + 2) + 2 + c;
+    float O = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) O = fmaf(src[s * sstride], w_lds[s][hh], O);
+    out[((int64_t)b * Hq + (int64_t)h * G + g) * DV + c] = O;
+  }
 }
 
-// Launch shape: head tiles of HT <= 16 heads; each wave batches TB 16-token
-// tiles, as many as fit a budget of about 160 VGPRs for the P.V accumulators
-// (HT*8) plus the prefetched K fragments and V chunks of the batch; splits are
-// sized for about 1024 workgroups. The 576-dim (MLA) rows are not prefetched.
+// Launch shape: head tiles of HT <= 16 heads; a workgroup takes 256-token
+// chunks (64 per wave); splits are sized for about 512 workgroups and capped
+// at kMaxSplits. The 576-dim (MLA) rows are not prefetched.
 static constexpr int head_tile(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 static constexpr bool prefetch_rows(int D) { return D <= 256; }
-static constexpr int tiles_per_batch(int D, int DV, int HT) {
-  if (!prefetch_rows(D)) return 1;
-  const int per_tile = (D / 32) * 4 + (16 / (64 / (DV / 8))) * 4;
-  const int room = 160 - HT * 8 - (D / 32) * 4;
-  return room >= 4 * per_tile ? 4 : room >= 2 * per_tile ? 2 : 1;
-}
 
 bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
   const int HT = head_tile(G);
   const int nht = (G + HT - 1) / HT;
-  const int wg_tokens = 4 * 16 * tiles_per_batch(D, DV, HT);
   const int units = pairs * nht;
-  const int want = (1024 + units - 1) / units;
+  const int want = (512 + units - 1) / units;
   int tps = (kt + want - 1) / want;
-  tps = ((tps + wg_tokens - 1) / wg_tokens) * wg_tokens;
-  if (tps < wg_tokens) tps = wg_tokens;
+  tps = ((tps + 255) / 256) * 256;
+  const int min_tps = ((kt + kMaxSplits - 1) / kMaxSplits + 255) / 256 * 256;
+  if (tps < min_tps) tps = min_tps;
+  if (tps < 256) tps = 256;
   const int nsplit = (kt + tps - 1) / tps;
   plan->HT = HT;
   plan->nht = nht;
   plan->tps = tps;
   plan->nsplit = nsplit;
   plan->part_bytes = (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
+  (void)D;
   return true;
 }
 
 template <int D, int DV, int HT>
 static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
-  constexpr int TB = tiles_per_batch(D, DV, HT);
-  hipLaunchKernelGGL((k_attend<D, DV, HT, TB, prefetch_rows(D)>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                     (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
-                     pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+  constexpr bool PRE = prefetch_rows(D);
+  if (a.slot_map)
+    hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
+                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+  else
+    hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
+                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid((unsigned)a.Hq, (unsigned)a.B);
-  hipLaunchKernelGGL(k_merge<DV>, mgrid, dim3(DV < 64 ? 64 : DV), 0, st, (const float*)a.part, a.out, a.lse, a.Hq,
-                     a.Hkv, a.G, pl.HT, pl.nht, pl.nsplit);
+  dim3 mgrid((unsigned)pl.nht, (unsigned)a.pairs);
+  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv, a.G,
+                     pl.nht, pl.nsplit);
   return hipGetLastError();
 }
 

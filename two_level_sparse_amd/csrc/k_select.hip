@@ -16,22 +16,25 @@
 // 16-byte fragment loads are fully used and consecutive blocks are
 // consecutive in memory.
 //
-// k_topk is an exact radix select over order-preserving 32-bit keys of the
-// scores, run by one 1024-thread workgroup per row. The digit width adapts to
-// the key range (histograms of (key - lo) >> shift with 256 bins), so keys that
-// share their upper bits do not pile into one bin. Elements equal to the
-// threshold key are taken in index order, which realises the lower-index tie
-// rule; the output is written ascending via one block-wide scan.
+// The top-k is an exact radix select over order-preserving 32-bit keys of the
+// scores, run by one 1024-thread workgroup per row (block_topk). Elements
+// equal to the threshold key are taken in index order, which realises the
+// lower-index tie rule; the output is written ascending via one block-wide
+// scan. The token stage scores its candidates on MFMA in a kernel spread over
+// the whole chip (the G heads times r label channels product is a dense
+// contraction; INT4 codes are exact in bf16), then selects per pair.
 #include "tls_dev.h"
 #include "tls_launch.h"
 
 namespace tls {
 
 // ----------------------------------------------------------- block scores --
-template <int MT, int NSUB>
+template <int MT, int NSUB, int KC, int UNR>
 __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ summ, float* __restrict__ S,
                                                       int Hq, int Hkv, int G, int D, int64_t NB) {
+  // KC = D/32 channel chunks when known at compile time (0: from D at run
+  // time); UNR chunks are unrolled so their summary loads are all in flight.
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -53,8 +56,10 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < D; c0 += 32) {
-    const int off = c0 + 8 * kq;
+  const int nchunk = KC > 0 ? KC : D / 32;
+#pragma unroll UNR
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int off = ci * 32 + 8 * kq;
     u32x4 kmx[NSUB], kmn[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -96,12 +101,23 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
   }
 }
 
-template <int MT, int NSUB>
-static void go_blocks(const BlockScoreArgs& a, hipStream_t st) {
+template <int MT, int NSUB, int KC, int UNR>
+static void go_blocks_k(const BlockScoreArgs& a, hipStream_t st) {
   const int64_t per_wg = 4 * 16 * NSUB;
   dim3 grid((unsigned)((a.NB + per_wg - 1) / per_wg), (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_score_blocks<MT, NSUB>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G, a.D,
-                     a.NB);
+  hipLaunchKernelGGL((k_score_blocks<MT, NSUB, KC, UNR>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G,
+                     a.D, a.NB);
+}
+
+template <int MT, int NSUB>
+static void go_blocks(const BlockScoreArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: go_blocks_k<MT, NSUB, 2, 2>(a, st); break;
+    case 128: go_blocks_k<MT, NSUB, 4, 4>(a, st); break;
+    case 256: go_blocks_k<MT, NSUB, 8, 4>(a, st); break;
+    case 576: go_blocks_k<MT, NSUB, 18, 2>(a, st); break;
+    default: go_blocks_k<MT, NSUB, 0, 1>(a, st); break;
+  }
 }
 
 hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st) {
@@ -120,198 +136,102 @@ hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ----------------------------------------------------------- token scores --
-// One thread per candidate. The label-channel query values of the G heads sit
-// in LDS (read as broadcasts); the candidate's packed codes are one 8- or
-// 16-byte load.
-template <int RMAX>
-__global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
-                                                      const int32_t* __restrict__ label_ch,
-                                                      const uint8_t* __restrict__ codes,
-                                                      const float* __restrict__ scale,
-                                                      const int32_t* __restrict__ block_idx, float* __restrict__ A,
-                                                      int Hq, int Hkv, int G, int D, int64_t N, int bs, int r,
-                                                      int kb) {
-  __shared__ float ql[128 * RMAX];
-  const int p = blockIdx.y;
-  const int b = p / Hkv, h = p % Hkv;
-  const int32_t* lab = label_ch + (int64_t)h * r;
-  const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-  for (int e = threadIdx.x; e < G * RMAX; e += blockDim.x) {
-    const int g = e / RMAX, i = e % RMAX;
-    ql[e] = i < r ? bf2f(qp[(int64_t)g * D + lab[i]]) : 0.0f;
-  }
-  __syncthreads();
-  const int ncand = kb * bs;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= ncand) return;
-  const int64_t t = (int64_t)block_idx[(int64_t)p * kb + c / bs] * bs + c % bs;
-  float outv = -INFINITY;
-  if (t >= 0 && t < N) {
-    const uint8_t* cp = codes + ((int64_t)p * N + t) * (r / 2);
-    float cv[RMAX];
-#pragma unroll
-    for (int i = 0; i < RMAX; i += 2) {
-      uint32_t byte = i < r ? cp[i / 2] : 0u;
-      cv[i] = (float)((int32_t)(byte << 28) >> 28);
-      cv[i + 1] = (float)((int32_t)(byte << 24) >> 28);
-    }
-    float best = -INFINITY;
-    for (int g = 0; g < G; ++g) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < RMAX; ++i) dot = fmaf(ql[g * RMAX + i], cv[i], dot);
-      best = fmaxf(best, dot);
-    }
-    outv = scale[(int64_t)p * N + t] * best;
-  }
-  A[(int64_t)p * ncand + c] = outv;
-}
-
-hipError_t launch_score_tokens(const TokenScoreArgs& a, hipStream_t st) {
-  const int ncand = a.kb * a.bs;
-  dim3 grid((unsigned)((ncand + 255) / 256), (unsigned)a.pairs);
-  if (a.r <= 16)
-    hipLaunchKernelGGL(k_score_tokens<16>, grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, a.block_idx,
-                       a.A, a.Hq, a.Hkv, a.G, a.D, a.N, a.bs, a.r, a.kb);
-  else
-    hipLaunchKernelGGL(k_score_tokens<32>, grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, a.block_idx,
-                       a.A, a.Hq, a.Hkv, a.G, a.D, a.N, a.bs, a.r, a.kb);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ top-k --
+// Exact top-k of one row per 1024-thread workgroup; keys in registers, thread
+// t owning elements [t*PER, t*PER+PER). Invalid elements carry key 0, below
+// every valid key.
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
+struct alignas(16) TopkLds {
+  uint32_t hist[256];
+  uint32_t red[3][kTopkWaves];
+  uint32_t scan[kTopkWaves];
+  uint32_t sel[2];
+};
+
 // Block-wide exclusive scan of one uint32 per thread; returns the prefix.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh /* kTopkWaves+1 */) {
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh /* kTopkWaves */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      uint32_t t = sh[w];
-      sh[w] = run;
-      run += t;
-    }
-    sh[kTopkWaves] = run;
-  }
-  __syncthreads();
-  return sh[wave] + x - v;
+  uint32_t before = 0u;
+  for (int w = 0; w < wave; ++w) before += sh[w];
+  return before + x - v;
 }
 
+// Selects the K largest keys (ties: lower element index first) and writes
+// their ids ascending to out[0..min(K, valid)), then -1 up to out_len.
+// Radix select on (key - lo) with an adaptive digit position: each pass
+// histograms the next 8 bits below the top set bit of (hi - lo), so clustered
+// keys still spread over the bins; 4 passes at most for 32-bit keys. One wave
+// finds the bin holding the krem-th largest key and clears the histogram.
 template <int PER>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ scores, int n, int K,
-                                                        const int32_t* __restrict__ block_idx, int kb, int bs,
-                                                        int64_t N, int32_t* __restrict__ out, int out_len) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t red[3][kTopkWaves];
-  __shared__ uint32_t scan_sh[kTopkWaves + 1];
-  __shared__ uint32_t sel[2];
-  const int row = blockIdx.x;
+__device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER], uint32_t K, int32_t* out,
+                           int out_len, TopkLds& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* sc = scores + (int64_t)row * n;
-
-  uint32_t key[PER];
-  int32_t id[PER];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nval = 0u;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int c = tid * PER + e;
-    key[e] = 0u;
-    id[e] = c;
-    if (c < n) {
-      bool valid = true;
-      if (block_idx) {
-        const int64_t t = (int64_t)block_idx[(int64_t)row * kb + c / bs] * bs + c % bs;
-        valid = t >= 0 && t < N;
-        id[e] = (int32_t)t;
-      }
-      if (valid) {
-        key[e] = order_key(sc[c]);
-        kmin = min(kmin, key[e]);
-        kmax = max(kmax, key[e]);
-        ++nval;
-      }
+  for (int e = 0; e < PER; ++e)
+    if (key[e] != 0u) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+      ++nval;
     }
-  }
-  // block-wide min / max / count of the valid keys
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o, 64));
-    nval += __shfl_xor(nval, o, 64);
-  }
+  kmin = wave_umin(kmin);
+  kmax = wave_umax(kmax);
+  nval = wave_usum(nval);
   if (lane == 0) {
-    red[0][wave] = kmin;
-    red[1][wave] = kmax;
-    red[2][wave] = nval;
+    sh.red[0][wave] = kmin;
+    sh.red[1][wave] = kmax;
+    sh.red[2][wave] = nval;
   }
+  if (tid < 256) sh.hist[tid] = 0u;
   __syncthreads();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, total = 0u;
+#pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
-    lo = min(lo, red[0][w]);
-    hi = max(hi, red[1][w]);
-    total += red[2][w];
+    lo = min(lo, sh.red[0][w]);
+    hi = max(hi, sh.red[1][w]);
+    total += sh.red[2][w];
   }
-  const uint32_t kk = (uint32_t)K < total ? (uint32_t)K : total;
-  uint32_t thr, krem;
-  if (kk == total) {  // keep every valid element
-    thr = 0u;
-    krem = 0u;
-  } else {
+  const uint32_t kk = K < total ? K : total;
+  uint32_t thr = 0u, krem = 0u;  // kk == total: keep every valid element
+  if (kk < total) {
     krem = kk;
-    if (tid == 0) {
-      sel[0] = 0u;
-      sel[1] = 0u;
-    }
     while (hi > lo) {
       const uint32_t diff = hi - lo;
       const int nbits = 32 - __clz(diff);
       const int shift = nbits > 8 ? nbits - 8 : 0;
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int e = 0; e < PER; ++e)
-        if (key[e] >= lo && key[e] <= hi && key[e] != 0u) atomicAdd(&hist[(key[e] - lo) >> shift], 1u);
+        if (key[e] >= lo && key[e] <= hi) atomicAdd(&sh.hist[(key[e] - lo) >> shift], 1u);
       __syncthreads();
       if (wave == 0) {
-        uint32_t hb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
+        // lane l holds bins 255-4l .. 252-4l, so a prefix scan over lanes
+        // counts the keys in the bins above
+        const int b0 = 252 - 4 * lane;
+        const u32x4 hb = *reinterpret_cast<const u32x4*>(&sh.hist[b0]);
+        *reinterpret_cast<u32x4*>(&sh.hist[b0]) = u32x4{0u, 0u, 0u, 0u};  // ready for the next pass
         const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
-        uint32_t suf = mine;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          uint32_t y = __shfl_down(suf, o, 64);
-          if (lane + o < 64) suf += y;
-        }
-        uint32_t above = suf - mine;
+        uint32_t above = wave_incl_scan(mine) - mine;
 #pragma unroll
         for (int i = 3; i >= 0; --i) {
           if (above < krem && krem <= above + hb[i]) {
-            sel[0] = 4 * lane + i;
-            sel[1] = above;
+            sh.sel[0] = b0 + i;
+            sh.sel[1] = above;
           }
           above += hb[i];
         }
       }
       __syncthreads();
-      const uint32_t d = sel[0];
-      krem -= sel[1];
+      const uint32_t d = sh.sel[0];
+      krem -= sh.sel[1];
       const uint32_t nlo = lo + (d << shift);
       const uint32_t span = shift == 0 ? 0u : ((1u << shift) - 1u);
       hi = (hi - nlo) > span ? nlo + span : hi;
       lo = nlo;
-      __syncthreads();
     }
     thr = lo;
   }
@@ -322,10 +242,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     gt += (key[e] > thr) ? 1u : 0u;
     eq += (key[e] == thr && key[e] != 0u) ? 1u : 0u;
   }
-  const uint32_t pre = block_exclusive_scan(gt | (eq << 16), scan_sh);
+  const uint32_t pre = block_exclusive_scan(gt | (eq << 16), sh.scan);
   uint32_t eq_before = pre >> 16;
   uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem);
-  int32_t* o = out + (int64_t)row * out_len;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     bool take = key[e] > thr;
@@ -334,26 +253,231 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       ++eq_before;
     }
     if (take) {
-      if (pos < kk) o[pos] = id[e];  // never more than kk entries
+      if (pos < kk) out[pos] = id[e];  // never more than kk entries
       ++pos;
     }
   }
-  for (int i = (int)kk + tid; i < out_len; i += kTopkThreads) o[i] = -1;
+  for (int i = (int)kk + tid; i < out_len; i += kTopkThreads) out[i] = -1;
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  const int per = (a.n + kTopkThreads - 1) / kTopkThreads;
-  dim3 grid((unsigned)a.rows);
-#define TLS_TOPK(P)                                                                                              \
-  hipLaunchKernelGGL(k_topk<P>, grid, dim3(kTopkThreads), 0, st, a.scores, a.n, a.K, a.block_idx, a.kb, a.bs, a.N, \
-                     a.out, a.out_len)
-  if (per <= 1) TLS_TOPK(1);
-  else if (per <= 2) TLS_TOPK(2);
-  else if (per <= 4) TLS_TOPK(4);
-  else if (per <= 8) TLS_TOPK(8);
-  else if (per <= 16) TLS_TOPK(16);
+// Top-Kb of the block scores of one pair per workgroup.
+template <int PER>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_blocks(const float* __restrict__ S, int n, int K,
+                                                               int32_t* __restrict__ out) {
+  __shared__ TopkLds sh;
+  const int row = blockIdx.x;
+  const float* sc = S + (int64_t)row * n;
+  uint32_t key[PER];
+  int32_t id[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = threadIdx.x * PER + e;
+    id[e] = c;
+    key[e] = c < n ? order_key(sc[c]) : 0u;
+  }
+  block_topk<PER>(key, id, (uint32_t)K, out + (int64_t)row * K, K, sh);
+}
+
+// ----------------------------------------------------------- token stage --
+// Candidate c of a pair is token block_idx[c / bs] * bs + c % bs (ascending
+// with c); it exists only when that token is < N.
+__device__ __forceinline__ int64_t cand_token(const int32_t* bidx, int c, int bs, int bsh, int64_t N) {
+  const int q = bsh >= 0 ? (c >> bsh) : c / bs;
+  const int64_t t = (int64_t)bidx[q] * bs + (c - q * bs);
+  return (t >= 0 && t < N) ? t : -1;
+}
+
+// Label-channel scores of 1024 candidates per workgroup (4 waves x 16 tiles of
+// 16). Sixteen candidates times sixteen heads is one MFMA (16x16x32 bf16):
+// A = q on the label channels (heads x channels, zero padded to 32 channels),
+// B = the candidates' INT4 codes widened to bf16 (exact). The epilogue takes
+// the max over the heads and multiplies by the token's scale (non-negative,
+// so the order of max and scale is immaterial). All loads of a wave are
+// issued before its MFMAs. Scores go to A[pair, candidate].
+template <int MT, int RB>
+__global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
+                                                      const int32_t* __restrict__ label_ch,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ scale,
+                                                      const int32_t* __restrict__ block_idx, float* __restrict__ A,
+                                                      int Hq, int Hkv, int G, int D, int64_t N, int bs, int bsh,
+                                                      int r, int kb) {
+  constexpr int TPW = 16;  // tiles per wave
+  const int p = blockIdx.y;
+  const int b = p / Hkv, h = p % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int ncand = kb * bs;
+  const int rb = r / 2;
+  const int32_t* bidx = block_idx + (int64_t)p * kb;
+  const uint8_t* cbase = codes + (int64_t)p * N * rb;
+  const float* sbase = scale + (int64_t)p * N;
+  const int32_t* lab = label_ch + (int64_t)h * r;
+  // Two independent load chains, both issued before any wait: label channel
+  // -> query elements, and block number -> codes and scale.
+  int ch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+
+  const int c0 = blockIdx.x * (4 * TPW * 16) + wave * (TPW * 16);
+  uint32_t cw[TPW];
+  float tsc[TPW];
+  bool ok[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int c = c0 + u * 16 + n;
+    const int64_t t = c < ncand ? cand_token(bidx, c, bs, bsh, N) : -1;
+    ok[u] = t >= 0;
+    const int64_t ts = ok[u] ? t : 0;  // masked candidates read token 0 of the pair
+    const uint8_t* cp = cbase + ts * rb;
+    if constexpr (RB > 0) {
+      cw[u] = *reinterpret_cast<const uint32_t*>(cp + (4 * kq < RB ? 4 * kq : 0));
+    } else {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= (uint32_t)cp[min(4 * kq + e, rb - 1)] << (8 * e);
+      cw[u] = w;
+    }
+    tsc[u] = sbase[ts];
+  }
+  // A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7 (clamped loads,
+  // out-of-range entries zeroed after).
+  u32x4 qa[MT];
+  {
+    const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int g = m * 16 + n;
+      const uint16_t* qr = qp + (int64_t)min(g, G - 1) * D;
+      uint32_t hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = qr[ch[e]];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (g >= G || 8 * kq + e >= r) hv[e] = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    uint32_t w = cw[u];
+    if constexpr (RB > 0) {
+      if (4 * kq >= RB) w = 0u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kq + e >= rb) w &= ~(0xFFu << (8 * e));
+    }
+    u32x4 bop;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // code of channel 8kq + 2e
+      const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // code of channel 8kq + 2e + 1
+      bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const f32x4 a = mfma16x16x32(qa[m], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (m * 16 + 4 * kq + i < G) best = fmaxf(best, a[i]);
+    }
+    best = fmaxf(best, __shfl_xor(best, 16, 64));
+    best = fmaxf(best, __shfl_xor(best, 32, 64));
+    const int c = c0 + u * 16 + n;
+    if (kq == 0 && c < ncand) A[(int64_t)p * ncand + c] = ok[u] ? tsc[u] * best : 0.0f;
+  }
+}
+
+// Top-Kt' of the candidate scores of one pair per workgroup; ids are tokens.
+template <int PER>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_tokens(const float* __restrict__ A,
+                                                               const int32_t* __restrict__ block_idx,
+                                                               int32_t* __restrict__ token_idx, int64_t N, int bs,
+                                                               int bsh, int kb, int kt) {
+  __shared__ TopkLds sh;
+  __shared__ int32_t bidx_lds[kTopkThreads * PER];  // kb <= ncand
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const int ncand = kb * bs;
+  for (int i = tid; i < kb; i += kTopkThreads) bidx_lds[i] = block_idx[(int64_t)p * kb + i];
+  const float* sc = A + (int64_t)p * ncand;
+  float v[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = tid * PER + e;
+    v[e] = sc[c < ncand ? c : 0];
+  }
+  __syncthreads();
+  uint32_t key[PER];
+  int32_t id[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = tid * PER + e;
+    const int64_t t = c < ncand ? cand_token(bidx_lds, c, bs, bsh, N) : -1;
+    key[e] = t >= 0 ? order_key(v[e]) : 0u;
+    id[e] = (int32_t)t;
+  }
+  block_topk<PER>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh);
+}
+
+#define TLS_PER_SWITCH(per, MACRO) \
+  if (per <= 1) MACRO(1);          \
+  else if (per <= 2) MACRO(2);     \
+  else if (per <= 4) MACRO(4);     \
+  else if (per <= 8) MACRO(8);     \
+  else if (per <= 16) MACRO(16);   \
   else return hipErrorInvalidValue;
-#undef TLS_TOPK
+
+hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* out, hipStream_t st) {
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+#define TLS_GO(P) hipLaunchKernelGGL(k_topk_blocks<P>, dim3(rows), dim3(kTopkThreads), 0, st, S, n, K, out)
+  TLS_PER_SWITCH(per, TLS_GO)
+#undef TLS_GO
+  return hipGetLastError();
+}
+
+static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }
+
+template <int MT, int RB>
+static void go_score_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
+  const int ncand = a.kb * a.bs;
+  dim3 grid((unsigned)((ncand + 1023) / 1024), (unsigned)a.pairs);
+  hipLaunchKernelGGL((k_score_tokens<MT, RB>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, a.block_idx,
+                     A, a.Hq, a.Hkv, a.G, a.D, a.N, a.bs, log2_or_neg(a.bs), a.r, a.kb);
+}
+
+template <int MT>
+static void go_score_tokens_rb(const TokenSelectArgs& a, float* A, hipStream_t st) {
+  switch (a.r) {
+    case 8: go_score_tokens<MT, 4>(a, A, st); break;
+    case 16: go_score_tokens<MT, 8>(a, A, st); break;
+    case 32: go_score_tokens<MT, 16>(a, A, st); break;
+    default: go_score_tokens<MT, 0>(a, A, st); break;
+  }
+}
+
+hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
+  switch ((a.G + 15) / 16) {
+    case 1: go_score_tokens_rb<1>(a, A, st); break;
+    case 2: go_score_tokens_rb<2>(a, A, st); break;
+    case 3: go_score_tokens_rb<3>(a, A, st); break;
+    case 4: go_score_tokens_rb<4>(a, A, st); break;
+    case 5: go_score_tokens_rb<5>(a, A, st); break;
+    case 6: go_score_tokens_rb<6>(a, A, st); break;
+    case 7: go_score_tokens_rb<7>(a, A, st); break;
+    case 8: go_score_tokens_rb<8>(a, A, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per = (a.kb * a.bs + kTopkThreads - 1) / kTopkThreads;
+#define TLS_GO(P)                                                                                                  \
+  hipLaunchKernelGGL(k_topk_tokens<P>, dim3(a.pairs), dim3(kTopkThreads), 0, st, A, a.block_idx, a.token_idx, a.N, \
+                     a.bs, log2_or_neg(a.bs), a.kb, a.kt)
+  TLS_PER_SWITCH(per, TLS_GO)
+#undef TLS_GO
   return hipGetLastError();
 }
 

@@ -145,8 +145,7 @@ int tls_select_blocks(const tls_shape_t* shape, const void* q, const void* summ,
   BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB};
   hipError_t e = launch_score_blocks(sa, st);
   if (e != hipSuccess) return hip_error(e, "score_blocks launch");
-  TopkArgs ta{S, d.pairs, (int)d.NB, d.kb, nullptr, 0, 1, d.N, block_idx, d.kb};
-  e = launch_topk(ta, st);
+  e = launch_topk_blocks(S, d.pairs, (int)d.NB, d.kb, block_idx, st);
   return e == hipSuccess ? TLS_OK : hip_error(e, "topk(blocks) launch");
 }
 
@@ -161,15 +160,10 @@ int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* la
     return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
   if (!ws || ws_len < ws_bytes(d, TLS_WS_TOKENS))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_TOKENS));
-  hipStream_t st = (hipStream_t)stream;
-  float* A = (float*)ws;
-  TokenScoreArgs sa{(const uint16_t*)q, label_ch, codes, scale, block_idx, A, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.bs,
-                    d.r, d.kb, d.N};
-  hipError_t e = launch_score_tokens(sa, st);
-  if (e != hipSuccess) return hip_error(e, "score_tokens launch");
-  TopkArgs ta{A, d.pairs, d.kb * d.bs, d.kt, block_idx, d.kb, d.bs, d.N, token_idx, d.kt};
-  e = launch_topk(ta, st);
-  return e == hipSuccess ? TLS_OK : hip_error(e, "topk(tokens) launch");
+  TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
+                    d.bs, d.r, d.kb, d.kt, d.N};
+  hipError_t e = launch_select_tokens(a, (float*)ws, (hipStream_t)stream);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "select_tokens launch");
 }
 
 int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,

@@ -37,16 +37,85 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Reductions across the 16 lanes that share lane/16.
+// ---- cross-lane helpers on DPP (data-parallel primitives: register moves
+// between lanes of a 16-lane row, no LDS round trip) and readlane.
+enum : int {
+  kDppQuadXor1 = 0xB1,     // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,     // quad_perm [2,3,0,1]
+  kDppRowShr1 = 0x111,     // row_shr:1 (lanes without a source read 0)
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowMirror = 0x140,
+  kDppRowHalfMirror = 0x141,
+};
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+
+// Reductions across the 16 lanes of a row (lanes that share lane/16); every
+// lane of the row receives the result.
 __device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, dppf<kDppQuadXor1>(v));
+  v = fmaxf(v, dppf<kDppQuadXor2>(v));
+  v = fmaxf(v, dppf<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dppf<kDppRowMirror>(v));
   return v;
 }
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  v += dppf<kDppQuadXor1>(v);
+  v += dppf<kDppQuadXor2>(v);
+  v += dppf<kDppRowHalfMirror>(v);
+  v += dppf<kDppRowMirror>(v);
   return v;
+}
+__device__ __forceinline__ uint32_t umin16(uint32_t v) {
+  v = min(v, dpp<kDppQuadXor1>(v));
+  v = min(v, dpp<kDppQuadXor2>(v));
+  v = min(v, dpp<kDppRowHalfMirror>(v));
+  return min(v, dpp<kDppRowMirror>(v));
+}
+__device__ __forceinline__ uint32_t umax16(uint32_t v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppRowHalfMirror>(v));
+  return max(v, dpp<kDppRowMirror>(v));
+}
+__device__ __forceinline__ uint32_t usum16(uint32_t v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  return v + dpp<kDppRowMirror>(v);
+}
+// Whole-wave reductions (result uniform).
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = umin16(v);
+  return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = umax16(v);
+  return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_usum(uint32_t v) {
+  v = usum16(v);
+  return readlane(v, 0) + readlane(v, 16) + readlane(v, 32) + readlane(v, 48);
+}
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<kDppRowShr1>(v);
+  v += dpp<kDppRowShr2>(v);
+  v += dpp<kDppRowShr4>(v);
+  v += dpp<kDppRowShr8>(v);
+  const uint32_t r0 = readlane(v, 15), r1 = readlane(v, 31), r2 = readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t add = row == 0 ? 0u : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
+  return v + add;
 }
 
 // Orders LDS traffic between lanes of one wavefront.

@@ -26,33 +26,21 @@ struct BlockScoreArgs {
 };
 hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st);
 
-struct TokenScoreArgs {
+// Stage 2 (token scores + top-k) for every pair.
+struct TokenSelectArgs {
   const uint16_t* q;
   const int32_t* label_ch;
   const uint8_t* codes;
   const float* scale;
   const int32_t* block_idx;  // [pairs, kb]
-  float* A;                  // [pairs, kb*bs]
-  int pairs, Hq, Hkv, G, D, bs, r, kb;
+  int32_t* token_idx;        // [pairs, kt], -1 padded
+  int pairs, Hq, Hkv, G, D, bs, r, kb, kt;
   int64_t N;
 };
-hipError_t launch_score_tokens(const TokenScoreArgs& a, hipStream_t st);
+hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A /* [pairs, kb*bs] scores */, hipStream_t st);
 
-// Exact top-k per row of `scores` ([rows, n] float). With block_idx == NULL the
-// selected ids are the column numbers; otherwise column c is token
-// block_idx[row*kb + c/bs]*bs + c%bs and is valid only when that token < N.
-struct TopkArgs {
-  const float* scores;
-  int rows;
-  int n;
-  int K;
-  const int32_t* block_idx;
-  int kb, bs;
-  int64_t N;
-  int32_t* out;  // [rows, out_len], -1 padded
-  int out_len;
-};
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Exact top-K per row of S ([rows, n] float); ids are column numbers.
+hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* out, hipStream_t st);
 
 struct DecodeArgs {
   const uint16_t* q;

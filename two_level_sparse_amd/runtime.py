@@ -45,19 +45,34 @@ class Cache:
         return self
 
 
-class Decoder:
-    """Per-step buffers; `step(q)` enqueues the three calls of one decode step."""
+class CacheView:
+    """Batch rows [b0, b1) of a Cache (contiguous slices, no copy)."""
 
-    def __init__(self, s, device="cuda"):
+    def __init__(self, cache, b0, b1):
+        self.s = cache.s.with_(B=b1 - b0)
+        self.shape = shape_of(self.s)
+        self.kv = cache.kv[b0:b1]
+        self.label_ch = cache.label_ch
+        self.summ = cache.summ[b0:b1]
+        self.codes = cache.codes[b0:b1]
+        self.scale = cache.scale[b0:b1]
+
+
+class Decoder:
+    """Per-step buffers; `step(q)` enqueues the three calls of one decode step.
+    `outputs` may supply the output tensors (e.g. views of larger buffers)."""
+
+    def __init__(self, s, device="cuda", outputs=None):
         self.s = s
         self.shape = shape_of(s)
         self.kb = min(s.Kb, s.NB)
         self.kt = min(s.Kt, self.kb * s.bs)
-        self.block_idx = torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device)
-        self.block_score = torch.empty((s.B, s.Hkv, s.NB), dtype=torch.float32, device=device)
-        self.token_idx = torch.empty((s.B, s.Hkv, self.kt), dtype=torch.int32, device=device)
-        self.out = torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device=device)
-        self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=device)
+        o = outputs or {}
+        self.block_idx = o.get("block_idx", torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device))
+        self.block_score = o.get("block_score", torch.empty((s.B, s.Hkv, s.NB), dtype=torch.float32, device=device))
+        self.token_idx = o.get("token_idx", torch.empty((s.B, s.Hkv, self.kt), dtype=torch.int32, device=device))
+        self.out = o.get("out", torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device=device))
+        self.lse = o.get("lse", torch.empty((s.B, s.Hq), dtype=torch.float32, device=device))
         self.ws_sizes = {w: tls_workspace_size(self.shape, w) for w in (TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE)}
         if min(self.ws_sizes.values()) == 0:
             raise ValueError(f"invalid shape for libtls: {s}")
@@ -84,3 +99,61 @@ class Decoder:
         self.select_tokens(q, cache, stream)
         self.decode(q, cache.kv, stream)
         return self.out
+
+
+class PipelinedDecoder:
+    """One decode step as `chunks` batch chunks, each on its own HIP stream.
+
+    The selection kernels of a chunk are latency-bound and occupy few compute
+    units (one workgroup per (batch, kv head) pair); running the chunks on
+    separate streams lets them overlap the bandwidth-bound summary scan and
+    attention of the other chunks. Each chunk is an ordinary call of the C ABI
+    on contiguous batch slices, with its own workspaces; outputs land in the
+    shared buffers. Streams keep the default priority.
+    """
+
+    def __init__(self, s, chunks, device="cuda"):
+        self.s = s
+        chunks = max(1, min(int(chunks), s.B))
+        edges = [round(i * s.B / chunks) for i in range(chunks + 1)]
+        self.ranges = [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+        self.full = Decoder(s, device)
+        self.parts = []
+        for b0, b1 in self.ranges:
+            outs = {k: getattr(self.full, k)[b0:b1] for k in ("block_idx", "block_score", "token_idx", "out", "lse")}
+            self.parts.append(Decoder(s.with_(B=b1 - b0), device, outputs=outs))
+        self.streams = [torch.cuda.Stream(device=device) for _ in self.ranges]
+        self._views = {}
+
+    @property
+    def out(self):
+        return self.full.out
+
+    @property
+    def lse(self):
+        return self.full.lse
+
+    @property
+    def block_idx(self):
+        return self.full.block_idx
+
+    @property
+    def token_idx(self):
+        return self.full.token_idx
+
+    def _view(self, cache, i):
+        key = (id(cache), i)
+        v = self._views.get(key)
+        if v is None:
+            v = self._views[key] = (cache, CacheView(cache, *self.ranges[i]))
+        return v[1]
+
+    def step(self, q, cache):
+        main = torch.cuda.current_stream()
+        for i, ((b0, b1), dec, st) in enumerate(zip(self.ranges, self.parts, self.streams)):
+            st.wait_stream(main)
+            with torch.cuda.stream(st):
+                dec.step(q[b0:b1], self._view(cache, i), stream=st)
+        for st in self.streams:
+            main.wait_stream(st)
+        return self.full.out
