@@ -1,0 +1,86 @@
+"""GPU parity of the staggered offloaded decode (AsyncTLS pages, section 2B)
+against the oracle's schedule: per step, the transferred blocks T_t, the new
+selection M_t, the token sets (band rule) and the outputs (2e-3) must match."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as W
+from gpu_common import band_check, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import two_level_sparse_amd as T
+    T.load_library()
+
+
+def run_staggered(s, q0, kv, lab, steps, helper):
+    from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
+    qs = W.drift_queries(s, q0, steps)
+    built = oracle.decode(s, q0, kv, lab)
+    ref = oracle.staggered(s, qs, kv, lab, built)
+    cache = Cache(s, kv, lab).build()
+    host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
+    sd = StaggeredDecoder(s, cache, host, bf16(q0))
+    np.testing.assert_array_equal(to_np(sd.mbuf[2]).reshape(s.pairs, -1), built.block_idx)
+    stats = dict(moved=0, token_band=0, max_err=0.0)
+    prev_blocks = built.block_idx
+    for t in range(steps):
+        out = sd.step(bf16(qs[t]), helper=helper)
+        torch.cuda.synchronize()
+        counts, blocks = sd.last_delta()
+        Mt = to_np(sd.mbuf[t % 2]).reshape(s.pairs, -1)
+        np.testing.assert_array_equal(Mt, ref.M[t])
+        np.testing.assert_array_equal(counts, ref.nT[t])
+        for p in range(s.pairs):
+            assert blocks[p, : counts[p]].tolist() == ref.T[t, p, : ref.nT[t, p]].tolist()
+        stats["moved"] += int(counts.sum())
+        # token sets inside M_{t-1}, scored with q_t
+        ti = to_np(sd.dec.token_idx).reshape(s.pairs, -1)
+        for p in range(s.pairs):
+            b, h = divmod(p, s.Hkv)
+            _, cand, cs = oracle.select_tokens_pair(s, qs[t, b, h * s.G:(h + 1) * s.G], lab[h], built.codes[p],
+                                                    built.scale[p], prev_blocks[p])
+            nb, _ = band_check(ti[p], cand, cs, s.Kt)
+            stats["token_band"] += nb
+        o = to_np(out).reshape(s.pairs, s.G, s.DV)
+        err = float(np.max(np.abs(o - ref.out[t])))
+        assert err <= 2e-3, (t, err)
+        stats["max_err"] = max(stats["max_err"], err)
+        prev_blocks = ref.M[t]
+    sd.close()
+    return stats
+
+
+@pytest.mark.parametrize("helper", [False, True])
+def test_staggered_small(helper):
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=21)
+    rng = np.random.default_rng(21)
+    q0 = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    k = rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32)
+    k[..., :4] *= 8
+    kv = W.f32_to_bf16_bits(k)
+    lab = np.tile(np.arange(s.r, dtype=np.int32), (s.Hkv, 1))
+    st = run_staggered(s, q0, kv, lab, steps=16, helper=helper)
+    print(f"[gpu] staggered small helper={helper}: {st}", flush=True)
+    assert st["moved"] > 0
+
+
+def test_staggered_full_256k_offload():
+    """The 256k-context offloaded workload (batch 4, 32/8 heads, Kb=128, Kt=4096),
+    first 8 drift steps, every pair checked."""
+    s = W.CONFIGS["c5_256k_offload"]
+    print("[gpu] offload 256k: generating inputs", flush=True)
+    q0 = W.gen_q(s)
+    kv = W.gen_kv(s)
+    lab = W.label_channels(s, kv[0])
+    st = run_staggered(s, q0, kv, lab, steps=8, helper=True)
+    print(f"[gpu] staggered 256k: {st}", flush=True)

@@ -157,3 +157,91 @@ class PipelinedDecoder:
         for st in self.streams:
             main.wait_stream(st)
         return self.full.out
+
+
+class StaggeredDecoder:
+    """Staggered decode steps over a KV cache held in pinned host memory.
+
+    Step t (AsyncTLS pages, section 2B): the token stage and the attention use
+    M_{t-1}, the blocks chosen at step t-1, which are resident on the device;
+    stage 1 for step t (M_t) runs on a side stream, and a helper thread calls
+    tls_prefetch_delta, which copies only the blocks of M_t missing from the
+    resident cache and writes the slot map of step t+1. The main stream of step
+    t+1 waits for those copies. Stream order makes the side work of step t start
+    after the attention of step t-1 finished, so no slot or map entry a running
+    kernel reads is ever written.
+
+    `cache` holds the summaries and label cache on the device (its `kv` is not
+    read); `host_kv` is the full cache [B,Hkv,N,row] bf16 in pinned memory.
+    """
+
+    def __init__(self, s, cache, host_kv, q0, device="cuda"):
+        self.s = s
+        self.cache = cache
+        self.host_kv = host_kv
+        self.dec = Decoder(s, device)
+        self.kb = self.dec.kb
+        self.cap = 2 * self.kb
+        self.dev_cache = torch.empty((s.B, s.Hkv, self.cap, s.bs, s.row), dtype=torch.bfloat16, device=device)
+        self.maps = [torch.full((s.B, s.Hkv, s.NB), -1, dtype=torch.int32, device=device) for _ in range(2)]
+        self.mbuf = [torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device) for _ in range(3)]
+        self.side = torch.cuda.Stream(device=device)
+        self.events = [torch.cuda.Event() for _ in range(2)]
+        for ev in self.events:
+            ev.record()  # materialise the HIP events
+        # prologue: M_{-1} = stage 1 of q_0, loaded synchronously
+        self.dec.select_blocks(q0, cache, block_idx=self.mbuf[2])
+        torch.cuda.synchronize()
+        init = self.mbuf[2].cpu().numpy().astype(np.int32)
+        self.ctx = tls_offload_create_ctx(self.dec.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
+        self.t = 0
+        self.copied = []
+
+    def step(self, q_t, helper=True):
+        """Enqueue step t; returns the output buffer [B, Hq, DV] (valid after sync)."""
+        import threading
+        from . import tls_offload_slot_map, tls_prefetch_delta
+        t = self.t
+        main = torch.cuda.current_stream()
+        mt = self.mbuf[t % 2]
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self.dec.select_blocks(q_t, self.cache, stream=self.side, block_idx=mt)
+        res = {}
+
+        def prefetch():
+            res["n"] = tls_prefetch_delta(self.ctx, t, mt, self.side, self.events[t % 2])
+
+        th = threading.Thread(target=prefetch) if helper else None
+        if th:
+            th.start()
+        else:
+            prefetch()
+        if t > 0:
+            main.wait_event(self.events[(t - 1) % 2])
+        prev = self.mbuf[2] if t == 0 else self.mbuf[(t - 1) % 2]
+        self.dec.select_tokens(q_t, self.cache, block_idx=prev)
+        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t), slots=self.cap)
+        if th:
+            th.join()
+        self.copied.append(res.get("n", 0))
+        self.t += 1
+        return self.dec.out
+
+    def last_delta(self):
+        from . import tls_offload_last_delta
+        counts = np.zeros(self.s.pairs, dtype=np.int32)
+        blocks = np.zeros((self.s.pairs, self.kb), dtype=np.int32)
+        tls_offload_last_delta(self.ctx, counts, blocks)
+        return counts, blocks
+
+    def close(self):
+        from . import tls_offload_destroy
+        if self.ctx:
+            tls_offload_destroy(self.ctx)
+            self.ctx = None
+
+
+def tls_offload_create_ctx(shape, host_kv, dev_cache, map0, map1, init):
+    from . import tls_offload_create
+    return tls_offload_create(shape, host_kv, dev_cache, map0, map1, init)
