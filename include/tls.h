@@ -170,9 +170,20 @@ const int32_t *tls_offload_slot_map(const tls_offload_t *ctx, int32_t step);
  * host->device copy per transferred block and the next slot map on `side`, and
  * records `copies_done` (a hipEvent_t) on `side`. Step step+1 must wait for
  * that event before reading the resident cache. n_copied_opt (host, may be
- * NULL) receives |T_t| summed over all pairs. */
+ * NULL) receives |T_t| summed over all pairs. The pinned staging buffers of
+ * the context are reused by the next call, which first waits for `side`. */
 int tls_prefetch_delta(tls_offload_t *ctx, int32_t step, const int32_t *dev_block_idx, void *side,
                        void *copies_done, int64_t *n_copied_opt);
+
+/* How tls_prefetch_delta moves the blocks of T_t.
+ *   TLS_COPY_GATHER (default when host_kv, allocated with hipHostMalloc, has
+ *     a device mapping): one kernel on the side stream reads every block of
+ *     T_t from host memory and applies the slot-map changes;
+ *   TLS_COPY_MEMCPY: one hipMemcpyAsync per block plus a full slot-map upload.
+ * Returns TLS_ERR_UNSUPPORTED for GATHER when host_kv has no device mapping.
+ * Either mode may be used at any step. */
+enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1 };
+int tls_offload_set_copy_mode(tls_offload_t *ctx, int mode);
 
 /* Host view of the last transfer (for checking): per pair the count |T_t|
  * and the transferred blocks ascending (host arrays [B*Hkv] and [B*Hkv, Kb']). */

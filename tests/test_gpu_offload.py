@@ -22,14 +22,14 @@ def need_gpu():
     T.load_library()
 
 
-def run_staggered(s, q0, kv, lab, steps, helper):
+def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
     from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
     qs = W.drift_queries(s, q0, steps)
     built = oracle.decode(s, q0, kv, lab)
     ref = oracle.staggered(s, qs, kv, lab, built)
     cache = Cache(s, kv, lab).build()
     host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
-    sd = StaggeredDecoder(s, cache, host, bf16(q0))
+    sd = StaggeredDecoder(s, cache, host, bf16(q0), copy_mode=copy_mode)
     np.testing.assert_array_equal(to_np(sd.mbuf[2]).reshape(s.pairs, -1), built.block_idx)
     stats = dict(moved=0, token_band=0, max_err=0.0)
     prev_blocks = built.block_idx
@@ -60,8 +60,8 @@ def run_staggered(s, q0, kv, lab, steps, helper):
     return stats
 
 
-@pytest.mark.parametrize("helper", [False, True])
-def test_staggered_small(helper):
+@pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0)])
+def test_staggered_small(helper, mode):
     s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=21)
     rng = np.random.default_rng(21)
     q0 = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
@@ -69,8 +69,8 @@ def test_staggered_small(helper):
     k[..., :4] *= 8
     kv = W.f32_to_bf16_bits(k)
     lab = np.tile(np.arange(s.r, dtype=np.int32), (s.Hkv, 1))
-    st = run_staggered(s, q0, kv, lab, steps=16, helper=helper)
-    print(f"[gpu] staggered small helper={helper}: {st}", flush=True)
+    st = run_staggered(s, q0, kv, lab, steps=16, helper=helper, copy_mode=mode)
+    print(f"[gpu] staggered small helper={helper} copy_mode={mode}: {st}", flush=True)
     assert st["moved"] > 0
 
 

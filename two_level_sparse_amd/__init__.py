@@ -28,9 +28,12 @@ TLS_ERR_HIP = -4
 TLS_ERR_STATE = -5
 TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE = 0, 1, 2
 
+TLS_COPY_GATHER, TLS_COPY_MEMCPY = 0, 1
+
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",
             "tls_sparse_decode", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
-            "tls_offload_last_delta", "tls_offload_destroy", "tls_last_error", "tls_version"]
+            "tls_offload_set_copy_mode", "tls_offload_last_delta", "tls_offload_destroy", "tls_last_error",
+            "tls_version"]
 
 
 class tls_shape_t(C.Structure):
@@ -71,6 +74,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_offload_slot_map": (vp, [vp, i32]),
         "tls_prefetch_delta": (C.c_int, [vp, i32, vp, vp, vp, C.POINTER(i64)]),
         "tls_offload_last_delta": (C.c_int, [vp, vp, vp]),
+        "tls_offload_set_copy_mode": (C.c_int, [vp, C.c_int]),
         "tls_offload_destroy": (None, [vp]),
         "tls_last_error": (C.c_char_p, []),
         "tls_version": (C.c_char_p, []),
@@ -157,6 +161,10 @@ def tls_prefetch_delta(ctx, step, dev_block_idx, side_stream, copies_done_event)
     _check(load_library().tls_prefetch_delta(ctx, step, _ptr(dev_block_idx), _stream(side_stream),
                                              copies_done_event.cuda_event, C.byref(n)))
     return n.value
+
+
+def tls_offload_set_copy_mode(ctx, mode):
+    _check(load_library().tls_offload_set_copy_mode(ctx, int(mode)))
 
 
 def tls_offload_last_delta(ctx, counts, blocks):

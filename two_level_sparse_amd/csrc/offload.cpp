@@ -15,6 +15,12 @@
 //      writes map (t+1)%2), and records `copies_done` on the side stream.
 // Capacity 2*Kb' is the least that always fits M_{t-1} u M_t.
 //
+// Copy modes: TLS_COPY_GATHER (default when the pinned host cache has a
+// device mapping) moves the whole step's transfer with one kernel that reads
+// the host blocks directly and patches the slot map with the changes of the
+// last two steps; TLS_COPY_MEMCPY issues one hipMemcpyAsync per block plus a
+// full slot-map upload.
+//
 // Ordering contract (the caller's streams): the side-stream work of step t
 // (stage 1 and this call) must start after the main stream finished step
 // t-1's attention, and step t+1's main-stream work must wait for
@@ -28,6 +34,7 @@
 
 #include "../../include/tls.h"
 #include "tls_api_internal.h"
+#include "tls_launch.h"
 
 using namespace tls;
 
@@ -48,10 +55,20 @@ struct tls_offload {
   int32_t* host_map[2] = {nullptr, nullptr};  // pinned staging of the slot maps
   std::vector<int32_t> last_counts, last_blocks;
   int32_t next_step = 0;
+  int copy_mode = TLS_COPY_MEMCPY;
+  const uint16_t* host_kv_dev = nullptr;  // device mapping of host_kv (gather mode)
+  tls::CopyItem* items = nullptr;          // pinned transfer list (host view)
+  tls::MapItem* map_items = nullptr;       // pinned slot-map changes (host view)
+  const tls::CopyItem* items_dev = nullptr;     // device views of the two lists
+  const tls::MapItem* map_items_dev = nullptr;
+  std::vector<tls::MapItem> prev_changes, cur_changes;
+  std::vector<int32_t> last_pos;           // [pairs*NB] dedupe scratch, -1 when unused
 };
 
 static void free_ctx(tls_offload* c) {
   if (!c) return;
+  if (c->items) (void)hipHostFree(c->items);
+  if (c->map_items) (void)hipHostFree(c->map_items);
   if (c->host_M) (void)hipHostFree(c->host_M);
   for (int i = 0; i < 2; ++i)
     if (c->host_map[i]) (void)hipHostFree(c->host_map[i]);
@@ -89,9 +106,28 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   hipError_t e = hipHostMalloc((void**)&c->host_M, (size_t)d.pairs * d.kb * sizeof(int32_t), hipHostMallocDefault);
   for (int i = 0; i < 2 && e == hipSuccess; ++i)
     e = hipHostMalloc((void**)&c->host_map[i], (size_t)d.pairs * d.NB * sizeof(int32_t), hipHostMallocDefault);
+  if (e == hipSuccess)
+    e = hipHostMalloc((void**)&c->items, (size_t)d.pairs * d.kb * sizeof(tls::CopyItem), hipHostMallocDefault);
+  if (e == hipSuccess)
+    e = hipHostMalloc((void**)&c->map_items, (size_t)d.pairs * d.kb * 4 * sizeof(tls::MapItem), hipHostMallocDefault);
   if (e != hipSuccess) {
     free_ctx(c);
     return hip_error(e, "hipHostMalloc(offload staging)");
+  }
+  {
+    // Gather mode needs device views of the host cache and of both lists.
+    void *dv = nullptr, *di = nullptr, *dm = nullptr;
+    if (hipHostGetDevicePointer(&dv, const_cast<void*>(host_kv), 0) == hipSuccess && dv &&
+        hipHostGetDevicePointer(&di, c->items, 0) == hipSuccess && di &&
+        hipHostGetDevicePointer(&dm, c->map_items, 0) == hipSuccess && dm) {
+      c->host_kv_dev = (const uint16_t*)dv;
+      c->items_dev = (const tls::CopyItem*)di;
+      c->map_items_dev = (const tls::MapItem*)dm;
+      c->copy_mode = TLS_COPY_GATHER;
+      c->last_pos.assign((size_t)d.pairs * d.NB, -1);
+    } else {
+      (void)hipGetLastError();  // not device-mapped: per-block copies
+    }
   }
   // Prologue: M_{-1} goes to slots 0..kb-1 of each pair, copied synchronously.
   for (int p = 0; p < d.pairs; ++p) {
@@ -144,6 +180,8 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   if (e != hipSuccess) return hip_error(e, "copy of M_t to host");
 
   int64_t total = 0;
+  int nitems = 0;
+  c->cur_changes.clear();
   std::vector<std::pair<int64_t, int32_t>> evict;
   std::vector<int32_t> free_slots;
   for (int p = 0; p < d.pairs; ++p) {
@@ -190,6 +228,7 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
         slot_of[blk] = -1;
         owner[sl] = -1;
         free_slots.push_back(sl);
+        c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NB + blk, -1, 0});
       }
       std::sort(free_slots.begin(), free_slots.end());
     }
@@ -198,10 +237,15 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
       const int32_t blk = T[i], sl = free_slots[i];
       slot_of[blk] = sl;
       owner[sl] = blk;
-      e = hipMemcpyAsync(c->dev_cache + ((size_t)p * c->cap + sl) * c->block_elems,
-                         c->host_kv + ((size_t)p * d.N + (size_t)blk * d.bs) * d.row, c->block_elems * 2,
-                         hipMemcpyHostToDevice, st);
-      if (e != hipSuccess) return hip_error(e, "block copy");
+      c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NB + blk, sl, 0});
+      const int64_t src = ((int64_t)p * d.N + (int64_t)blk * d.bs) * d.row;
+      const int64_t dst = ((int64_t)p * c->cap + sl) * (int64_t)c->block_elems;
+      if (c->copy_mode == TLS_COPY_GATHER) {
+        c->items[nitems++] = tls::CopyItem{src, dst};
+      } else {
+        e = hipMemcpyAsync(c->dev_cache + dst, c->host_kv + src, c->block_elems * 2, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_error(e, "block copy");
+      }
     }
     for (int i = 0; i < d.kb; ++i) {
       last[cur[i]] = step;
@@ -209,13 +253,40 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
     }
   }
   const int nxt = (step + 1) & 1;
-  std::memcpy(c->host_map[nxt], c->slot_of.data(), c->slot_of.size() * sizeof(int32_t));
-  e = hipMemcpyAsync(c->dev_map[nxt], c->host_map[nxt], c->slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice,
-                     st);
-  if (e == hipSuccess) e = hipEventRecord((hipEvent_t)copies_done, st);
-  if (e != hipSuccess) return hip_error(e, "slot map upload");
+  if (c->copy_mode == TLS_COPY_GATHER) {
+    // map (step+1)&1 holds the state of two prefetches ago: apply the changes
+    // of the previous and of this prefetch (one entry per index, last wins).
+    int nmap = 0;
+    std::vector<tls::MapItem> both(c->prev_changes);
+    both.insert(both.end(), c->cur_changes.begin(), c->cur_changes.end());
+    for (size_t k = 0; k < both.size(); ++k) c->last_pos[both[k].index] = (int32_t)k;
+    for (size_t k = 0; k < both.size(); ++k)
+      if (c->last_pos[both[k].index] == (int32_t)k) c->map_items[nmap++] = both[k];
+    for (size_t k = 0; k < both.size(); ++k) c->last_pos[both[k].index] = -1;
+    e = tls::launch_gather_blocks(c->host_kv_dev, c->dev_cache, c->items_dev, nitems, c->map_items_dev, nmap,
+                                  c->dev_map[nxt], (int64_t)c->block_elems, st);
+    if (e != hipSuccess) return hip_error(e, "gather launch");
+  } else {
+    std::memcpy(c->host_map[nxt], c->slot_of.data(), c->slot_of.size() * sizeof(int32_t));
+    e = hipMemcpyAsync(c->dev_map[nxt], c->host_map[nxt], c->slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice,
+                       st);
+    if (e != hipSuccess) return hip_error(e, "slot map upload");
+  }
+  c->prev_changes.swap(c->cur_changes);
+  e = hipEventRecord((hipEvent_t)copies_done, st);
+  if (e != hipSuccess) return hip_error(e, "event record");
   c->next_step = step + 1;
   if (n_copied_opt) *n_copied_opt = total;
+  return TLS_OK;
+}
+
+int tls_offload_set_copy_mode(tls_offload_t* c, int mode) {
+  clear_error();
+  if (!c) return set_error(TLS_ERR_INVALID_ARG, "NULL context");
+  if (mode != TLS_COPY_GATHER && mode != TLS_COPY_MEMCPY) return set_error(TLS_ERR_INVALID_ARG, "unknown copy mode");
+  if (mode == TLS_COPY_GATHER && !c->host_kv_dev)
+    return set_error(TLS_ERR_UNSUPPORTED, "host cache has no device mapping; only TLS_COPY_MEMCPY is available");
+  c->copy_mode = mode;
   return TLS_OK;
 }
 

@@ -59,6 +59,21 @@ struct DecodePlan {
   size_t part_bytes;  // partial results (m, l, o) per split
 };
 bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan);
+
+// One transferred block (element offsets into the host cache and the resident
+// cache) and one slot-map change.
+struct CopyItem {
+  int64_t src_elem;
+  int64_t dst_elem;
+};
+struct MapItem {
+  int64_t index;
+  int32_t value;
+  int32_t pad;
+};
+hipError_t launch_gather_blocks(const uint16_t* host_kv_dev, uint16_t* dev_cache, const CopyItem* items, int nitems,
+                                const MapItem* map_items, int nmap, int32_t* slot_map, int64_t block_elems,
+                                hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t st);
 
 }  // namespace tls

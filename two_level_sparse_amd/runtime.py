@@ -175,7 +175,7 @@ class StaggeredDecoder:
     read); `host_kv` is the full cache [B,Hkv,N,row] bf16 in pinned memory.
     """
 
-    def __init__(self, s, cache, host_kv, q0, device="cuda"):
+    def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None):
         self.s = s
         self.cache = cache
         self.host_kv = host_kv
@@ -194,6 +194,9 @@ class StaggeredDecoder:
         torch.cuda.synchronize()
         init = self.mbuf[2].cpu().numpy().astype(np.int32)
         self.ctx = tls_offload_create_ctx(self.dec.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
+        if copy_mode is not None:
+            from . import tls_offload_set_copy_mode
+            tls_offload_set_copy_mode(self.ctx, copy_mode)
         self.t = 0
         self.copied = []
 
