@@ -52,6 +52,23 @@ def algorithmic_bytes(s):
                 attention=rows + q + out + s.B * s.Hq * 4)
 
 
+def measured_traffic(config):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the attention kernel source changed since the counters were taken."""
+    import hashlib
+    prof = ROOT / "profiles" / f"traffic_{config}.txt"
+    src = ROOT / "two_level_sparse_amd" / "csrc" / "k_decode.hip"
+    if not prof.exists():
+        return None
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    for line in prof.read_text().splitlines():
+        if line.startswith("k_attend_traffic_bytes="):
+            kv = dict(tok.split("=") for tok in line.split())
+            if kv.get("source_sha256_prefix") == sha:
+                return int(kv["k_attend_traffic_bytes"])
+    return None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -90,6 +107,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
     ap.add_argument("--chunks", type=int, default=1, help="batch chunks pipelined on separate streams")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 256 MiB device copy before timing (counter calibration for profiles)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -108,7 +127,7 @@ def main():
         return bench_offload(args, s)
     ab = algorithmic_bytes(s)
     touched = ab["total"]
-    R = args.rotate or max(1, math.ceil((1 << 30) / touched))
+    R = args.rotate or max(1, min(64, math.ceil((1 << 30) / touched)))
     log(f"[bench] {s.name}: generating inputs (rotation over {R} cache copies)")
     q0 = W.gen_q(s)
     kv = W.gen_kv(s)
@@ -164,6 +183,12 @@ def main():
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
+    if args.calibrate_copy:  # a copy kernel of known size: 256 MiB read + 256 MiB written
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     K = args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -187,7 +212,8 @@ def main():
     if dec_ms:
         ach = ab["attention"] / (dec_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "kernel": "k_attend (tls_sparse_decode)", "achieved": round(ach, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(s.name),
                 "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"]}
 
     res = {
