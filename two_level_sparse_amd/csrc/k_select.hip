@@ -147,7 +147,7 @@ struct alignas(16) TopkLds {
   uint32_t hist[256];
   uint32_t red[3][kTopkWaves];
   uint32_t scan[kTopkWaves];
-  uint32_t sel[2];
+  uint32_t sel[3];
 };
 
 // Block-wide exclusive scan of one uint32 per thread; returns the prefix.
@@ -163,10 +163,34 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 
 // Selects the K largest keys (ties: lower element index first) and writes
 // their ids ascending to out[0..min(K, valid)), then -1 up to out_len.
-// Radix select on (key - lo) with an adaptive digit position: each pass
-// histograms the next 8 bits below the top set bit of (hi - lo), so clustered
-// keys still spread over the bins; 4 passes at most for 32-bit keys. One wave
-// finds the bin holding the krem-th largest key and clears the histogram.
+// Radix select. The first pass bins the keys' float values linearly between
+// the smallest and the largest (a monotone map, so a bin holds one interval
+// of keys; binning the raw keys instead would put every float of one binade
+// into a single bin). The later passes histogram (key - lo) >> shift, the next
+// 8 bits below the top set bit of (hi - lo), over the keys left in [lo, hi].
+// The search stops as soon as the chosen bin is taken whole, with the
+// threshold at the bin's lower edge and every key equal to it kept. One wave finds
+// the bin holding the krem-th largest key and clears the histogram.
+__device__ __forceinline__ void topk_pick_bin(uint32_t krem, TopkLds& sh) {
+  const int lane = threadIdx.x & 63;
+  // lane l holds bins 255-4l .. 252-4l, so a prefix scan over lanes counts
+  // the keys in the bins above
+  const int b0 = 252 - 4 * lane;
+  const u32x4 hb = *reinterpret_cast<const u32x4*>(&sh.hist[b0]);
+  *reinterpret_cast<u32x4*>(&sh.hist[b0]) = u32x4{0u, 0u, 0u, 0u};  // ready for the next pass
+  const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
+  uint32_t above = wave_incl_scan(mine) - mine;
+#pragma unroll
+  for (int i = 3; i >= 0; --i) {
+    if (above < krem && krem <= above + hb[i]) {
+      sh.sel[0] = b0 + i;
+      sh.sel[1] = above;
+      sh.sel[2] = hb[i];
+    }
+    above += hb[i];
+  }
+}
+
 template <int PER>
 __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER], uint32_t K, int32_t* out,
                            int out_len, TopkLds& sh) {
@@ -200,7 +224,64 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
   uint32_t thr = 0u, krem = 0u;  // kk == total: keep every valid element
   if (kk < total) {
     krem = kk;
-    while (hi > lo) {
+    bool done = false;
+    const float vlo = key_float(lo), vhi = key_float(hi);
+    const float sc = 256.0f / (vhi - vlo);
+    if (hi > lo && sc > 0.0f && sc < INFINITY) {
+      uint32_t bin[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float x = key[e] != 0u ? (key_float(key[e]) - vlo) * sc : 0.0f;  // in [0, 256]
+        bin[e] = min((uint32_t)x, 255u);
+        if (key[e] != 0u) atomicAdd(&sh.hist[bin[e]], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) topk_pick_bin(krem, sh);
+      __syncthreads();
+      const uint32_t d = sh.sel[0];
+      krem -= sh.sel[1];
+      if (krem == sh.sel[2]) {
+        // the whole bin is taken: the threshold is its smallest key
+        kmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if (key[e] != 0u && bin[e] == d) kmin = min(kmin, key[e]);
+        kmin = wave_umin(kmin);
+        if (lane == 0) sh.red[0][wave] = kmin;
+        __syncthreads();
+        lo = 0xFFFFFFFFu;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) lo = min(lo, sh.red[0][w]);
+        thr = lo;
+        krem = 0xFFFFFFFFu;
+        done = true;
+      } else {
+        // keys of bin d: one interval [lo, hi]
+        kmin = 0xFFFFFFFFu;
+        kmax = 0u;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if (key[e] != 0u && bin[e] == d) {
+            kmin = min(kmin, key[e]);
+            kmax = max(kmax, key[e]);
+          }
+        kmin = wave_umin(kmin);
+        kmax = wave_umax(kmax);
+        if (lane == 0) {
+          sh.red[0][wave] = kmin;
+          sh.red[1][wave] = kmax;
+        }
+        __syncthreads();
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) {
+          lo = min(lo, sh.red[0][w]);
+          hi = max(hi, sh.red[1][w]);
+        }
+      }
+    }
+    while (!done && hi > lo) {
       const uint32_t diff = hi - lo;
       const int nbits = 32 - __clz(diff);
       const int shift = nbits > 8 ? nbits - 8 : 0;
@@ -208,34 +289,26 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
       for (int e = 0; e < PER; ++e)
         if (key[e] >= lo && key[e] <= hi) atomicAdd(&sh.hist[(key[e] - lo) >> shift], 1u);
       __syncthreads();
-      if (wave == 0) {
-        // lane l holds bins 255-4l .. 252-4l, so a prefix scan over lanes
-        // counts the keys in the bins above
-        const int b0 = 252 - 4 * lane;
-        const u32x4 hb = *reinterpret_cast<const u32x4*>(&sh.hist[b0]);
-        *reinterpret_cast<u32x4*>(&sh.hist[b0]) = u32x4{0u, 0u, 0u, 0u};  // ready for the next pass
-        const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
-        uint32_t above = wave_incl_scan(mine) - mine;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          if (above < krem && krem <= above + hb[i]) {
-            sh.sel[0] = b0 + i;
-            sh.sel[1] = above;
-          }
-          above += hb[i];
-        }
-      }
+      if (wave == 0) topk_pick_bin(krem, sh);
       __syncthreads();
       const uint32_t d = sh.sel[0];
       krem -= sh.sel[1];
       const uint32_t nlo = lo + (d << shift);
+      if (krem == sh.sel[2]) {
+        // the whole bin is taken: every key in it is >= nlo and every key
+        // of a lower bin is < nlo
+        thr = nlo;
+        krem = 0xFFFFFFFFu;
+        done = true;
+        break;
+      }
       const uint32_t span = shift == 0 ? 0u : ((1u << shift) - 1u);
       hi = (hi - nlo) > span ? nlo + span : hi;
       lo = nlo;
     }
-    thr = lo;
+    if (!done) thr = lo;
   }
-  // Elements above the threshold, plus the first krem equal to it (index order).
+// Elements above the threshold, plus the first krem equal to it (index order).
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -293,7 +366,8 @@ __device__ __forceinline__ int64_t cand_token(const int32_t* bidx, int c, int bs
 // B = the candidates' INT4 codes widened to bf16 (exact). The epilogue takes
 // the max over the heads and multiplies by the token's scale (non-negative,
 // so the order of max and scale is immaterial). All loads of a wave are
-// issued before its MFMAs. Scores go to A[pair, candidate].
+// issued in two dependent batches (block numbers, then codes and scales)
+// before its MFMAs. Scores go to A[pair, candidate].
 template <int MT, int RB>
 __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
                                                       const int32_t* __restrict__ label_ch,
@@ -303,6 +377,7 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
                                                       int Hq, int Hkv, int G, int D, int64_t N, int bs, int bsh,
                                                       int r, int kb) {
   constexpr int TPW = 16;  // tiles per wave
+  constexpr int NG = TPW / 4;  // groups of four tiles, one output store each
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,21 +389,37 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
   const float* sbase = scale + (int64_t)p * N;
   const int32_t* lab = label_ch + (int64_t)h * r;
   // Two independent load chains, both issued before any wait: label channel
-  // -> query elements, and block number -> codes and scale.
+  // -> query elements, and block number -> codes and scales.
   int ch[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
 
   const int c0 = blockIdx.x * (4 * TPW * 16) + wave * (TPW * 16);
+  // Candidates read by lane (n, kq): c0 + 16u + n for the MFMA operand of
+  // tile u; c0 + 64j + lane for the score it stores in group j.
+  int cq[TPW], sq[NG], cid[TPW], sid[NG];
+  if (bsh >= 0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) >> bsh;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) >> bsh;
+  } else {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) / bs;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) / bs;
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) cid[u] = bidx[cq[u]];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) sid[j] = bidx[sq[j]];
+
   uint32_t cw[TPW];
-  float tsc[TPW];
-  bool ok[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int c = c0 + u * 16 + n;
-    const int64_t t = c < ncand ? cand_token(bidx, c, bs, bsh, N) : -1;
-    ok[u] = t >= 0;
-    const int64_t ts = ok[u] ? t : 0;  // masked candidates read token 0 of the pair
+    const int64_t t = (int64_t)cid[u] * bs + (c - cq[u] * bs);
+    const int64_t ts = (c < ncand && t >= 0 && t < N) ? t : 0;  // masked candidates read token 0
     const uint8_t* cp = cbase + ts * rb;
     if constexpr (RB > 0) {
       cw[u] = *reinterpret_cast<const uint32_t*>(cp + (4 * kq < RB ? 4 * kq : 0));
@@ -338,7 +429,15 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
       for (int e = 0; e < 4; ++e) w |= (uint32_t)cp[min(4 * kq + e, rb - 1)] << (8 * e);
       cw[u] = w;
     }
-    tsc[u] = sbase[ts];
+  }
+  float tsc[NG];
+  bool ok[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int c = c0 + 64 * j + lane;
+    const int64_t t = (int64_t)sid[j] * bs + (c - sq[j] * bs);
+    ok[j] = c < ncand && t >= 0 && t < N;
+    tsc[j] = sbase[ok[j] ? t : 0];
   }
   // A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7 (clamped loads,
   // out-of-range entries zeroed after).
@@ -359,35 +458,53 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
       for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
     }
   }
+  const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    uint32_t w = cw[u];
-    if constexpr (RB > 0) {
-      if (4 * kq >= RB) w = 0u;
-    } else {
+  for (int j = 0; j < NG; ++j) {
+    // x[jj]: max over the heads this lane holds (rows 4kq .. 4kq+3 of every
+    // head tile) for candidate n of tile 4j + jj.
+    float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * kq + e >= rb) w &= ~(0xFFu << (8 * e));
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t w = cw[4 * j + jj];
+      if constexpr (RB > 0) {
+        if (4 * kq >= RB) w = 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * kq + e >= rb) w &= ~(0xFFu << (8 * e));
+      }
+      u32x4 bop;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // code of channel 8kq + 2e
+        const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // code of channel 8kq + 2e + 1
+        bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
+      }
+      float best = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const f32x4 a = mfma16x16x32(qa[m], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (m * 16 + 4 * kq + i < G) best = fmaxf(best, a[i]);
+      }
+      x[jj] = best;
     }
-    u32x4 bop;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // code of channel 8kq + 2e
-      const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // code of channel 8kq + 2e + 1
-      bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
-    }
-    float best = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const f32x4 a = mfma16x16x32(qa[m], bop, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (m * 16 + 4 * kq + i < G) best = fmaxf(best, a[i]);
-    }
-    best = fmaxf(best, __shfl_xor(best, 16, 64));
-    best = fmaxf(best, __shfl_xor(best, 32, 64));
-    const int c = c0 + u * 16 + n;
-    if (kq == 0 && c < ncand) A[(int64_t)p * ncand + c] = ok[u] ? tsc[u] * best : 0.0f;
+    // Max across the four 16-lane rows, scattered so that row kq ends with
+    // tile 4j + kq: the 32-lane swap pairs rows (0,2) and (1,3) and leaves
+    // tiles {0,1} in the low half, {2,3} in the high half; the 16-lane swap
+    // then pairs rows (0,1) and (2,3).
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]), false, false);
+    const float y0 = fmaxf(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
+    const float y1 = fmaxf(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y0), __float_as_uint(y1), false, false);
+    const float best = fmaxf(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+    // Bounded buffer store: the hardware drops candidates >= ncand, so the
+    // scale load above stays unconditional (no branch to sink it into).
+    const float val = ok[j] ? tsc[j] * best : 0.0f;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), arow, (c0 + 64 * j + lane) * 4, 0, 0);
   }
 }
 

@@ -37,6 +37,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key for keys of finite floats.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // ---- cross-lane helpers on DPP (data-parallel primitives: register moves
 // between lanes of a 16-lane row, no LDS round trip) and readlane.
 enum : int {
@@ -116,6 +121,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   const int row = (threadIdx.x & 63) >> 4;
   const uint32_t add = row == 0 ? 0u : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
   return v + add;
+}
+
+// Raw buffer resource over `bytes` bytes at `base`: loads beyond the range
+// return 0 and stores beyond it are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
 // Orders LDS traffic between lanes of one wavefront.
