@@ -339,14 +339,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_blocks(const float* __res
                                                                int32_t* __restrict__ out) {
   __shared__ TopkLds sh;
   const int row = blockIdx.x;
-  const float* sc = S + (int64_t)row * n;
+  float v[PER];
+  load_row_f32<PER>(S + (int64_t)row * n, n, threadIdx.x * PER, v);
   uint32_t key[PER];
   int32_t id[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int c = threadIdx.x * PER + e;
     id[e] = c;
-    key[e] = c < n ? order_key(sc[c]) : 0u;
+    key[e] = c < n ? order_key(v[e]) : 0u;
   }
   block_topk<PER>(key, id, (uint32_t)K, out + (int64_t)row * K, K, sh);
 }
@@ -354,11 +355,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_blocks(const float* __res
 // ----------------------------------------------------------- token stage --
 // Candidate c of a pair is token block_idx[c / bs] * bs + c % bs (ascending
 // with c); it exists only when that token is < N.
-__device__ __forceinline__ int64_t cand_token(const int32_t* bidx, int c, int bs, int bsh, int64_t N) {
-  const int q = bsh >= 0 ? (c >> bsh) : c / bs;
-  const int64_t t = (int64_t)bidx[q] * bs + (c - q * bs);
-  return (t >= 0 && t < N) ? t : -1;
-}
 
 // Label-channel scores of 1024 candidates per workgroup (4 waves x 16 tiles of
 // 16). Sixteen candidates times sixteen heads is one MFMA (16x16x32 bf16):
@@ -515,26 +511,29 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_tokens(const float* __res
                                                                int32_t* __restrict__ token_idx, int64_t N, int bs,
                                                                int bsh, int kb, int kt) {
   __shared__ TopkLds sh;
-  __shared__ int32_t bidx_lds[kTopkThreads * PER];  // kb <= ncand
   const int p = blockIdx.x, tid = threadIdx.x;
   const int ncand = kb * bs;
-  for (int i = tid; i < kb; i += kTopkThreads) bidx_lds[i] = block_idx[(int64_t)p * kb + i];
-  const float* sc = A + (int64_t)p * ncand;
+  const int32_t* bidx = block_idx + (int64_t)p * kb;
+  // scores and block numbers of this thread's candidates, all loads in flight together
   float v[PER];
+  load_row_f32<PER>(A + (int64_t)p * ncand, ncand, tid * PER, v);
+  int bq[PER], bid[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int c = tid * PER + e;
-    v[e] = sc[c < ncand ? c : 0];
+    const int c = min(tid * PER + e, ncand - 1);
+    bq[e] = bsh >= 0 ? (c >> bsh) : c / bs;
   }
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < PER; ++e) bid[e] = bidx[bq[e]];
   uint32_t key[PER];
   int32_t id[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int c = tid * PER + e;
-    const int64_t t = c < ncand ? cand_token(bidx_lds, c, bs, bsh, N) : -1;
-    key[e] = t >= 0 ? order_key(v[e]) : 0u;
-    id[e] = (int32_t)t;
+    const int64_t t = (int64_t)bid[e] * bs + (c - bq[e] * bs);
+    const bool ok = c < ncand && t >= 0 && t < N;
+    key[e] = ok ? order_key(v[e]) : 0u;
+    id[e] = ok ? (int32_t)t : -1;
   }
   block_topk<PER>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh);
 }

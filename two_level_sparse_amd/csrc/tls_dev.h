@@ -129,6 +129,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
+// v[e] = row[first + e] for first + e < n, else 0, via bounded buffer loads
+// (no branches, so all PER loads are in flight together). When n is a
+// multiple of 4 and PER of 4, 16-byte loads (a group is wholly in or out).
+template <int PER>
+__device__ __forceinline__ void load_row_f32(const float* row, int n, int first, float (&v)[PER]) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, n * 4);
+  if (PER % 4 == 0 && (n & 3) == 0) {
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) {
+      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (first + e) * 4, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[e + i] = __uint_as_float(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (first + e) * 4, 0, 0));
+  }
+}
+
 // Orders LDS traffic between lanes of one wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
