@@ -23,18 +23,43 @@
 // scan. The token stage scores its candidates on MFMA in a kernel spread over
 // the whole chip (the G heads times r label channels product is a dense
 // contraction; INT4 codes are exact in bf16), then selects per pair.
+#include <algorithm>
+
 #include "tls_dev.h"
 #include "tls_launch.h"
 
 namespace tls {
 
 // ----------------------------------------------------------- block scores --
+// Max over the four 16-lane rows of the wave; every lane receives the result
+// for its column (lane % 16). The swaps pair rows (l, l^32), then (l, l^16).
+__device__ __forceinline__ float max_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// q+ and q- of one A fragment: per 16-bit half, sign set -> negative part.
+__device__ __forceinline__ void split_sign(u32x4 raw, u32x4& pos, u32x4& neg) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t mask = ((raw[e] >> 15) & 0x00010001u) * 0xFFFFu;
+    neg[e] = raw[e] & mask;
+    pos[e] = raw[e] & ~mask;
+  }
+}
+
+// Streaming scorer for small head groups (G <= 48): every summary byte is used
+// by at most three 16-row MFMA tiles, so the kernel is a plain HBM stream.
+// Each wave scores 16*NSUB consecutive blocks; the channel loop runs in groups
+// of UNR chunks of 32 channels whose loads (summaries and q fragments) are all
+// issued before the group's MFMAs. KC = D/32 when known at compile time (0:
+// from D at run time, with UNR = 1).
 template <int MT, int NSUB, int KC, int UNR>
 __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ summ, float* __restrict__ S,
                                                       int Hq, int Hkv, int G, int D, int64_t NB) {
-  // KC = D/32 channel chunks when known at compile time (0: from D at run
-  // time); UNR chunks are unrolled so their summary loads are all in flight.
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -47,9 +72,12 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
   const uint16_t* brow[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    int64_t j = jbase + s * 16 + n;
+    const int64_t j = jbase + s * 16 + n;
     brow[s] = sp + (j < NB ? j : NB - 1) * 2 * D;
   }
+  const uint16_t* qrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) qrow[m] = qp + (int64_t)min(m * 16 + n, G - 1) * D;  // rows past G repeat G-1, unused
   f32x4 acc[MT][NSUB];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -57,32 +85,31 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
     for (int s = 0; s < NSUB; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nchunk = KC > 0 ? KC : D / 32;
-#pragma unroll UNR
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int off = ci * 32 + 8 * kq;
-    u32x4 kmx[NSUB], kmn[NSUB];
+  for (int cb = 0; cb < nchunk; cb += UNR) {
+    u32x4 kmx[UNR][NSUB], kmn[UNR][NSUB], qr[UNR][MT];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      kmx[s] = ld16(brow[s] + off);
-      kmn[s] = ld16(brow[s] + D + off);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int g = m * 16 + n;
-      u32x4 raw = g < G ? ld16(qp + (int64_t)g * D + off) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 pos, neg;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // per 16-bit half: sign set -> negative part, else positive part
-        uint32_t sgn = (raw[e] >> 15) & 0x00010001u;
-        uint32_t mask = sgn * 0xFFFFu;
-        neg[e] = raw[e] & mask;
-        pos[e] = raw[e] & ~mask;
-      }
+    for (int u = 0; u < UNR; ++u) {
+      const int off = (cb + u) * 32 + 8 * kq;
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        acc[m][s] = mfma16x16x32(pos, kmx[s], acc[m][s]);
-        acc[m][s] = mfma16x16x32(neg, kmn[s], acc[m][s]);
+        kmx[u][s] = ld16(brow[s] + off);
+        kmn[u][s] = ld16(brow[s] + D + off);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) qr[u][m] = ld16(qrow[m] + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the group's loads ahead of its MFMAs
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        u32x4 pos, neg;
+        split_sign(qr[u][m], pos, neg);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          acc[m][s] = mfma16x16x32(pos, kmx[u][s], acc[m][s]);
+          acc[m][s] = mfma16x16x32(neg, kmn[u][s], acc[m][s]);
+        }
       }
     }
   }
@@ -94,29 +121,158 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (m * 16 + 4 * kq + i < G) best = fmaxf(best, acc[m][s][i]);
-    best = fmaxf(best, __shfl_xor(best, 16, 64));
-    best = fmaxf(best, __shfl_xor(best, 32, 64));
+    best = max_rows(best);
     const int64_t j = jbase + s * 16 + n;
     if (kq == 0 && j < NB) S[(int64_t)p * NB + j] = best;
   }
 }
 
-template <int MT, int NSUB, int KC, int UNR>
+// LDS-staged scorer for large head groups (G > 48, e.g. MLA's 128 heads on
+// one latent kv head): a GEMM with M = G heads, N = blocks, K = 2*D. A
+// workgroup scores kLdsTiles tiles of 16 consecutive blocks of one pair. Each
+// of the 4 waves keeps the q fragments of its MW = ceil(MT/4) head tiles for
+// every channel chunk in registers. All summary loads of the workgroup's
+// tiles are issued at once into registers; tile t is then written to LDS as
+// B fragments (piece (chunk, max|min) = 64 lanes x 16 bytes, read back
+// conflict-free by all 4 waves) and multiplied while the later tiles are
+// still in flight. Per-wave head maxima are combined through LDS at the end.
+constexpr int kLdsTiles = 4;
+
+template <int MT, int KC>
+__global__ __launch_bounds__(256) void k_score_blocks_lds(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ summ,
+                                                          float* __restrict__ S, int Hq, int Hkv, int G,
+                                                          int64_t NB) {
+  constexpr int D = KC * 32;
+  constexpr int MW = (MT + 3) / 4;
+  constexpr int PIECES = 2 * KC;  // per tile; KC is even, so 4 waves share them evenly
+  constexpr int PPW = PIECES / 4;
+  constexpr int CG = KC % 6 == 0 ? 6 : KC % 4 == 0 ? 4 : 2;  // chunks per group of LDS reads
+  static_assert(PIECES % 4 == 0, "KC must be even");
+  __shared__ u32x4 bt[kLdsTiles][PIECES][64];
+  __shared__ float part[kLdsTiles][4][16];
+  const int p = blockIdx.y;
+  const int b = p / Hkv, h = p % Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, kq = lane >> 4;
+  // A workgroup always loads kLdsTiles tiles; rows past NB repeat row NB-1
+  // and are not stored.
+  const int64_t t0 = (int64_t)blockIdx.x * kLdsTiles;
+  const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
+  const uint16_t* sp = summ + (int64_t)p * NB * 2 * D;
+
+  // Rows past G repeat row G-1; their products are left out of the maxima.
+  u32x4 qf[MW][KC];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const uint16_t* qr = qp + (int64_t)min((wave * MW + i) * 16 + n, G - 1) * D + 8 * kq;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[i][c] = ld16(qr + c * 32);
+  }
+  u32x4 stg[kLdsTiles][PPW];
+#pragma unroll
+  for (int t = 0; t < kLdsTiles; ++t) {
+    const int64_t j = min((t0 + t) * 16 + n, NB - 1);
+    const uint16_t* src = sp + j * 2 * D + 8 * kq;
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+      const int pc = wave + 4 * k;
+      stg[t][k] = ld16(src + (pc & 1) * D + (pc >> 1) * 32);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is in flight before the first wait
+
+#pragma unroll
+  for (int t = 0; t < kLdsTiles; ++t) {
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) bt[t][wave + 4 * k][lane] = stg[t][k];
+    // LDS writes done, then a barrier without a memory fence (a fence would
+    // wait for the later tiles' loads too).
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f32x4 acc[MW];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cg = 0; cg < KC; cg += CG) {
+      u32x4 bmx[CG], bmn[CG];
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        bmx[u] = bt[t][2 * (cg + u)][lane];
+        bmn[u] = bt[t][2 * (cg + u) + 1][lane];
+      }
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+#pragma unroll
+        for (int i = 0; i < MW; ++i) {
+          if (MT % 4 == 0 || wave * MW + i < MT) {
+            u32x4 pos, neg;
+            split_sign(qf[i][cg + u], pos, neg);
+            acc[i] = mfma16x16x32(pos, bmx[u], acc[i]);
+            acc[i] = mfma16x16x32(neg, bmn[u], acc[i]);
+          }
+        }
+      }
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((wave * MW + i) * 16 + 4 * kq + r < G) best = fmaxf(best, acc[i][r]);
+    best = max_rows(best);
+    if (kq == 0) part[t][wave][n] = best;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int t = lane >> 4, jj = lane & 15;
+    const int64_t j = (t0 + t) * 16 + jj;
+    if (j < NB)
+      S[(int64_t)p * NB + j] = fmaxf(fmaxf(part[t][0][jj], part[t][1][jj]), fmaxf(part[t][2][jj], part[t][3][jj]));
+  }
+}
+
+// Largest divisor of kc whose chunk group keeps at most 24 16-byte loads in
+// flight per lane.
+constexpr int unroll_for(int kc, int loads_per_chunk) {
+  int u = 1;
+  for (int d = 1; d <= kc; ++d)
+    if (kc % d == 0 && d * loads_per_chunk <= 24) u = d;
+  return u;
+}
+
+template <int MT, int NSUB, int KC>
 static void go_blocks_k(const BlockScoreArgs& a, hipStream_t st) {
+  constexpr int UNR = KC > 0 ? unroll_for(KC, 2 * NSUB + MT) : 1;
   const int64_t per_wg = 4 * 16 * NSUB;
   dim3 grid((unsigned)((a.NB + per_wg - 1) / per_wg), (unsigned)a.pairs);
   hipLaunchKernelGGL((k_score_blocks<MT, NSUB, KC, UNR>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G,
                      a.D, a.NB);
 }
 
+template <int MT, int KC>
+static void go_blocks_lds(const BlockScoreArgs& a, hipStream_t st) {
+  const int64_t ntiles = (a.NB + 15) / 16;
+  dim3 grid((unsigned)((ntiles + kLdsTiles - 1) / kLdsTiles), (unsigned)a.pairs);
+  hipLaunchKernelGGL((k_score_blocks_lds<MT, KC>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G, a.NB);
+}
+
 template <int MT, int NSUB>
 static void go_blocks(const BlockScoreArgs& a, hipStream_t st) {
+  if constexpr (MT >= 4) {
+    switch (a.D) {
+      case 64: go_blocks_lds<MT, 2>(a, st); return;
+      case 128: go_blocks_lds<MT, 4>(a, st); return;
+      case 256: go_blocks_lds<MT, 8>(a, st); return;
+      case 576: go_blocks_lds<MT, 18>(a, st); return;
+      default: break;
+    }
+  }
   switch (a.D) {
-    case 64: go_blocks_k<MT, NSUB, 2, 2>(a, st); break;
-    case 128: go_blocks_k<MT, NSUB, 4, 4>(a, st); break;
-    case 256: go_blocks_k<MT, NSUB, 8, 4>(a, st); break;
-    case 576: go_blocks_k<MT, NSUB, 18, 2>(a, st); break;
-    default: go_blocks_k<MT, NSUB, 0, 1>(a, st); break;
+    case 64: go_blocks_k<MT, NSUB, 2>(a, st); break;
+    case 128: go_blocks_k<MT, NSUB, 4>(a, st); break;
+    case 256: go_blocks_k<MT, NSUB, 8>(a, st); break;
+    case 576: go_blocks_k<MT, NSUB, 18>(a, st); break;
+    default: go_blocks_k<MT, NSUB, 0>(a, st); break;
   }
 }
 

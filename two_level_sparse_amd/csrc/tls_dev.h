@@ -148,6 +148,13 @@ __device__ __forceinline__ void load_row_f32(const float* row, int n, int first,
   }
 }
 
+// s_waitcnt vmcnt(N): at most N vector memory loads of this wave in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Orders LDS traffic between lanes of one wavefront.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
