@@ -65,6 +65,12 @@ SMALL = {
     "g64_lds": W.small_shape(B=1, Hq=128, Hkv=2, N=3000, bs=32, Kb=12, Kt=200),
     "g80_d256": W.small_shape(B=1, Hq=80, Hkv=1, D=256, DV=256, N=1500, bs=16, Kb=20, Kt=150),
     "g100_d64": W.small_shape(B=2, Hq=100, Hkv=1, D=64, DV=64, N=5000, bs=64, r=8, Kb=9, Kt=300),
+    # latent attention on MFMA: a half-empty second head group, 16 splits of one tile
+    "mla_g48": W.small_shape(B=1, Hq=48, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=3000, bs=32, r=32,
+                             Kb=20, Kt=500, n_outlier=0),
+    # few heads on the 576-wide rows: the vector attention kernel
+    "mla_g8": W.small_shape(B=2, Hq=8, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=1500, bs=64, r=32,
+                            Kb=6, Kt=200, n_outlier=0),
 }
 
 

@@ -26,6 +26,10 @@
 
 namespace tls {
 
+// A split's partial per head: m, l, two unused floats, then o[DV] (16-byte
+// aligned for the merge's vector loads).
+constexpr int kPartHdr = 4;
+
 template <int D, int DV, int HT, bool PRE, bool SMAP>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map,
@@ -238,10 +242,10 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
     }
     __syncthreads();
   }
-  // ---- the workgroup partial: per head (m, l, o[DV]) ----
-  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + 2);
-  for (int e = threadIdx.x; e < HT * (DV + 2); e += 256) {
-    const int hh = e / (DV + 2), c = e % (DV + 2);
+  // ---- the workgroup partial: per head (m, l, -, -, o[DV]) ----
+  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + kPartHdr);
+  for (int e = threadIdx.x; e < HT * (DV + kPartHdr); e += 256) {
+    const int hh = e / (DV + kPartHdr), c = e % (DV + kPartHdr);
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
@@ -256,58 +260,266 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
         l += mw == -INFINITY ? 0.0f : ml_lds[w][hh][1] * exp2f(mw - ms);
       }
       val = l;
+    } else if (c < kPartHdr) {
+      val = 0.0f;
     } else {
-      val = o_lds[hh * DV + c - 2];
+      val = o_lds[hh * DV + c - kPartHdr];
     }
     dst[e] = val;
   }
 }
 
-// One workgroup per (pair, head tile): the split weights 2^(m_s - M) / L of
-// every head are formed once in LDS, then each output channel is one pass of
-// independent loads over the splits.
+// k_attend_mla: the latent-attention shape (K rows of 576, V = their first
+// 512 channels, many query heads on one kv row), with both products on MFMA.
+// Workgroup = 4 wavefronts = one (pair, group of 32 heads, token split).
+//   - The split's token rows are resolved once into LDS; 32-token tiles of
+//     whole rows are staged into LDS, double-buffered: the loads of tile j+1
+//     are in flight while tile j is used, and a masked token's row is zeros.
+//   - Wave w owns head tile w&1 (16 heads) and value channels 256*(w>>1) ..
+//     +255. S^T = K q^T on MFMA (A = 16 staged key rows, B = the wave's query
+//     fragments, kept in registers), for both 16-token halves of the tile; the
+//     lane holding head n then has tokens 4kq+i of each half, which is exactly
+//     an A-operand row of P for the next product when the k-slots of P.V are
+//     ordered (half, i) -- so P never leaves the registers.
+//   - Online softmax per head in the exp2 domain; the running max is made
+//     common across the lanes of a head with cross-row swaps.
+//   - O += P V on MFMA. P is carried as two bf16 terms (hi + lo, each exact
+//     in the product, together within about 2^-17 of the fp32 value), so the
+//     product keeps fp32-level accuracy. V fragments (8 tokens of one channel
+//     per lane) come from the row-major tile with the LDS transpose read
+//     (ds_read_b64_tr_b16): within a 16-lane group, lane j receives element
+//     j%4 of the 4-element pieces addressed by lanes 4e + j/4, e = 0..3.
+// The partial (m, l, o) of the 32 heads goes to the workspace for k_merge.
+constexpr int kMlaHeads = 32;
+constexpr int kMlaTile = 32;
+constexpr int kMlaMaxTps = 1024;
+constexpr int kMlaPad = 8;  // bf16 of padding per staged row
+
+template <bool SMAP>
+__global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ kv,
+                                                       const int32_t* __restrict__ slot_map,
+                                                       const int32_t* __restrict__ token_idx,
+                                                       float* __restrict__ part, int Hq, int Hkv, int G, int64_t N,
+                                                       int bs, int64_t NB, int slots, int kt, int tps, int nsplit,
+                                                       int nhg, float qk_scale) {
+  constexpr int D = 576, DV = 512, KS = D / 32;
+  constexpr int RS = D + kMlaPad;             // staged row stride (elements)
+  constexpr int CPR = D / 8;                  // 16-byte pieces per row
+  constexpr int PPT = kMlaTile * CPR / 256;   // pieces per thread per tile
+  static_assert(kMlaTile * CPR % 256 == 0, "tile pieces must divide over the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kMlaTile * RS];
+  __shared__ int32_t rows[kMlaMaxTps];
+  __shared__ float c_lds[4][16];
+
+  const int split = blockIdx.x, hg = blockIdx.y, p = blockIdx.z;
+  const int b = p / Hkv, h = p % Hkv;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int n = lane & 15, kq = lane >> 4;
+  const int mt = wave & 1, chh = wave >> 1;
+  const int t_begin = split * tps;
+  const int t_end = min(t_begin + tps, kt);
+  const int ntok = max(t_end - t_begin, 0);
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * D;
+
+  // rows of the split's tokens (-1: masked)
+  {
+    const int32_t* tix = token_idx + (int64_t)p * kt + t_begin;
+    const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
+    for (int k = tid; k < tps; k += 256) {
+      const int tok = k < ntok ? tix[k] : -1;
+      int r = -1;
+      if (tok >= 0 && tok < N) {
+        if constexpr (SMAP) {
+          const int slot = smap[tok / bs];
+          if (slot >= 0 && slot < slots) r = slot * bs + tok % bs;
+        } else {
+          r = tok;
+        }
+      }
+      rows[k] = r;
+    }
+  }
+  // query fragments of the wave's 16 heads (rows past G repeat row G-1)
+  u32x4 qf[KS];
+  {
+    const int g = min(hg * kMlaHeads + mt * 16 + n, G - 1);
+    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qf[k] = ld16(qr + 32 * k);
+  }
+  __syncthreads();
+
+  const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
+  u32x4 stg[PPT];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = i * 256 + tid, r = pc / CPR, c = pc % CPR;
+      const int row = rows[j * kMlaTile + r];
+      stg[i] = ld16(kvp + (int64_t)(row < 0 ? 0 : row) * D + c * 8);
+      if (row < 0) stg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = i * 256 + tid, r = pc / CPR, c = pc % CPR;
+      *reinterpret_cast<u32x4*>(&tile[buf][r * RS + c * 8]) = stg[i];
+    }
+  };
+
+  float m_run = -INFINITY, l_part = 0.0f;  // head n of the wave's tile (common over kq after the swaps)
+  f32x4 o[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const uint16_t* tb = tile[buf];
+    // ---- S^T for the two 16-token halves ----
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(tb + n * RS + 32 * k + 8 * kq);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(tb + (16 + n) * RS + 32 * k + 8 * kq);
+      s0 = mfma16x16x32(k0, qf[k], s0);
+      s1 = mfma16x16x32(k1, qf[k], s1);
+    }
+    // ---- online softmax: this lane has tokens 4kq+i and 16+4kq+i of head n ----
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok0 = rows[j * kMlaTile + 4 * kq + i] >= 0;
+      const bool ok1 = rows[j * kMlaTile + 16 + 4 * kq + i] >= 0;
+      z[i] = ok0 ? s0[i] * qk_scale : -INFINITY;
+      z[4 + i] = ok1 ? s1[i] * qk_scale : -INFINITY;
+    }
+    float tmax = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+    tmax = max_rows(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float ref = m_new == -INFINITY ? 0.0f : m_new;
+    const float corr = exp2f(m_run - ref);
+    float pr[8], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = exp2f(z[i] - ref);
+      psum += pr[i];
+    }
+    l_part = l_part * corr + psum;
+    m_run = m_new;
+    // P as hi + lo bf16, k-slot order (half, i)
+    u32x4 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t h0 = f32_to_bf16_rn(pr[2 * e]), h1 = f32_to_bf16_rn(pr[2 * e + 1]);
+      const uint32_t l0 = f32_to_bf16_rn(pr[2 * e] - bf2f(h0)), l1 = f32_to_bf16_rn(pr[2 * e + 1] - bf2f(h1));
+      phi[e] = h0 | (h1 << 16);
+      plo[e] = l0 | (l1 << 16);
+    }
+    // rescale o (rows = heads 4kq+i) when a running max moved
+    if (__ballot(corr != 1.0f)) {
+      if (kq == 0) c_lds[wave][n] = corr;
+      wave_lds_sync();
+      const f32x4 cr = *reinterpret_cast<const f32x4*>(&c_lds[wave][4 * kq]);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[t] *= cr;
+    }
+    // ---- O += P V over the wave's 16 channel tiles ----
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int c0 = chh * 256 + t * 16 + 4 * (n & 3);
+      const uint16_t* a0 = tb + (4 * kq + (n >> 2)) * RS + c0;
+      const uint16_t* a1 = tb + (16 + 4 * kq + (n >> 2)) * RS + c0;
+      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a1);
+      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+      const u32x4 vf = {w0[0], w0[1], w1[0], w1[1]};
+      o[t] = mfma16x16x32(phi, vf, o[t]);
+      o[t] = mfma16x16x32(plo, vf, o[t]);
+    }
+    if (j + 1 < ntiles) {
+      store_tile(buf ^ 1);  // tile j-1's buffer: every wave finished it before the last barrier
+    }
+    __syncthreads();
+  }
+
+  // ---- the partial of the 32 heads: (m, l, -, -, o[DV]) ----
+  const float l_tot = sum_rows(l_part);
+  float* dst = part + (((int64_t)p * nhg + hg) * nsplit + split) * kMlaHeads * (DV + kPartHdr);
+  if (chh == 0 && kq == 0) {
+    float* hd = dst + (mt * 16 + n) * (DV + kPartHdr);
+    hd[0] = m_run;
+    hd[1] = l_tot;
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dst[(mt * 16 + 4 * kq + i) * (DV + kPartHdr) + kPartHdr + chh * 256 + t * 16 + n] = o[t][i];
+}
+
+// Split merge. Workgroup = (256 float4 outputs, head tile, pair): the split
+// weights 2^(m_s - M) / L of the tile's heads are formed in LDS, then every
+// thread reads its float4 of o from all splits with independent loads.
 constexpr int kMaxSplits = 64;
 template <int DV, int HT>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
                                                float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
-  __shared__ float m_lds[kMaxSplits][HT];
+  __shared__ float ml_lds[kMaxSplits][HT][2];
   __shared__ float w_lds[kMaxSplits][HT];
-  const int ht = blockIdx.x, p = blockIdx.y;
+  const int ht = blockIdx.y, p = blockIdx.z, tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
-  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * (DV + 2);
-  const int64_t sstride = (int64_t)HT * (DV + 2);
-  for (int e = threadIdx.x; e < nsplit * HT; e += 256) {
+  constexpr int PS = DV + kPartHdr;  // floats per head in a partial
+  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * PS;
+  for (int e = tid; e < nsplit * HT; e += 256) {
     const int s = e / HT, hh = e % HT;
-    m_lds[s][hh] = base[s * sstride + hh * (DV + 2)];
+    const float* src = base + ((int64_t)s * HT + hh) * PS;
+    ml_lds[s][hh][0] = src[0];
+    ml_lds[s][hh][1] = src[1];
   }
   __syncthreads();
-  if (threadIdx.x < HT) {
-    const int hh = threadIdx.x;
+  if (tid < HT) {
+    const int hh = tid;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, m_lds[s][hh]);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_lds[s][hh][0]);
     float L = 0.0f;
     for (int s = 0; s < nsplit; ++s) {
-      const float ms = m_lds[s][hh];
+      const float ms = ml_lds[s][hh][0];
       const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-      L += base[s * sstride + hh * (DV + 2) + 1] * w;
+      L += ml_lds[s][hh][1] * w;
       w_lds[s][hh] = w;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int s = 0; s < nsplit; ++s) w_lds[s][hh] *= inv;
     const int g = ht * HT + hh;
-    if (lse && g < G) lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    if (lse && blockIdx.x == 0 && g < G)
+      lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < HT * DV; e += 256) {
-    const int hh = e / DV, c = e % DV;
-    const int g = ht * HT + hh;
-    if (g >= G) continue;
-    const float* src = base + hh * (DV + 2) + 2 + c;
-    float O = 0.0f;
+  const int e = blockIdx.x * 256 + tid;  // float4 index in [HT, DV/4]
+  if (e >= HT * (DV / 4)) return;
+  const int hh = e / (DV / 4), c = (e % (DV / 4)) * 4;
+  const int g = ht * HT + hh;
+  if (g >= G) return;
+  const float* src = base + (int64_t)hh * PS + kPartHdr + c;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) O = fmaf(src[s * sstride], w_lds[s][hh], O);
-    out[((int64_t)b * Hq + (int64_t)h * G + g) * DV + c] = O;
+  for (int s = 0; s < nsplit; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)s * HT * PS);
+    const float w = w_lds[s][hh];
+    o += v * w;
   }
+  *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + (int64_t)h * G + g) * DV + c) = o;
 }
 
 // Launch shape: head tiles of HT <= 16 heads; a workgroup takes 256-token
@@ -316,7 +528,27 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, f
 static constexpr int head_tile(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 static constexpr bool prefetch_rows(int D) { return D <= 256; }
 
-bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
+void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, DecodePlan* plan) {
+  if (D == 576 && DV == 512 && v_is_k_prefix && G > 16 && kt <= kMaxSplits * kMlaMaxTps) {
+    // latent attention: 32-head groups, 32-token tiles; about 256 workgroups
+    // (one per CU), which keeps the partials (2 KB per head and split) small
+    const int nht = (G + kMlaHeads - 1) / kMlaHeads;
+    const int units = pairs * nht;
+    const int want = (256 + units - 1) / units;
+    int tps = (kt + want - 1) / want;
+    tps = ((tps + kMlaTile - 1) / kMlaTile) * kMlaTile;
+    const int min_tps = ((kt + kMaxSplits - 1) / kMaxSplits + kMlaTile - 1) / kMlaTile * kMlaTile;
+    if (tps < min_tps) tps = min_tps;
+    if (tps < kMlaTile) tps = kMlaTile;
+    if (tps > kMlaMaxTps) tps = kMlaMaxTps;  // kt <= kMaxSplits * kMlaMaxTps keeps nsplit in range
+    plan->mla = 1;
+    plan->HT = kMlaHeads;
+    plan->nht = nht;
+    plan->tps = tps;
+    plan->nsplit = (kt + tps - 1) / tps;
+    plan->part_bytes = (size_t)pairs * nht * plan->nsplit * kMlaHeads * (DV + kPartHdr) * sizeof(float);
+    return;
+  }
   const int HT = head_tile(G);
   const int nht = (G + HT - 1) / HT;
   const int units = pairs * nht;
@@ -327,13 +559,21 @@ bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan) {
   if (tps < min_tps) tps = min_tps;
   if (tps < 256) tps = 256;
   const int nsplit = (kt + tps - 1) / tps;
+  plan->mla = 0;
   plan->HT = HT;
   plan->nht = nht;
   plan->tps = tps;
   plan->nsplit = nsplit;
-  plan->part_bytes = (size_t)pairs * nht * nsplit * HT * (DV + 2) * sizeof(float);
+  plan->part_bytes = (size_t)pairs * nht * nsplit * HT * (DV + kPartHdr) * sizeof(float);
   (void)D;
-  return true;
+}
+
+template <int DV, int HT>
+static hipError_t launch_merge(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
+  dim3 mgrid((unsigned)((HT * DV / 4 + 255) / 256), (unsigned)pl.nht, (unsigned)a.pairs);
+  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv, a.G,
+                     pl.nht, pl.nsplit);
+  return hipGetLastError();
 }
 
 template <int D, int DV, int HT>
@@ -350,10 +590,7 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid((unsigned)pl.nht, (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv, a.G,
-                     pl.nht, pl.nsplit);
-  return hipGetLastError();
+  return launch_merge<DV, HT>(a, pl, st);
 }
 
 template <int D, int DV>
@@ -368,7 +605,23 @@ static hipError_t go_decode_ht(const DecodeArgs& a, const DecodePlan& pl, hipStr
   }
 }
 
+static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
+  dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
+  if (a.slot_map)
+    hipLaunchKernelGGL(k_attend_mla<true>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
+                       a.Hq, a.Hkv, a.G, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
+                       a.sm_scale * kLog2e);
+  else
+    hipLaunchKernelGGL(k_attend_mla<false>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
+                       a.Hq, a.Hkv, a.G, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
+                       a.sm_scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge<512, kMlaHeads>(a, pl, st);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
+  if (pl.mla) return go_decode_mla(a, pl, st);
   if (a.D == 64 && a.DV == 64) return go_decode_ht<64, 64>(a, pl, st);
   if (a.D == 128 && a.DV == 128) return go_decode_ht<128, 128>(a, pl, st);
   if (a.D == 256 && a.DV == 256) return go_decode_ht<256, 256>(a, pl, st);

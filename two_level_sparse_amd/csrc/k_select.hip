@@ -31,15 +31,6 @@
 namespace tls {
 
 // ----------------------------------------------------------- block scores --
-// Max over the four 16-lane rows of the wave; every lane receives the result
-// for its column (lane % 16). The swaps pair rows (l, l^32), then (l, l^16).
-__device__ __forceinline__ float max_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // q+ and q- of one A fragment: per 16-bit half, sign set -> negative part.
 __device__ __forceinline__ void split_sign(u32x4 raw, u32x4& pos, u32x4& neg) {
 #pragma unroll

@@ -88,7 +88,7 @@ size_t ws_bytes(const Derived& d, int which) {
     case TLS_WS_TOKENS: return round_up((size_t)d.pairs * d.kb * d.bs * sizeof(float));
     case TLS_WS_DECODE: {
       DecodePlan pl;
-      plan_decode(d.pairs, d.G, d.D, d.DV, d.kt, &pl);
+      plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
       return round_up(pl.part_bytes);
     }
     default: return 0;
@@ -182,7 +182,7 @@ int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_ca
   if (!dims_ok)
     return set_error(TLS_ERR_UNSUPPORTED, "attention is compiled for (D,DV) in {(64,64),(128,128),(256,256),(576,512)}");
   DecodePlan pl;
-  plan_decode(d.pairs, d.G, d.D, d.DV, d.kt, &pl);
+  plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
   if (!ws || ws_len < ws_bytes(d, TLS_WS_DECODE))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
   DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, ws, out, lse_opt,

@@ -56,9 +56,11 @@ struct DecodeArgs {
 };
 struct DecodePlan {
   int HT, nht, tps, nsplit;
+  int mla;            // 1: the MFMA latent-attention kernel (D 576, DV 512, HT 32)
   size_t part_bytes;  // partial results (m, l, o) per split
 };
-bool plan_decode(int pairs, int G, int D, int DV, int kt, DecodePlan* plan);
+// Always succeeds for the shapes the API accepts.
+void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, DecodePlan* plan);
 
 // One transferred block (element offsets into the host cache and the resident
 // cache) and one slot-map change.
