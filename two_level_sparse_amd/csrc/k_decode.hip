@@ -272,9 +272,14 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
 // k_attend_mla: the latent-attention shape (K rows of 576, V = their first
 // 512 channels, many query heads on one kv row), with both products on MFMA.
 // Workgroup = 4 wavefronts = one (pair, group of 32 heads, token split).
-//   - The split's token rows are resolved once into LDS; 32-token tiles of
-//     whole rows are staged into LDS, double-buffered: the loads of tile j+1
-//     are in flight while tile j is used, and a masked token's row is zeros.
+//   - The split's token rows are resolved once into LDS. 32-token tiles of
+//     whole rows go to LDS with direct global->LDS 16-byte loads, double-
+//     buffered in two LDS objects (so the compiler sees that reading tile j
+//     does not wait for the loads of tile j+1). Layout: 72 chunks of 512
+//     bytes, one per 16-byte column piece cp, holding the 32 rows; row r of
+//     chunk cp sits in slot r ^ (4 * (cp & 1)), which keeps both read
+//     patterns below free of bank conflicts. A masked token loads the row of
+//     the split's first valid token (finite data) and is masked in softmax.
 //   - Wave w owns head tile w&1 (16 heads) and value channels 256*(w>>1) ..
 //     +255. S^T = K q^T on MFMA (A = 16 staged key rows, B = the wave's query
 //     fragments, kept in registers), for both 16-token halves of the tile; the
@@ -286,14 +291,13 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
 //   - O += P V on MFMA. P is carried as two bf16 terms (hi + lo, each exact
 //     in the product, together within about 2^-17 of the fp32 value), so the
 //     product keeps fp32-level accuracy. V fragments (8 tokens of one channel
-//     per lane) come from the row-major tile with the LDS transpose read
+//     per lane) come from the staged rows with the LDS transpose read
 //     (ds_read_b64_tr_b16): within a 16-lane group, lane j receives element
 //     j%4 of the 4-element pieces addressed by lanes 4e + j/4, e = 0..3.
 // The partial (m, l, o) of the 32 heads goes to the workspace for k_merge.
 constexpr int kMlaHeads = 32;
 constexpr int kMlaTile = 32;
 constexpr int kMlaMaxTps = 1024;
-constexpr int kMlaPad = 8;  // bf16 of padding per staged row
 
 template <bool SMAP>
 __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restrict__ q,
@@ -304,13 +308,15 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
                                                        int bs, int64_t NB, int slots, int kt, int tps, int nsplit,
                                                        int nhg, float qk_scale) {
   constexpr int D = 576, DV = 512, KS = D / 32;
-  constexpr int RS = D + kMlaPad;             // staged row stride (elements)
-  constexpr int CPR = D / 8;                  // 16-byte pieces per row
-  constexpr int PPT = kMlaTile * CPR / 256;   // pieces per thread per tile
-  static_assert(kMlaTile * CPR % 256 == 0, "tile pieces must divide over the workgroup");
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kMlaTile * RS];
+  constexpr int CP = D / 8;           // 16-byte column pieces per row = LDS chunks per tile
+  constexpr int CHUNK = kMlaTile * 16;  // bytes per chunk
+  constexpr int NLOAD = CP / 2;       // 1 KB direct loads per tile (two chunks each)
+  static_assert(NLOAD % 4 == 0 && kMlaTile == 32, "tile layout");
+  __shared__ __attribute__((aligned(1024))) uint8_t tA[CP * CHUNK];
+  __shared__ __attribute__((aligned(1024))) uint8_t tB[CP * CHUNK];
   __shared__ int32_t rows[kMlaMaxTps];
   __shared__ float c_lds[4][16];
+  __shared__ int first_ok;
 
   const int split = blockIdx.x, hg = blockIdx.y, p = blockIdx.z;
   const int b = p / Hkv, h = p % Hkv;
@@ -322,7 +328,9 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   const int ntok = max(t_end - t_begin, 0);
   const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * D;
 
-  // rows of the split's tokens (-1: masked)
+  // rows of the split's tokens (-1: masked), and the first valid one
+  if (tid == 0) first_ok = 0x7FFFFFFF;
+  __syncthreads();
   {
     const int32_t* tix = token_idx + (int64_t)p * kt + t_begin;
     const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
@@ -338,6 +346,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
         }
       }
       rows[k] = r;
+      if (r >= 0) atomicMin(&first_ok, k);
     }
   }
   // query fragments of the wave's 16 heads (rows past G repeat row G-1)
@@ -349,23 +358,21 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
     for (int k = 0; k < KS; ++k) qf[k] = ld16(qr + 32 * k);
   }
   __syncthreads();
+  const int fb = first_ok < tps ? rows[first_ok] : -1;
+  const int ntiles = fb < 0 ? 0 : (ntok + kMlaTile - 1) / kMlaTile;  // nothing valid: empty partial
 
-  const int ntiles = (ntok + kMlaTile - 1) / kMlaTile;
-  u32x4 stg[PPT];
-  auto load_tile = [&](int j) {
+  // direct loads of tile j into `dst`: wave w issues loads w, w+4, ..; lane L
+  // of load i fills slot L&31 of chunk 2i + (L>>5)
+  auto issue = [&](uint8_t* dst, int j) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = i * 256 + tid, r = pc / CPR, c = pc % CPR;
+    for (int k = 0; k < NLOAD / 4; ++k) {
+      const int i = wave + 4 * k;
+      const int cp = 2 * i + (lane >> 5);
+      const int r = (lane & 31) ^ (4 * (cp & 1));
       const int row = rows[j * kMlaTile + r];
-      stg[i] = ld16(kvp + (int64_t)(row < 0 ? 0 : row) * D + c * 8);
-      if (row < 0) stg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = i * 256 + tid, r = pc / CPR, c = pc % CPR;
-      *reinterpret_cast<u32x4*>(&tile[buf][r * RS + c * 8]) = stg[i];
+      const uint16_t* src = kvp + (int64_t)(row >= 0 ? row : fb) * D + cp * 8;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(dst + i * 2 * CHUNK), 16, 0, 0);
     }
   };
 
@@ -374,23 +381,30 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
 #pragma unroll
   for (int t = 0; t < 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const uint16_t* tb = tile[buf];
+  auto compute = [&](const uint8_t* tb, int j) {
     // ---- S^T for the two 16-token halves ----
+    // key fragments in groups of KG steps: all reads of a group are issued
+    // before its MFMAs
+    constexpr int KG = 6;
+    static_assert(KS % KG == 0, "key step groups");
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(tb + n * RS + 32 * k + 8 * kq);
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(tb + (16 + n) * RS + 32 * k + 8 * kq);
-      s0 = mfma16x16x32(k0, qf[k], s0);
-      s1 = mfma16x16x32(k1, qf[k], s1);
+    for (int kg = 0; kg < KS; kg += KG) {
+      u32x4 k0[KG], k1[KG];
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        const int cp = 4 * (kg + u) + kq;
+        const uint8_t* cb = tb + cp * CHUNK;
+        const int sw = 4 * (cp & 1);
+        k0[u] = *reinterpret_cast<const u32x4*>(cb + (n ^ sw) * 16);
+        k1[u] = *reinterpret_cast<const u32x4*>(cb + ((16 + n) ^ sw) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        s0 = mfma16x16x32(k0[u], qf[kg + u], s0);
+        s1 = mfma16x16x32(k1[u], qf[kg + u], s1);
+      }
     }
     // ---- online softmax: this lane has tokens 4kq+i and 16+4kq+i of head n ----
     float z[8];
@@ -434,23 +448,39 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
       for (int t = 0; t < 16; ++t) o[t] *= cr;
     }
     // ---- O += P V over the wave's 16 channel tiles ----
+    // lane n of a group addresses row 4kq + n/4 (+16), channels c0 + 4(n%4) ..
+    // +3: chunk c0/8 + (n%4)/2, byte 8*(n&1) of the row's slot
     typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const int cpo = (n >> 1) & 1;
+    const int r0 = (4 * kq + (n >> 2)) ^ (4 * cpo), r1 = (16 + 4 * kq + (n >> 2)) ^ (4 * cpo);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int c0 = chh * 256 + t * 16 + 4 * (n & 3);
-      const uint16_t* a0 = tb + (4 * kq + (n >> 2)) * RS + c0;
-      const uint16_t* a1 = tb + (16 + 4 * kq + (n >> 2)) * RS + c0;
-      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
-      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a1);
+      const uint8_t* cb = tb + (chh * 32 + 2 * t + cpo) * CHUNK + 8 * (n & 1);
+      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(cb + r0 * 16));
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(cb + r1 * 16));
       const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
       const u32x4 vf = {w0[0], w0[1], w1[0], w1[1]};
       o[t] = mfma16x16x32(phi, vf, o[t]);
       o[t] = mfma16x16x32(plo, vf, o[t]);
     }
-    if (j + 1 < ntiles) {
-      store_tile(buf ^ 1);  // tile j-1's buffer: every wave finished it before the last barrier
-    }
-    __syncthreads();
+  };
+
+  // Barrier without a memory fence (a fence would also wait for the loads of
+  // the next tile); this wave's direct loads are complete before it.
+  auto tile_barrier = [&]() {
+    wait_vmcnt<0>();
+    __asm__ volatile("s_barrier" ::: "memory");
+  };
+  if (ntiles > 0) issue(tA, 0);
+  tile_barrier();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue(tB, j + 1);
+    compute(tA, j);
+    tile_barrier();  // tile j+1 landed; every wave is done with tA
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue(tA, j + 2);
+    compute(tB, j + 1);
+    tile_barrier();
   }
 
   // ---- the partial of the 32 heads: (m, l, -, -, o[DV]) ----
@@ -530,11 +560,12 @@ static constexpr bool prefetch_rows(int D) { return D <= 256; }
 
 void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, DecodePlan* plan) {
   if (D == 576 && DV == 512 && v_is_k_prefix && G > 16 && kt <= kMaxSplits * kMlaMaxTps) {
-    // latent attention: 32-head groups, 32-token tiles; about 256 workgroups
-    // (one per CU), which keeps the partials (2 KB per head and split) small
+    // latent attention: 32-head groups, 32-token tiles; about 512 workgroups
+    // (two per CU, so that one's loads and barriers overlap the other's
+    // MFMAs); the partials cost 2 KB per head and split
     const int nht = (G + kMlaHeads - 1) / kMlaHeads;
     const int units = pairs * nht;
-    const int want = (256 + units - 1) / units;
+    const int want = (512 + units - 1) / units;
     int tps = (kt + want - 1) / want;
     tps = ((tps + kMlaTile - 1) / kMlaTile) * kMlaTile;
     const int min_tps = ((kt + kMaxSplits - 1) / kMaxSplits + kMlaTile - 1) / kMlaTile * kMlaTile;
