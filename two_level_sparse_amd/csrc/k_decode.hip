@@ -21,6 +21,8 @@
 // partial. k_merge then combines the splits of every head. (A fused
 // last-workgroup merge would need an agent-scope release per workgroup, which
 // on this part writes back the XCD's whole L2; a second launch is cheaper.)
+#include <type_traits>
+
 #include "tls_dev.h"
 #include "tls_launch.h"
 
@@ -236,6 +238,237 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float* dst = &o_lds[hh * DV + chunk * 8 + e];
+          const float val = f[hh] * acc[hh][e];
+          *dst = w == 0 ? val : *dst + val;
+        }
+    }
+    __syncthreads();
+  }
+  // ---- the workgroup partial: per head (m, l, -, -, o[DV]) ----
+  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + kPartHdr);
+  for (int e = threadIdx.x; e < HT * (DV + kPartHdr); e += 256) {
+    const int hh = e / (DV + kPartHdr), c = e % (DV + kPartHdr);
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
+    float val;
+    if (c == 0) {
+      val = ms;
+    } else if (c == 1) {
+      float l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = ml_lds[w][hh][0];
+        l += mw == -INFINITY ? 0.0f : ml_lds[w][hh][1] * exp2f(mw - ms);
+      }
+      val = l;
+    } else if (c < kPartHdr) {
+      val = 0.0f;
+    } else {
+      val = o_lds[hh * DV + c - kPartHdr];
+    }
+    dst[e] = val;
+  }
+}
+
+// k_attend_gqa: k_attend for rows of up to 128 channels, with the value
+// product laid out so that every lane owns distinct outputs: lane l keeps
+// channels CPL*l .. CPL*l+CPL-1 (CPL = DV/64) of every head of the tile, and
+// reads, for each token, just those channels (one small load per token per
+// lane, 256 bytes per wave for DV = 128). The accumulator is HT*CPL floats
+// per lane instead of HT*8, which leaves room for two waves per SIMD with the
+// 16-token tiles double-buffered; the probabilities are broadcast from LDS.
+// Token validity and rows for the value loads are wave-uniform (readlane).
+template <int D, int DV, int HT, bool SMAP>
+__global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                                       const int32_t* __restrict__ slot_map,
+                                                       const int32_t* __restrict__ token_idx,
+                                                       float* __restrict__ part, int Hq, int Hkv, int G, int row,
+                                                       int v_off, int64_t N, int bs, int64_t NB, int slots, int kt,
+                                                       int tps, int nsplit, int nht, float qk_scale) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int CPL = DV / 64;  // value channels per lane
+  static_assert(D % 32 == 0 && DV % 64 == 0 && (CPL == 1 || CPL == 2 || CPL == 4), "unsupported shape");
+  using VT = typename std::conditional<CPL == 1, uint16_t, typename std::conditional<CPL == 2, uint32_t, u32x2>::type>::type;
+
+  __shared__ __attribute__((aligned(16))) float p_lds[4][16][16];  // [wave][token][head]
+  __shared__ __attribute__((aligned(16))) float c_lds[4][16];      // [wave][head] rescale factors
+  __shared__ float ml_lds[4][16][2];                               // [wave][head] (m, l)
+  __shared__ float o_lds[HT * DV];
+
+  const int split = blockIdx.x, ht = blockIdx.y, p = blockIdx.z;
+  const int b = p / Hkv, h = p % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, kq = lane >> 4;
+
+  // query fragments of this lane's MFMA row (head ht*HT + n)
+  const int g_row = ht * HT + n;
+  const bool row_ok = n < HT && g_row < G;
+  u32x4 qf[KSTEPS];
+  {
+    const uint16_t* qrow = q + ((int64_t)b * Hq + (int64_t)h * G + (row_ok ? g_row : 0)) * D;
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) qf[k] = ld16(qrow + k * 32 + 8 * kq);
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k)
+      if (!row_ok) qf[k] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int t_begin = split * tps;
+  const int t_end = min(t_begin + tps, kt);
+  const int32_t* tix = token_idx + (int64_t)p * kt;
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
+  const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.0f;
+  }
+  float acc[HT][CPL];
+#pragma unroll
+  for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[hh][c] = 0.0f;
+
+  for (int c0 = t_begin + 64 * wave; c0 < t_end; c0 += 256) {
+    int my_tok = -1, my_row = 0;
+    {
+      const int pos = c0 + lane;
+      const int tok = pos < t_end ? tix[pos] : -1;
+      if (tok >= 0 && tok < N) {
+        if constexpr (SMAP) {
+          const int slot = smap[tok / bs];
+          if (slot >= 0 && slot < slots) {  // a block that is not resident is never read
+            my_tok = tok;
+            my_row = slot * bs + tok % bs;
+          }
+        } else {
+          my_tok = tok;
+          my_row = tok;
+        }
+      }
+    }
+    const int ntile = min(4, (t_end - c0 + 15) / 16);
+
+    u32x4 kbuf[2][KSTEPS];
+    VT vbuf[2][16];
+    int ktk[2] = {-1, -1};
+    auto issue = [&](int j, int slot) {
+      ktk[slot] = __shfl(my_tok, 16 * j + n, 64);
+      const uint16_t* kr = kvp + (int64_t)__shfl(my_row, 16 * j + n, 64) * row + 8 * kq;
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) kbuf[slot][k] = ld16(kr + k * 32);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = __builtin_amdgcn_readlane(my_row, 16 * j + t);
+        vbuf[slot][t] = *reinterpret_cast<const VT*>(kvp + (int64_t)r * row + v_off + CPL * lane);
+      }
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= ntile) break;
+      const int cur = j & 1;
+      if (j + 1 < ntile) issue(j + 1, cur ^ 1);
+      const bool tok_ok = ktk[cur] >= 0;
+      // ---- scores of the 16 tokens (MFMA) ----
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) z = mfma16x16x32(qf[k], kbuf[cur][k], z);
+      // ---- online softmax (lane holds heads 4*kq+i of token n) ----
+      float pr[4], corr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zi = tok_ok ? z[i] * qk_scale : -INFINITY;
+        const float tmax = max16(zi);
+        const float m_new = fmaxf(m_run[i], tmax);
+        const float ref = m_new == -INFINITY ? 0.0f : m_new;
+        corr[i] = exp2f(m_run[i] - ref);
+        pr[i] = exp2f(zi - ref);
+        l_run[i] = l_run[i] * corr[i] + pr[i];
+        m_run[i] = m_new;
+      }
+      *reinterpret_cast<f32x4*>(&p_lds[wave][n][4 * kq]) = f32x4{pr[0], pr[1], pr[2], pr[3]};
+      if (n == 0) *reinterpret_cast<f32x4*>(&c_lds[wave][4 * kq]) = f32x4{corr[0], corr[1], corr[2], corr[3]};
+      wave_lds_sync();
+      // ---- P.V: this lane's channels of every head ----
+      if (__ballot(corr[0] != 1.0f || corr[1] != 1.0f || corr[2] != 1.0f || corr[3] != 1.0f)) {
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh) {
+          const float c = c_lds[wave][hh];
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[hh][e] *= c;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const bool vok = __builtin_amdgcn_readlane(my_tok, 16 * j + t) >= 0;
+        float vv[CPL];
+        if constexpr (CPL == 1) {
+          vv[0] = bf2f(vbuf[cur][t]);
+        } else if constexpr (CPL == 2) {
+          vv[0] = bf_lo(vbuf[cur][t]);
+          vv[1] = bf_hi(vbuf[cur][t]);
+        } else {
+          vv[0] = bf_lo(vbuf[cur][t][0]);
+          vv[1] = bf_hi(vbuf[cur][t][0]);
+          vv[2] = bf_lo(vbuf[cur][t][1]);
+          vv[3] = bf_hi(vbuf[cur][t][1]);
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          if (!vok) vv[e] = 0.0f;  // masked token: its row may hold anything
+        float ph[HT];
+        if constexpr (HT % 4 == 0) {
+#pragma unroll
+          for (int g4 = 0; g4 < HT / 4; ++g4) {
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(&p_lds[wave][t][4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ph[4 * g4 + i] = pv[i];
+          }
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < HT; ++hh) ph[hh] = p_lds[wave][t][hh];
+        }
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[hh][e] = fmaf(ph[hh], vv[e], acc[hh][e]);
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // ---- per-wave totals: l over the 16 token columns ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l_run[i] = sum16(l_run[i]);
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ml_lds[wave][4 * kq + i][0] = m_run[i];
+      ml_lds[wave][4 * kq + i][1] = l_run[i];
+    }
+  }
+  __syncthreads();
+  // ---- merge the 4 waves ----
+  float f[HT];
+#pragma unroll
+  for (int hh = 0; hh < HT; ++hh) {
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
+    const float mw = ml_lds[wave][hh][0];
+    f[hh] = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          float* dst = &o_lds[hh * DV + CPL * lane + e];
           const float val = f[hh] * acc[hh][e];
           *dst = w == 0 ? val : *dst + val;
         }
@@ -611,6 +844,19 @@ template <int D, int DV, int HT>
 static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
   constexpr bool PRE = prefetch_rows(D);
+  if constexpr (D <= 128) {  // wider rows: the per-lane buffers of k_attend_gqa would spill
+    if (a.slot_map)
+      hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
+                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+    else
+      hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
+                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge<DV, HT>(a, pl, st);
+  }
   if (a.slot_map)
     hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
                        (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
