@@ -10,11 +10,13 @@ The default workload is the 128k-context GQA decode (batch 8, 64 query heads on
 
 Cold measurement: R copies of the cache live at distinct device addresses and
 the steps rotate over them, so no step finds its bytes in the 256 MB Infinity
-Cache left there by the previous step (R * touched bytes >= 1 GiB).
+Cache left there by the previous step (R * touched bytes >= 1 GiB). Each timed
+step replays a HIP graph captured from the step's library calls (no host
+launch cost in the timed region; --no-graph launches them one by one).
 
 Prints one JSON line: queries/sec (= batch / step time), the HBM roofline of
-the dominant kernel (attention; its launches timed with HIP events on the
-stream they run on) and the fp64 oracle timed on host cores over a bounded
+the dominant kernel (attention; the library records HIP events around each
+of its launches on the stream it runs on) and the fp64 oracle timed on host cores over a bounded
 sample of pairs as the CPU baseline.
 """
 from __future__ import annotations
@@ -36,6 +38,7 @@ import workload as W  # noqa: E402
 
 METRIC = "sparse-attn decode queries/sec at 32k/128k ctx; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def algorithmic_bytes(s):
@@ -52,6 +55,13 @@ def algorithmic_bytes(s):
                 attention=rows + q + out + s.B * s.Hq * 4)
 
 
+def attention_kernel(s):
+    """Name of the attention kernel tls_sparse_decode launches for this shape."""
+    if s.D == 576 and s.DV == 512 and s.v_is_k_prefix and s.G > 16:
+        return "k_attend_mla"
+    return "k_attend_gqa" if s.D <= 128 else "k_attend"
+
+
 def measured_traffic(config):
     """HBM bytes per attention launch from the committed counter summary, or
     None when the attention kernel source changed since the counters were taken."""
@@ -62,11 +72,37 @@ def measured_traffic(config):
         return None
     sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
     for line in prof.read_text().splitlines():
-        if line.startswith("k_attend_traffic_bytes="):
+        if line.startswith("attention_traffic_bytes="):
             kv = dict(tok.split("=") for tok in line.split())
             if kv.get("source_sha256_prefix") == sha:
-                return int(kv["k_attend_traffic_bytes"])
+                return int(kv["attention_traffic_bytes"])
     return None
+
+
+def block_scorer_mfma(s, dec, qs, caches, stream, reps=20):
+    """The block-score GEMM [G x 2D] . [2D x NB] per pair, timed alone with the
+    library's events: cold (rotating over the cache copies) and warm (one
+    copy, its summaries left in the Infinity Cache by the previous call)."""
+    import torch
+    import two_level_sparse_amd as T
+    flops = 2.0 * s.G * s.NB * 2 * s.D * s.pairs
+    summ_bytes = s.pairs * s.NB * 2 * s.D * 2
+    out = {"kernel": "k_score_blocks_lds" if s.G > 48 else "k_score_blocks", "flops": flops,
+           "bytes": summ_bytes, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+    for mode in ("cold", "warm"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps + 2):
+            r = i % len(caches) if mode == "cold" else 0
+            if i >= 2:
+                T.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES, *evs[i - 2])
+            dec.select_blocks(qs[r], caches[r])
+            T.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        out[mode] = {"us": round(us, 2), "tflops": round(flops / us / 1e6, 1),
+                     "mfma_util": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "GBps": round(summ_bytes / us / 1e3, 1)}
+    return out
 
 
 def log(msg):
@@ -104,7 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3_128k_gqa", choices=list(W.CONFIGS))
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for 1 GiB)")
-    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch the timed steps one call at a time instead of replaying a captured HIP graph per step")
     ap.add_argument("--chunks", type=int, default=1, help="batch chunks pipelined on separate streams")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -148,7 +185,7 @@ def main():
     torch.cuda.synchronize()
 
     graphs = None
-    if args.graph:
+    if args.graph and args.chunks == 1:
         graphs = []
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -164,9 +201,9 @@ def main():
 
     pipelined = args.chunks > 1
 
-    def one_step(i, ev=None):
+    def one_step(i, ev=None, eager=False):
         r = i % R
-        if graphs is not None:
+        if graphs is not None and not eager:
             graphs[r].replay()
             return
         if pipelined:
@@ -174,11 +211,11 @@ def main():
             return
         dec.select_blocks(qs[r], caches[r])
         dec.select_tokens(qs[r], caches[r])
-        if ev is not None:
-            ev[0].record(stream)
+        if ev is not None:  # the library records these around its attention kernel
+            T.tls_profile_events(T.TLS_PROFILE_ATTENTION, ev[0], ev[1])
         dec.decode(qs[r], caches[r].kv)
         if ev is not None:
-            ev[1].record(stream)
+            T.tls_profile_events(T.TLS_PROFILE_ATTENTION)
 
     for i in range(args.warmup):
         one_step(i)
@@ -191,30 +228,48 @@ def main():
         del src, dst
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # five windows of the timed steps, for the median rate
+    bounds = sorted({K * w // 5 for w in range(1, 5)})
+    wev = {b: torch.cuda.Event(enable_timing=True) for b in bounds}
     start.record(stream)
     for i in range(K):
-        one_step(i, None if (graphs is not None or pipelined) else evs[i])
+        if i in wev:
+            wev[i].record(stream)
+        one_step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / K
     step_s = ms_step / 1e3
+    marks = [(0, start)] + [(b, wev[b]) for b in bounds] + [(K, end)]
+    win = [a[1].elapsed_time(b[1]) / (b[0] - a[0]) for a, b in zip(marks, marks[1:]) if b[0] > a[0]]
+    ms_median = float(np.median(win))
 
-    dec_ms = None
-    if graphs is None and not pipelined:
+    # The attention kernel alone, timed with the events the library records
+    # around it, over further eager steps on the same rotating caches.
+    dec_ms, scorer = None, None
+    if not pipelined:
+        P = max(20, 2 * R)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(P)]
+        for i in range(P):
+            one_step(i, evs[i], eager=True)
+        torch.cuda.synchronize()
         dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        scorer = block_scorer_mfma(s, dec, qs, caches, stream)
+
     roof = None
     if dec_ms:
         ach = ab["attention"] / (dec_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_attend (tls_sparse_decode)", "achieved": round(ach, 1),
+        roof = {"bound": "hbm", "kernel": f"{attention_kernel(s)} (attention of tls_sparse_decode)",
+                "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(s.name),
-                "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"]}
+                "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"],
+                "timing": "HIP events recorded by the library around each attention launch, eager steps"}
 
     res = {
         "metric": METRIC,
@@ -236,6 +291,8 @@ def main():
                 "achieved_GBps": round(ab["total"] / step_s / 1e9, 1),
                 "frac_of_peak": round(ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
+        "ms_per_step_median_of_5_windows": round(ms_median, 5),
+        "block_scorer": scorer,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:

@@ -191,6 +191,21 @@ int tls_offload_last_delta(const tls_offload_t *ctx, int32_t *counts, int32_t *b
 
 void tls_offload_destroy(tls_offload_t *ctx);
 
+/* Measurement hook. From now on every call that launches kernel `which`
+ * records start_event and end_event (hipEvent_t handles created and owned by
+ * the caller) on its stream immediately before and after that kernel, so its
+ * duration can be read with hipEventElapsedTime apart from the launches
+ * around it:
+ *   TLS_PROFILE_BLOCK_SCORES: the block-score GEMM of tls_select_blocks
+ *     (not its top-k);
+ *   TLS_PROFILE_ATTENTION: the attention kernel of tls_sparse_decode (not
+ *     its split merge).
+ * NULL, NULL turns it off. Process-wide; set it while no other thread is
+ * calling the library. TLS_ERR_INVALID_ARG if exactly one event is NULL or
+ * `which` is unknown. */
+enum { TLS_PROFILE_BLOCK_SCORES = 0, TLS_PROFILE_ATTENTION = 1 };
+int tls_profile_events(int which, void *start_event, void *end_event);
+
 /* Message for the last failed call on this thread ("" if none). */
 const char *tls_last_error(void);
 

@@ -80,3 +80,8 @@ def test_argument_errors_before_any_device_work(lib):
     assert rc == T.TLS_ERR_INVALID_ARG and h.value is None
     rc = lib.tls_prefetch_delta(None, 0, None, None, None, None)
     assert rc == T.TLS_ERR_INVALID_ARG
+    # the measurement hook takes both events or neither, for a known kernel
+    rc = lib.tls_profile_events(T.TLS_PROFILE_ATTENTION, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"both" in lib.tls_last_error()
+    assert lib.tls_profile_events(7, None, None) == T.TLS_ERR_INVALID_ARG
+    assert lib.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES, None, None) == T.TLS_OK

@@ -29,11 +29,12 @@ TLS_ERR_STATE = -5
 TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE = 0, 1, 2
 
 TLS_COPY_GATHER, TLS_COPY_MEMCPY = 0, 1
+TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION = 0, 1
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",
             "tls_sparse_decode", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
-            "tls_offload_set_copy_mode", "tls_offload_last_delta", "tls_offload_destroy", "tls_last_error",
-            "tls_version"]
+            "tls_offload_set_copy_mode", "tls_offload_last_delta", "tls_offload_destroy", "tls_profile_events",
+            "tls_last_error", "tls_version"]
 
 
 class tls_shape_t(C.Structure):
@@ -76,6 +77,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_offload_last_delta": (C.c_int, [vp, vp, vp]),
         "tls_offload_set_copy_mode": (C.c_int, [vp, C.c_int]),
         "tls_offload_destroy": (None, [vp]),
+        "tls_profile_events": (C.c_int, [C.c_int, vp, vp]),
         "tls_last_error": (C.c_char_p, []),
         "tls_version": (C.c_char_p, []),
     }
@@ -174,6 +176,22 @@ def tls_offload_last_delta(ctx, counts, blocks):
 
 def tls_offload_destroy(ctx):
     load_library().tls_offload_destroy(ctx)
+
+
+def tls_profile_events(which, start_event=None, end_event=None):
+    """torch.cuda.Event pair recorded around kernel `which` (TLS_PROFILE_*) of
+    every later call that launches it (None, None: off). A torch event gets its
+    HIP handle at its first record, so unrecorded events are recorded once here
+    (the library's later record replaces that timestamp)."""
+    handles = []
+    for ev in (start_event, end_event):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:
+            ev.record()
+        handles.append(ev.cuda_event)
+    _check(load_library().tls_profile_events(int(which), handles[0], handles[1]))
 
 
 def tls_version() -> str:

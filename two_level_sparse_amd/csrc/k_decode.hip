@@ -832,6 +832,10 @@ void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, De
   (void)D;
 }
 
+static void prof_mark(hipEvent_t ev, hipStream_t st) {
+  if (ev) (void)hipEventRecord(ev, st);
+}
+
 template <int DV, int HT>
 static hipError_t launch_merge(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 mgrid((unsigned)((HT * DV / 4 + 255) / 256), (unsigned)pl.nht, (unsigned)a.pairs);
@@ -844,6 +848,7 @@ template <int D, int DV, int HT>
 static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
   constexpr bool PRE = prefetch_rows(D);
+  prof_mark(a.prof_start, st);
   if constexpr (D <= 128) {  // wider rows: the per-lane buffers of k_attend_gqa would spill
     if (a.slot_map)
       hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
@@ -855,6 +860,7 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
                          pl.nsplit, pl.nht, a.sm_scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    prof_mark(a.prof_end, st);
     return launch_merge<DV, HT>(a, pl, st);
   }
   if (a.slot_map)
@@ -867,6 +873,7 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_mark(a.prof_end, st);
   return launch_merge<DV, HT>(a, pl, st);
 }
 
@@ -884,6 +891,7 @@ static hipError_t go_decode_ht(const DecodeArgs& a, const DecodePlan& pl, hipStr
 
 static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
+  prof_mark(a.prof_start, st);
   if (a.slot_map)
     hipLaunchKernelGGL(k_attend_mla<true>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
                        a.Hq, a.Hkv, a.G, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
@@ -894,6 +902,7 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
                        a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_mark(a.prof_end, st);
   return launch_merge<512, kMlaHeads>(a, pl, st);
 }
 

@@ -120,104 +120,175 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
 
 // LDS-staged scorer for large head groups (G > 48, e.g. MLA's 128 heads on
 // one latent kv head): a GEMM with M = G heads, N = blocks, K = 2*D. A
-// workgroup scores kLdsTiles tiles of 16 consecutive blocks of one pair. Each
-// of the 4 waves keeps the q fragments of its MW = ceil(MT/4) head tiles for
-// every channel chunk in registers. All summary loads of the workgroup's
-// tiles are issued at once into registers; tile t is then written to LDS as
-// B fragments (piece (chunk, max|min) = 64 lanes x 16 bytes, read back
-// conflict-free by all 4 waves) and multiplied while the later tiles are
-// still in flight. Per-wave head maxima are combined through LDS at the end.
+// workgroup of 8 waves scores kLdsTiles tiles of 16 consecutive blocks of one
+// pair. Wave w takes head tiles 2*(w&3), 2*(w&3)+1 and one half of the
+// channel chunks (w>>2), whose q fragments it keeps in registers; the two
+// halves' sums meet in LDS. The summaries of all the workgroup's tiles go to
+// LDS with direct global->LDS 16-byte loads, laid out as B fragments (piece
+// (chunk, max|min) = 64 lanes x 16 bytes, read back conflict-free), and are
+// read by the 4 waves that share a channel half. q is loaded once per
+// workgroup for kLdsTiles tiles of summaries.
 constexpr int kLdsTiles = 4;
+constexpr int kLdsWaves = 8;
 
 template <int MT, int KC>
-__global__ __launch_bounds__(256) void k_score_blocks_lds(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ summ,
-                                                          float* __restrict__ S, int Hq, int Hkv, int G,
-                                                          int64_t NB) {
+__global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint16_t* __restrict__ q,
+                                                                     const uint16_t* __restrict__ summ,
+                                                                     float* __restrict__ S, int Hq, int Hkv, int G,
+                                                                     int64_t NB) {
   constexpr int D = KC * 32;
-  constexpr int MW = (MT + 3) / 4;
-  constexpr int PIECES = 2 * KC;  // per tile; KC is even, so 4 waves share them evenly
-  constexpr int PPW = PIECES / 4;
-  constexpr int CG = KC % 6 == 0 ? 6 : KC % 4 == 0 ? 4 : 2;  // chunks per group of LDS reads
-  static_assert(PIECES % 4 == 0, "KC must be even");
-  __shared__ u32x4 bt[kLdsTiles][PIECES][64];
+  constexpr int MW = 2;                 // head tiles per wave
+  constexpr int KH = KC / 2;            // channel chunks per wave
+  constexpr int PIECES = 2 * KC;        // per tile
+  constexpr int PPW = (PIECES + kLdsWaves - 1) / kLdsWaves;
+  constexpr int CG = KH % 3 == 0 ? 3 : KH % 2 == 0 ? 2 : 1;  // chunks per group of LDS reads
+  static_assert(MT <= 8 && KC % 2 == 0 && kLdsTiles == 4, "tile layout");
+  // tiles 0-1 and 2-3 in two LDS objects, so that reading tiles 0-1 does not
+  // wait for the loads of tiles 2-3
+  __shared__ u32x4 btA[2][PIECES][64], btB[2][PIECES][64];
   __shared__ float part[kLdsTiles][4][16];
-  const int p = blockIdx.y;
+  // after the products: the second channel half's sums, [tile][head-tile pair][MW][lane],
+  // in btA when it is large enough
+  constexpr int HALF = kLdsTiles * 4 * MW * 64;
+  constexpr bool kAlias = 2 * PIECES * 64 >= HALF;
+  __shared__ f32x4 half_own[kAlias ? 1 : HALF];
+  f32x4* half1 = kAlias ? reinterpret_cast<f32x4*>(&btA[0][0][0]) : half_own;
+  auto bt = [&](int t) -> u32x4(*)[64] { return t < 2 ? btA[t] : btB[t - 2]; };
+  // Workgroup -> (pair, tile group). Workgroups are dealt to the 8 XCDs in
+  // turn (linear id mod 8); when the pair count allows, every workgroup of a
+  // pair lands on one XCD, whose L2 then serves the pair's q to all of them.
+  const int gx = (int)((NB + 16 * kLdsTiles - 1) / (16 * kLdsTiles));  // tile groups per pair
+  const int npairs = (int)gridDim.x / gx;
+  int p, tg;
+  if (npairs % 8 == 0) {
+    const int xcd = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
+    p = xcd + 8 * (slot / gx);
+    tg = slot % gx;
+  } else {
+    p = (int)blockIdx.x / gx;
+    tg = (int)blockIdx.x % gx;
+  }
   const int b = p / Hkv, h = p % Hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, kq = lane >> 4;
+  const int hp = wave & 3, kh = wave >> 2;  // head-tile pair, channel half
   // A workgroup always loads kLdsTiles tiles; rows past NB repeat row NB-1
   // and are not stored.
-  const int64_t t0 = (int64_t)blockIdx.x * kLdsTiles;
+  const int64_t t0 = (int64_t)tg * kLdsTiles;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
   const uint16_t* sp = summ + (int64_t)p * NB * 2 * D;
 
-  // Rows past G repeat row G-1; their products are left out of the maxima.
-  u32x4 qf[MW][KC];
+  // Direct loads of tiles [ta, tb): wave w issues pieces w, w+8, ...
+  auto issue = [&](int ta, int tb) {
 #pragma unroll
-  for (int i = 0; i < MW; ++i) {
-    const uint16_t* qr = qp + (int64_t)min((wave * MW + i) * 16 + n, G - 1) * D + 8 * kq;
+    for (int t = ta; t < tb; ++t) {
+      const int64_t j = min((t0 + t) * 16 + n, NB - 1);
+      const uint16_t* src = sp + j * 2 * D + 8 * kq;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) qf[i][c] = ld16(qr + c * 32);
-  }
-  u32x4 stg[kLdsTiles][PPW];
-#pragma unroll
-  for (int t = 0; t < kLdsTiles; ++t) {
-    const int64_t j = min((t0 + t) * 16 + n, NB - 1);
-    const uint16_t* src = sp + j * 2 * D + 8 * kq;
-#pragma unroll
-    for (int k = 0; k < PPW; ++k) {
-      const int pc = wave + 4 * k;
-      stg[t][k] = ld16(src + (pc & 1) * D + (pc >> 1) * 32);
+      for (int k = 0; k < PPW; ++k) {
+        const int pc = wave + kLdsWaves * k;
+        if (pc < PIECES)
+          __builtin_amdgcn_global_load_lds(
+              (__attribute__((address_space(1))) void*)(src + (pc & 1) * D + (pc >> 1) * 32),
+              (__attribute__((address_space(3))) void*)&bt(t)[pc][0], 16, 0, 0);
+      }
     }
+  };
+  // Tiles 0 and 1 first, then the q fragments (rows past G repeat row G-1;
+  // their products are left out of the maxima), split once into q+ / q-.
+  // Waiting for q also waits for those two tiles; tiles 2 and 3 are issued
+  // after it and land while tiles 0 and 1 are multiplied.
+  issue(0, 2);
+  u32x4 qpos[MW][KH], qneg[MW][KH];
+  {
+    u32x4 raw[MW][KH];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const uint16_t* qr = qp + (int64_t)min((2 * hp + i) * 16 + n, G - 1) * D + 8 * kq + kh * KH * 32;
+#pragma unroll
+      for (int c = 0; c < KH; ++c) raw[i][c] = ld16(qr + c * 32);
+    }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+      for (int c = 0; c < KH; ++c) split_sign(raw[i][c], qpos[i][c], qneg[i][c]);
   }
-  __builtin_amdgcn_sched_barrier(0);  // every load above is in flight before the first wait
+  __builtin_amdgcn_sched_barrier(0);
+  issue(2, kLdsTiles);
+  // tiles 0 and 1 are in LDS for every wave: a barrier without a memory fence
+  // (a fence would wait for tiles 2 and 3 as well)
+  __asm__ volatile("s_barrier" ::: "memory");
 
+  f32x4 tot[kLdsTiles][MW];
+  auto product = [&](int t) {
+    // four independent accumulation chains per head tile (q+ / q- terms of
+    // even / odd chunks), so that consecutive MFMAs do not wait on each other
+    f32x4 acc[MW][4];
 #pragma unroll
-  for (int t = 0; t < kLdsTiles; ++t) {
+    for (int i = 0; i < MW; ++i)
 #pragma unroll
-    for (int k = 0; k < PPW; ++k) bt[t][wave + 4 * k][lane] = stg[t][k];
-    // LDS writes done, then a barrier without a memory fence (a fence would
-    // wait for the later tiles' loads too).
-    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    f32x4 acc[MW];
+      for (int a = 0; a < 4; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < MW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cg = 0; cg < KC; cg += CG) {
+    for (int cg = 0; cg < KH; cg += CG) {
       u32x4 bmx[CG], bmn[CG];
 #pragma unroll
       for (int u = 0; u < CG; ++u) {
-        bmx[u] = bt[t][2 * (cg + u)][lane];
-        bmn[u] = bt[t][2 * (cg + u) + 1][lane];
+        const int c = kh * KH + cg + u;
+        bmx[u] = bt(t)[2 * c][lane];
+        bmn[u] = bt(t)[2 * c + 1][lane];
       }
 #pragma unroll
       for (int u = 0; u < CG; ++u) {
 #pragma unroll
         for (int i = 0; i < MW; ++i) {
-          if (MT % 4 == 0 || wave * MW + i < MT) {
-            u32x4 pos, neg;
-            split_sign(qf[i][cg + u], pos, neg);
-            acc[i] = mfma16x16x32(pos, bmx[u], acc[i]);
-            acc[i] = mfma16x16x32(neg, bmn[u], acc[i]);
+          {
+            const int a = 2 * (u & 1);
+            acc[i][a] = mfma16x16x32(qpos[i][cg + u], bmx[u], acc[i][a]);
+            acc[i][a + 1] = mfma16x16x32(qneg[i][cg + u], bmn[u], acc[i][a + 1]);
           }
         }
       }
     }
-    float best = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < MW; ++i)
+    for (int i = 0; i < MW; ++i) tot[t][i] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+  };
+  product(0);
+  product(1);
+  wait_vmcnt<0>();
+  __asm__ volatile("s_barrier" ::: "memory");
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if ((wave * MW + i) * 16 + 4 * kq + r < G) best = fmaxf(best, acc[i][r]);
-    best = max_rows(best);
-    if (kq == 0) part[t][wave][n] = best;
+  for (int t = 2; t < kLdsTiles; ++t) product(t);
+  // the second channel half hands its sums to the first (through the tile
+  // buffer, once every wave is done reading it)
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < kLdsTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < MW; ++i) half1[((t * 4 + hp) * MW + i) * 64 + lane] = tot[t][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int t = 0; t < kLdsTiles; ++t) {
+      float best = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        const f32x4 sum = tot[t][i] + half1[((t * 4 + hp) * MW + i) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((2 * hp + i) * 16 + 4 * kq + r < G) best = fmaxf(best, sum[r]);
+      }
+      best = max_rows(best);
+      if (kq == 0) part[t][hp][n] = best;
+    }
   }
   __syncthreads();
   if (wave == 0) {
     const int t = lane >> 4, jj = lane & 15;
     const int64_t j = (t0 + t) * 16 + jj;
-    if (j < NB)
+    if (t < kLdsTiles && j < NB)
       S[(int64_t)p * NB + j] = fmaxf(fmaxf(part[t][0][jj], part[t][1][jj]), fmaxf(part[t][2][jj], part[t][3][jj]));
   }
 }
@@ -240,21 +311,23 @@ static void go_blocks_k(const BlockScoreArgs& a, hipStream_t st) {
                      a.D, a.NB);
 }
 
-template <int MT, int KC>
+// Always 8 head tiles: for G < 128 the extra tiles run on clamped q rows and
+// are masked; their waves would otherwise idle beside the others.
+template <int KC>
 static void go_blocks_lds(const BlockScoreArgs& a, hipStream_t st) {
   const int64_t ntiles = (a.NB + 15) / 16;
-  dim3 grid((unsigned)((ntiles + kLdsTiles - 1) / kLdsTiles), (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_score_blocks_lds<MT, KC>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G, a.NB);
+  const int64_t gx = (ntiles + kLdsTiles - 1) / kLdsTiles;
+  hipLaunchKernelGGL((k_score_blocks_lds<8, KC>), dim3((unsigned)(gx * a.pairs)), dim3(kLdsWaves * 64), 0, st, a.q, a.summ,
+                     a.S, a.Hq, a.Hkv, a.G, a.NB);
 }
 
 template <int MT, int NSUB>
 static void go_blocks(const BlockScoreArgs& a, hipStream_t st) {
   if constexpr (MT >= 4) {
     switch (a.D) {
-      case 64: go_blocks_lds<MT, 2>(a, st); return;
-      case 128: go_blocks_lds<MT, 4>(a, st); return;
-      case 256: go_blocks_lds<MT, 8>(a, st); return;
-      case 576: go_blocks_lds<MT, 18>(a, st); return;
+      case 128: go_blocks_lds<4>(a, st); return;
+      case 256: go_blocks_lds<8>(a, st); return;
+      case 576: go_blocks_lds<18>(a, st); return;
       default: break;
     }
   }
@@ -503,113 +576,105 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_blocks(const float* __res
 // Candidate c of a pair is token block_idx[c / bs] * bs + c % bs (ascending
 // with c); it exists only when that token is < N.
 
-// Label-channel scores of 1024 candidates per workgroup (4 waves x 16 tiles of
+// Label-channel scores of candidates in units of 256 per wave (16 tiles of
 // 16). Sixteen candidates times sixteen heads is one MFMA (16x16x32 bf16):
 // A = q on the label channels (heads x channels, zero padded to 32 channels),
 // B = the candidates' INT4 codes widened to bf16 (exact). The epilogue takes
 // the max over the heads and multiplies by the token's scale (non-negative,
-// so the order of max and scale is immaterial). All loads of a wave are
-// issued in two dependent batches (block numbers, then codes and scales)
-// before its MFMAs. Scores go to A[pair, candidate].
-template <int MT, int RB>
-__global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
-                                                      const int32_t* __restrict__ label_ch,
-                                                      const uint8_t* __restrict__ codes,
-                                                      const float* __restrict__ scale,
-                                                      const int32_t* __restrict__ block_idx, float* __restrict__ A,
-                                                      int Hq, int Hkv, int G, int D, int64_t N, int bs, int bsh,
-                                                      int r, int kb) {
-  constexpr int TPW = 16;  // tiles per wave
-  constexpr int NG = TPW / 4;  // groups of four tiles, one output store each
-  const int p = blockIdx.y;
-  const int b = p / Hkv, h = p % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, kq = lane >> 4;
-  const int ncand = kb * bs;
-  const int rb = r / 2;
-  const int32_t* bidx = block_idx + (int64_t)p * kb;
-  const uint8_t* cbase = codes + (int64_t)p * N * rb;
-  const float* sbase = scale + (int64_t)p * N;
-  const int32_t* lab = label_ch + (int64_t)h * r;
-  // Two independent load chains, both issued before any wait: label channel
-  // -> query elements, and block number -> codes and scales.
-  int ch[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+// so the order of max and scale is immaterial). A unit's loads go out in two
+// dependent batches (block numbers, then codes and scales) before its MFMAs;
+// the label-channel -> query chain runs beside them.
+constexpr int kUnitTiles = 16;               // tiles of 16 candidates per unit
+constexpr int kUnitGroups = kUnitTiles / 4;  // groups of four tiles; one score per lane each
 
-  const int c0 = blockIdx.x * (4 * TPW * 16) + wave * (TPW * 16);
-  // Candidates read by lane (n, kq): c0 + 16u + n for the MFMA operand of
-  // tile u; c0 + 64j + lane for the score it stores in group j.
-  int cq[TPW], sq[NG], cid[TPW], sid[NG];
+struct UnitLoads {
+  uint32_t cw[kUnitTiles];  // lane (n, kq): code bytes 4kq..4kq+3 of candidate c0 + 16u + n
+  float tsc[kUnitGroups];   // scale of candidate c0 + 64j + lane
+  bool ok[kUnitGroups];     // that candidate exists
+};
+
+// Issues the loads of the unit starting at candidate c0. `bidx` is the pair's
+// block list (global or LDS).
+template <int RB>
+__device__ __forceinline__ void unit_loads(UnitLoads& L, const int32_t* bidx, const uint8_t* cbase,
+                                           const float* sbase, int c0, int ncand, int64_t N, int bs, int bsh,
+                                           int rb) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
+  int cq[kUnitTiles], sq[kUnitGroups], cid[kUnitTiles], sid[kUnitGroups];
   if (bsh >= 0) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) >> bsh;
+    for (int u = 0; u < kUnitTiles; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) >> bsh;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) >> bsh;
+    for (int j = 0; j < kUnitGroups; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) >> bsh;
   } else {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) / bs;
+    for (int u = 0; u < kUnitTiles; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) / bs;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) / bs;
+    for (int j = 0; j < kUnitGroups; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) / bs;
   }
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) cid[u] = bidx[cq[u]];
+  for (int u = 0; u < kUnitTiles; ++u) cid[u] = bidx[cq[u]];
 #pragma unroll
-  for (int j = 0; j < NG; ++j) sid[j] = bidx[sq[j]];
-
-  uint32_t cw[TPW];
+  for (int j = 0; j < kUnitGroups; ++j) sid[j] = bidx[sq[j]];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
+  for (int u = 0; u < kUnitTiles; ++u) {
     const int c = c0 + u * 16 + n;
     const int64_t t = (int64_t)cid[u] * bs + (c - cq[u] * bs);
     const int64_t ts = (c < ncand && t >= 0 && t < N) ? t : 0;  // masked candidates read token 0
     const uint8_t* cp = cbase + ts * rb;
     if constexpr (RB > 0) {
-      cw[u] = *reinterpret_cast<const uint32_t*>(cp + (4 * kq < RB ? 4 * kq : 0));
+      L.cw[u] = *reinterpret_cast<const uint32_t*>(cp + (4 * kq < RB ? 4 * kq : 0));
     } else {
       uint32_t w = 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w |= (uint32_t)cp[min(4 * kq + e, rb - 1)] << (8 * e);
-      cw[u] = w;
+      L.cw[u] = w;
     }
   }
-  float tsc[NG];
-  bool ok[NG];
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
+  for (int j = 0; j < kUnitGroups; ++j) {
     const int c = c0 + 64 * j + lane;
     const int64_t t = (int64_t)sid[j] * bs + (c - sq[j] * bs);
-    ok[j] = c < ncand && t >= 0 && t < N;
-    tsc[j] = sbase[ok[j] ? t : 0];
+    L.ok[j] = c < ncand && t >= 0 && t < N;
+    L.tsc[j] = sbase[L.ok[j] ? t : 0];
   }
-  // A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7 (clamped loads,
-  // out-of-range entries zeroed after).
-  u32x4 qa[MT];
-  {
-    const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
+}
+
+// A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7, from the label
+// channel numbers ch[] (clamped loads, out-of-range entries zeroed after).
+template <int MT>
+__device__ __forceinline__ void label_q(u32x4 (&qa)[MT], const int (&ch)[8], const uint16_t* qp, int G, int D,
+                                        int r) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int g = m * 16 + n;
-      const uint16_t* qr = qp + (int64_t)min(g, G - 1) * D;
-      uint32_t hv[8];
+  for (int m = 0; m < MT; ++m) {
+    const int g = m * 16 + n;
+    const uint16_t* qr = qp + (int64_t)min(g, G - 1) * D;
+    uint32_t hv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = qr[ch[e]];
+    for (int e = 0; e < 8; ++e) hv[e] = qr[ch[e]];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (g >= G || 8 * kq + e >= r) hv[e] = 0u;
+    for (int e = 0; e < 8; ++e)
+      if (g >= G || 8 * kq + e >= r) hv[e] = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
-    }
+    for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
   }
-  const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
+}
+
+// Scores of the unit: val[j] for candidate c0 + 64j + lane (0 if it does not
+// exist).
+template <int MT, int RB>
+__device__ __forceinline__ void unit_scores(float (&val)[kUnitGroups], const UnitLoads& L, const u32x4 (&qa)[MT],
+                                            int G, int rb) {
+  const int lane = threadIdx.x & 63, kq = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
+  for (int j = 0; j < kUnitGroups; ++j) {
     // x[jj]: max over the heads this lane holds (rows 4kq .. 4kq+3 of every
     // head tile) for candidate n of tile 4j + jj.
     float x[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      uint32_t w = cw[4 * j + jj];
+      uint32_t w = L.cw[4 * j + jj];
       if constexpr (RB > 0) {
         if (4 * kq >= RB) w = 0u;
       } else {
@@ -644,11 +709,41 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
     const float y1 = fmaxf(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
     const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y0), __float_as_uint(y1), false, false);
     const float best = fmaxf(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
-    // Bounded buffer store: the hardware drops candidates >= ncand, so the
-    // scale load above stays unconditional (no branch to sink it into).
-    const float val = ok[j] ? tsc[j] * best : 0.0f;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), arow, (c0 + 64 * j + lane) * 4, 0, 0);
+    val[j] = L.ok[j] ? L.tsc[j] * best : 0.0f;
   }
+}
+
+// Token scores of 1024 candidates per workgroup (one unit per wave), spread
+// over the chip; the scores go to A[pair, candidate] for k_topk_tokens.
+template <int MT, int RB>
+__global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
+                                                      const int32_t* __restrict__ label_ch,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ scale,
+                                                      const int32_t* __restrict__ block_idx, float* __restrict__ A,
+                                                      int Hq, int Hkv, int G, int D, int64_t N, int bs, int bsh,
+                                                      int r, int kb) {
+  const int p = blockIdx.y;
+  const int b = p / Hkv, h = p % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kq = lane >> 4;
+  const int ncand = kb * bs, rb = r / 2;
+  const int32_t* lab = label_ch + (int64_t)h * r;
+  int ch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+  const int c0 = blockIdx.x * (4 * kUnitTiles * 16) + wave * (kUnitTiles * 16);
+  UnitLoads L;
+  unit_loads<RB>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * N * rb, scale + (int64_t)p * N, c0, ncand, N,
+                 bs, bsh, rb);
+  u32x4 qa[MT];
+  label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
+  float val[kUnitGroups];
+  unit_scores<MT, RB>(val, L, qa, G, rb);
+  // bounded buffer stores: the hardware drops candidates >= ncand
+  const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
+#pragma unroll
+  for (int j = 0; j < kUnitGroups; ++j)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
 }
 
 // Top-Kt' of the candidate scores of one pair per workgroup; ids are tokens.
@@ -685,6 +780,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_tokens(const float* __res
   block_topk<PER>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh);
 }
 
+static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }
 #define TLS_PER_SWITCH(per, MACRO) \
   if (per <= 1) MACRO(1);          \
   else if (per <= 2) MACRO(2);     \
@@ -701,7 +797,6 @@ hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* o
   return hipGetLastError();
 }
 
-static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }
 
 template <int MT, int RB>
 static void go_score_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {

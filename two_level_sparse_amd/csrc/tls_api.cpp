@@ -3,6 +3,7 @@
 // every buffer comes from the caller.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,8 @@
 namespace tls {
 
 static thread_local char g_err[512] = "";
+// events recorded around the profiled kernels (index: TLS_PROFILE_*)
+static std::atomic<hipEvent_t> g_prof_start[2], g_prof_end[2];
 
 int set_error(int code, const char* fmt, ...) {
   va_list ap;
@@ -105,6 +108,16 @@ const char* tls_last_error(void) { return g_err; }
 
 const char* tls_version(void) { return "tls-gfx950 0.1"; }
 
+int tls_profile_events(int which, void* start_event, void* end_event) {
+  if (which != TLS_PROFILE_BLOCK_SCORES && which != TLS_PROFILE_ATTENTION)
+    return set_error(TLS_ERR_INVALID_ARG, "unknown profiled kernel %d", which);
+  if ((start_event == nullptr) != (end_event == nullptr))
+    return set_error(TLS_ERR_INVALID_ARG, "pass both events or neither");
+  g_prof_start[which].store((hipEvent_t)start_event, std::memory_order_relaxed);
+  g_prof_end[which].store((hipEvent_t)end_event, std::memory_order_relaxed);
+  return TLS_OK;
+}
+
 size_t tls_workspace_size(const tls_shape_t* shape, int which) {
   Derived d;
   if (derive(shape, &d) != TLS_OK) return 0;
@@ -143,7 +156,11 @@ int tls_select_blocks(const tls_shape_t* shape, const void* q, const void* summ,
   }
   hipStream_t st = (hipStream_t)stream;
   BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB};
+  const hipEvent_t pb = g_prof_start[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
+  const hipEvent_t pe = g_prof_end[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
+  if (pb) (void)hipEventRecord(pb, st);
   hipError_t e = launch_score_blocks(sa, st);
+  if (pe) (void)hipEventRecord(pe, st);
   if (e != hipSuccess) return hip_error(e, "score_blocks launch");
   e = launch_topk_blocks(S, d.pairs, (int)d.NB, d.kb, block_idx, st);
   return e == hipSuccess ? TLS_OK : hip_error(e, "topk(blocks) launch");
@@ -187,7 +204,9 @@ int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_ca
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
   DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, ws, out, lse_opt,
                d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
-               slot_map ? slots_per_pair : 0, d.N, d.NB, d.sm};
+               slot_map ? slots_per_pair : 0, d.N, d.NB, d.sm,
+               g_prof_start[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed),
+               g_prof_end[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed)};
   hipError_t e = launch_decode(a, pl, (hipStream_t)stream);
   return e == hipSuccess ? TLS_OK : hip_error(e, "sparse_decode launch");
 }

@@ -53,6 +53,7 @@ struct DecodeArgs {
   int pairs, B, Hq, Hkv, G, D, DV, row, v_off, bs, kt, slots;
   int64_t N, NB;
   float sm_scale;
+  hipEvent_t prof_start, prof_end;  // recorded around the attention kernel when not null
 };
 struct DecodePlan {
   int HT, nht, tps, nsplit;
