@@ -41,13 +41,14 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def algorithmic_bytes(s):
+def algorithmic_bytes(s, dense=False):
     """Bytes the selection must touch per step (summaries, label cache of the
-    candidates, gathered K/V rows, q, out) and the attention kernel's share."""
+    candidates, gathered K/V rows, q, out) and the attention kernel's share.
+    dense: attention over every token, nothing selected."""
     kb = min(s.Kb, s.NB)
     kt = min(s.Kt, kb * s.bs)
-    summ = s.pairs * s.NB * 2 * s.D * 2
-    label = s.pairs * kb * s.bs * (s.r // 2 + 4)
+    summ = 0 if dense else s.pairs * s.NB * 2 * s.D * 2
+    label = 0 if dense else s.pairs * kb * s.bs * (s.r // 2 + 4)
     rows = s.pairs * kt * s.row * 2
     q = s.B * s.Hq * s.D * 2
     out = s.B * s.Hq * s.DV * 4
@@ -106,6 +107,24 @@ def block_scorer_mfma(s, dec, qs, caches, stream, reps=20):
     return out
 
 
+class DenseDecoder:
+    """Attention over every cached token through the same library call (the
+    baseline the pages compare against: dense decode at the same shape)."""
+
+    def __init__(self, s):
+        import torch
+        from two_level_sparse_amd.runtime import Decoder
+        self.dec = Decoder(s)
+        self.idx = torch.arange(s.N, dtype=torch.int32, device="cuda").expand(s.B, s.Hkv, s.N).contiguous()
+
+    def decode(self, q, kv, **kw):
+        self.dec.decode(q, kv, token_idx=self.idx, **kw)
+
+    def step(self, q, cache, stream=None):
+        self.dec.decode(q, cache.kv, stream, token_idx=self.idx)
+        return self.dec.out
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -148,6 +167,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy before timing (counter calibration for profiles)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--mode", default="tls", choices=["tls", "quest", "dense"],
+                    help="tls: the two-level step; quest: block stage only (every token of the kept blocks); "
+                         "dense: attention over every cached token, no selection (baselines at the same shape)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this operator is built and "
@@ -163,14 +185,19 @@ def main():
     s = W.CONFIGS[args.config]
     if s.steps:
         return bench_offload(args, s)
-    ab = algorithmic_bytes(s)
+    s_data = s  # the cache and queries; s below is the shape the calls run with
+    if args.mode == "quest":
+        s = s.with_(Kt=min(s.Kb, s.NB) * s.bs)
+    elif args.mode == "dense":
+        s = s.with_(Kb=s.NB, Kt=s.N)
+    ab = algorithmic_bytes(s, dense=args.mode == "dense")
     touched = ab["total"]
     R = args.rotate or max(1, min(64, math.ceil((1 << 30) / touched)))
-    log(f"[bench] {s.name}: generating inputs (rotation over {R} cache copies)")
-    q0 = W.gen_q(s)
-    kv = W.gen_kv(s)
-    lab = W.label_channels(s, kv[0])
-    base = Cache(s, kv, lab).build()
+    log(f"[bench] {s.name} ({args.mode}): generating inputs (rotation over {R} cache copies)")
+    q0 = W.gen_q(s_data)
+    kv = W.gen_kv(s_data)
+    lab = W.label_channels(s_data, kv[0])
+    base = Cache(s_data, kv, lab).build()
     torch.cuda.synchronize()
     caches = [base]
     for r in range(1, R):
@@ -181,7 +208,10 @@ def main():
         c.summ, c.codes, c.scale = base.summ.clone(), base.codes.clone(), base.scale.clone()
         caches.append(c)
     qs = [bf16(q0)] + [bf16(W.gen_q(s.with_(seed=s.seed + 100 * r))) for r in range(1, R)]
-    dec = PipelinedDecoder(s, args.chunks) if args.chunks > 1 else Decoder(s)
+    if args.mode == "dense":
+        dec = DenseDecoder(s)
+    else:
+        dec = PipelinedDecoder(s, args.chunks) if args.chunks > 1 else Decoder(s)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -210,8 +240,9 @@ def main():
         if pipelined:
             dec.step(qs[r], caches[r])
             return
-        dec.select_blocks(qs[r], caches[r])
-        dec.select_tokens(qs[r], caches[r])
+        if args.mode != "dense":
+            dec.select_blocks(qs[r], caches[r])
+            dec.select_tokens(qs[r], caches[r])
         if ev is not None:  # the library records these around its attention kernel
             T.tls_profile_events(T.TLS_PROFILE_ATTENTION, ev[0], ev[1])
         dec.decode(qs[r], caches[r].kv)
@@ -256,7 +287,7 @@ def main():
     # of them, so the GPU runs them back to back as in the timed replays.
     dec_ms, scorer, how = None, None, None
     if not pipelined:
-        P = max(20, 2 * R)
+        P = max(20, 2 * R) if args.mode != "dense" else 5
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(P)]
         torch.cuda._sleep(int(2e7))
         for i in range(P):
@@ -264,7 +295,8 @@ def main():
         torch.cuda.synchronize()
         dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         how = "HIP events recorded by the library around each attention launch, steps queued behind a spin kernel"
-        scorer = block_scorer_mfma(s, dec, qs, caches, stream)
+        if args.mode != "dense":
+            scorer = block_scorer_mfma(s, dec, qs, caches, stream)
 
     roof = None
     if dec_ms:
@@ -272,7 +304,7 @@ def main():
         roof = {"bound": "hbm", "kernel": f"{attention_kernel(s)} (attention of tls_sparse_decode)",
                 "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(s.name),
+                "traffic": measured_traffic(s.name) if args.mode == "tls" else None,
                 "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"],
                 "timing": how}
 
@@ -291,7 +323,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{s.name}: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim {s.D}/{s.DV}, "
                                f"context {s.N}, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, {s.r} INT4 label channels",
-                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs), "chunks": args.chunks},
+                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs), "chunks": args.chunks,
+                   "mode": args.mode},
         "hbm": {"algorithmic_bytes_per_step": ab["total"],
                 "achieved_GBps": round(ab["total"] / step_s / 1e9, 1),
                 "frac_of_peak": round(ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, 4)},
@@ -300,7 +333,7 @@ def main():
         "block_scorer": scorer,
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu:
+    if not args.no_cpu and args.mode == "tls":
         log("[bench] oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline(s, q0, kv, lab, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -93,7 +93,9 @@ typedef struct tls_shape {
 
 /* Bytes of workspace needed by tls_select_blocks (TLS_WS_BLOCKS),
  * tls_select_tokens (TLS_WS_TOKENS) or tls_sparse_decode (TLS_WS_DECODE) for
- * this shape; 0 if the shape is invalid. */
+ * this shape; 0 if the shape is invalid for that call. tls_select_tokens
+ * handles at most 16384 candidates per pair (Kb' * bs); the other calls have
+ * no such limit (attention over every token is Kb >= NB, Kt >= N). */
 size_t tls_workspace_size(const tls_shape_t *shape, int which);
 
 /* Block summaries and the INT4 label cache (section 2A: the block-level index

@@ -85,3 +85,15 @@ def test_argument_errors_before_any_device_work(lib):
     assert rc == T.TLS_ERR_INVALID_ARG and b"both" in lib.tls_last_error()
     assert lib.tls_profile_events(7, None, None) == T.TLS_ERR_INVALID_ARG
     assert lib.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES, None, None) == T.TLS_OK
+
+
+def test_candidate_limit_applies_to_the_token_stage_only(lib):
+    """Attention over every token (Kb >= NB, Kt >= N) is a valid decode shape even
+    when Kb*bs exceeds what the token stage takes (16384 candidates per pair)."""
+    s = W.CONFIGS["c3_128k_gqa"].with_(Kb=2048, Kt=131072)
+    sh = T.shape_of(s)
+    assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_TOKENS) == 0
+    assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_DECODE) > 0
+    assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_BLOCKS) > 0
+    rc = lib.tls_select_tokens(C.byref(sh), 16, 16, 16, 16, 16, 16, 16, 1 << 30, None)
+    assert rc == T.TLS_ERR_UNSUPPORTED and b"candidate" in lib.tls_last_error()

@@ -76,7 +76,6 @@ int derive(const tls_shape_t* s, Derived* d) {
   if (d->bs > 64) return set_error(TLS_ERR_UNSUPPORTED, "block_size above 64");
   if (d->r > 32) return set_error(TLS_ERR_UNSUPPORTED, "more than 32 label channels");
   if (d->NB > 16384) return set_error(TLS_ERR_UNSUPPORTED, "more than 16384 blocks per sequence");
-  if (cand > 16384) return set_error(TLS_ERR_UNSUPPORTED, "more than 16384 candidate tokens (Kb*bs)");
   if (d->N > (int64_t)0x7FFFFFFF) return set_error(TLS_ERR_UNSUPPORTED, "ctx_len above 2^31-1");
   return TLS_OK;
 }
@@ -88,7 +87,9 @@ static size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t ws_bytes(const Derived& d, int which) {
   switch (which) {
     case TLS_WS_BLOCKS: return round_up((size_t)d.pairs * d.NB * sizeof(float));
-    case TLS_WS_TOKENS: return round_up((size_t)d.pairs * d.kb * d.bs * sizeof(float));
+    case TLS_WS_TOKENS:
+      if ((int64_t)d.kb * d.bs > kMaxCandidates) return 0;
+      return round_up((size_t)d.pairs * d.kb * d.bs * sizeof(float));
     case TLS_WS_DECODE: {
       DecodePlan pl;
       plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
@@ -175,6 +176,8 @@ int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* la
   if (rc) return rc;
   if (!q || !label_ch || !codes || !scale || !block_idx || !token_idx)
     return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if ((int64_t)d.kb * d.bs > kMaxCandidates)
+    return set_error(TLS_ERR_UNSUPPORTED, "more than %lld candidate tokens (Kb*bs)", (long long)kMaxCandidates);
   if (!ws || ws_len < ws_bytes(d, TLS_WS_TOKENS))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_TOKENS));
   TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,

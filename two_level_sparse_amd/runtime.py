@@ -74,10 +74,10 @@ class Decoder:
         self.out = o.get("out", torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device=device))
         self.lse = o.get("lse", torch.empty((s.B, s.Hq), dtype=torch.float32, device=device))
         self.ws_sizes = {w: tls_workspace_size(self.shape, w) for w in (TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE)}
-        if min(self.ws_sizes.values()) == 0:
+        if self.ws_sizes[TLS_WS_BLOCKS] == 0 or self.ws_sizes[TLS_WS_DECODE] == 0:
             raise ValueError(f"invalid shape for libtls: {s}")
-        # zero-filled: the decode workspace begins with self-resetting split counters
-        self.ws = {w: torch.zeros(n, dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
+        # (a zero TOKENS size: more candidates than the token stage takes; select_tokens then fails)
+        self.ws = {w: torch.zeros(max(n, 256), dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
 
     def select_blocks(self, q, cache, stream=None, keep_scores=False, block_idx=None):
         bi = self.block_idx if block_idx is None else block_idx
