@@ -732,9 +732,11 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
 }
 
 // Split merge. Workgroup = (256 float4 outputs, head tile, pair): the split
-// weights 2^(m_s - M) / L of the tile's heads are formed in LDS, then every
-// thread reads its float4 of o from all splits with independent loads.
+// weights 2^(m_s - M) / L of the tile's heads are formed in LDS while every
+// thread's float4 of o from the first kMergePre splits is already in flight;
+// then a weighted sum.
 constexpr int kMaxSplits = 64;
+constexpr int kMergePre = 8;
 template <int DV, int HT>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
                                                float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
@@ -744,44 +746,59 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, f
   const int b = p / Hkv, h = p % Hkv;
   constexpr int PS = DV + kPartHdr;  // floats per head in a partial
   const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * PS;
-  for (int e = tid; e < nsplit * HT; e += 256) {
-    const int s = e / HT, hh = e % HT;
-    const float* src = base + ((int64_t)s * HT + hh) * PS;
-    ml_lds[s][hh][0] = src[0];
-    ml_lds[s][hh][1] = src[1];
+  // (m, l) of the splits first, then this thread's o loads, all in flight together
+  float2 ml[(kMaxSplits * HT + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * HT + 255) / 256; ++k) {
+    const int e = tid + 256 * k;
+    if (e < nsplit * HT) {
+      const int s = e / HT, hh = e % HT;
+      ml[k] = *reinterpret_cast<const float2*>(base + ((int64_t)s * HT + hh) * PS);
+    }
+  }
+  const int e = blockIdx.x * 256 + tid;  // float4 index in [HT, DV/4]
+  const int ee = min(e, HT * (DV / 4) - 1);
+  const int hh = ee / (DV / 4), c = (ee % (DV / 4)) * 4;
+  const int g = ht * HT + hh;
+  const bool active = e < HT * (DV / 4) && g < G;
+  const float* src = base + (int64_t)hh * PS + kPartHdr + c;
+  f32x4 ov[kMergePre];
+#pragma unroll
+  for (int s = 0; s < kMergePre; ++s) ov[s] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(s, nsplit - 1) * HT * PS);
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * HT + 255) / 256; ++k) {
+    const int e2 = tid + 256 * k;
+    if (e2 < nsplit * HT) {
+      ml_lds[e2 / HT][e2 % HT][0] = ml[k].x;
+      ml_lds[e2 / HT][e2 % HT][1] = ml[k].y;
+    }
   }
   __syncthreads();
   if (tid < HT) {
-    const int hh = tid;
+    const int hd = tid;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_lds[s][hh][0]);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_lds[s][hd][0]);
     float L = 0.0f;
     for (int s = 0; s < nsplit; ++s) {
-      const float ms = ml_lds[s][hh][0];
+      const float ms = ml_lds[s][hd][0];
       const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-      L += ml_lds[s][hh][1] * w;
-      w_lds[s][hh] = w;
+      L += ml_lds[s][hd][1] * w;
+      w_lds[s][hd] = w;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int s = 0; s < nsplit; ++s) w_lds[s][hh] *= inv;
-    const int g = ht * HT + hh;
-    if (lse && blockIdx.x == 0 && g < G)
-      lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    for (int s = 0; s < nsplit; ++s) w_lds[s][hd] *= inv;
+    const int gg = ht * HT + hd;
+    if (lse && blockIdx.x == 0 && gg < G)
+      lse[(int64_t)b * Hq + (int64_t)h * G + gg] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  const int e = blockIdx.x * 256 + tid;  // float4 index in [HT, DV/4]
-  if (e >= HT * (DV / 4)) return;
-  const int hh = e / (DV / 4), c = (e % (DV / 4)) * 4;
-  const int g = ht * HT + hh;
-  if (g >= G) return;
-  const float* src = base + (int64_t)hh * PS + kPartHdr + c;
+  if (!active) return;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)s * HT * PS);
-    const float w = w_lds[s][hh];
-    o += v * w;
-  }
+#pragma unroll
+  for (int s = 0; s < kMergePre; ++s)
+    if (s < nsplit) o += ov[s] * w_lds[s][hh];
+  for (int s = kMergePre; s < nsplit; ++s)
+    o += *reinterpret_cast<const f32x4*>(src + (int64_t)s * HT * PS) * w_lds[s][hh];
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + (int64_t)h * G + g) * DV + c) = o;
 }
 

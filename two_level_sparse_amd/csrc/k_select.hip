@@ -364,10 +364,9 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
 struct alignas(16) TopkLds {
-  uint32_t hist[256];
+  uint32_t hist[3][256];  // pass i counts into hist[i % 3]
   uint32_t red[3][kTopkWaves];
   uint32_t scan[kTopkWaves];
-  uint32_t sel[3];
 };
 
 // Block-wide exclusive scan of one uint32 per thread; returns the prefix.
@@ -381,6 +380,34 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
+// The bin of a 256-bin histogram that holds the krem-th largest key: every
+// wave reads the whole histogram and finds it on its own (wave-uniform
+// results, no LDS round trip). Lane l holds bins 255-4l .. 252-4l, so an
+// exclusive prefix scan over lanes counts the keys in the bins above.
+struct BinPick {
+  uint32_t bin, above, count;
+};
+__device__ __forceinline__ BinPick pick_bin(const uint32_t* hist, uint32_t krem) {
+  const int lane = threadIdx.x & 63;
+  const int b0 = 252 - 4 * lane;
+  const u32x4 hb = *reinterpret_cast<const u32x4*>(&hist[b0]);
+  const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
+  const uint32_t above = wave_incl_scan(mine) - mine;
+  const uint64_t hit = __ballot(above < krem && krem <= above + mine);
+  const int L = __builtin_ctzll(hit);  // the lane whose 4 bins hold it (one exists: krem <= keys in range)
+  uint32_t bin = 0u, ab = 0u, cnt = 0u, run = above;
+#pragma unroll
+  for (int i = 3; i >= 0; --i) {
+    if (run < krem && krem <= run + hb[i]) {  // true for exactly one bin of lane L
+      bin = (uint32_t)(b0 + i);
+      ab = run;
+      cnt = hb[i];
+    }
+    run += hb[i];
+  }
+  return BinPick{readlane(bin, L), readlane(ab, L), readlane(cnt, L)};
+}
+
 // Selects the K largest keys (ties: lower element index first) and writes
 // their ids ascending to out[0..min(K, valid)), then -1 up to out_len.
 // Radix select. The first pass bins the keys' float values linearly between
@@ -389,28 +416,9 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // into a single bin). The later passes histogram (key - lo) >> shift, the next
 // 8 bits below the top set bit of (hi - lo), over the keys left in [lo, hi].
 // The search stops as soon as the chosen bin is taken whole, with the
-// threshold at the bin's lower edge and every key equal to it kept. One wave finds
-// the bin holding the krem-th largest key and clears the histogram.
-__device__ __forceinline__ void topk_pick_bin(uint32_t krem, TopkLds& sh) {
-  const int lane = threadIdx.x & 63;
-  // lane l holds bins 255-4l .. 252-4l, so a prefix scan over lanes counts
-  // the keys in the bins above
-  const int b0 = 252 - 4 * lane;
-  const u32x4 hb = *reinterpret_cast<const u32x4*>(&sh.hist[b0]);
-  *reinterpret_cast<u32x4*>(&sh.hist[b0]) = u32x4{0u, 0u, 0u, 0u};  // ready for the next pass
-  const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
-  uint32_t above = wave_incl_scan(mine) - mine;
-#pragma unroll
-  for (int i = 3; i >= 0; --i) {
-    if (above < krem && krem <= above + hb[i]) {
-      sh.sel[0] = b0 + i;
-      sh.sel[1] = above;
-      sh.sel[2] = hb[i];
-    }
-    above += hb[i];
-  }
-}
-
+// threshold at the bin's lower edge and every key equal to it kept. One
+// barrier per pass: the histograms rotate over three buffers (a buffer is
+// cleared two passes after its last read), and every wave picks the bin.
 template <int PER>
 __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER], uint32_t K, int32_t* out,
                            int out_len, TopkLds& sh) {
@@ -431,7 +439,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
     sh.red[1][wave] = kmax;
     sh.red[2][wave] = nval;
   }
-  if (tid < 256) sh.hist[tid] = 0u;
+  if (tid < 512) sh.hist[tid >> 8][tid & 255] = 0u;  // buffers 0 and 1
   __syncthreads();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, total = 0u;
 #pragma unroll
@@ -445,6 +453,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
   if (kk < total) {
     krem = kk;
     bool done = false;
+    int pass = 0;  // histogram buffer = pass % 3; pass p clears buffer (p + 1) % 3
     const float vlo = key_float(lo), vhi = key_float(hi);
     const float sc = 256.0f / (vhi - vlo);
     if (hi > lo && sc > 0.0f && sc < INFINITY) {
@@ -453,68 +462,61 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
       for (int e = 0; e < PER; ++e) {
         const float x = key[e] != 0u ? (key_float(key[e]) - vlo) * sc : 0.0f;  // in [0, 256]
         bin[e] = min((uint32_t)x, 255u);
-        if (key[e] != 0u) atomicAdd(&sh.hist[bin[e]], 1u);
+        if (key[e] != 0u) atomicAdd(&sh.hist[0][bin[e]], 1u);
+      }
+      if (tid < 256) sh.hist[2][tid] = 0u;  // (buffer 1 was cleared at the start)
+      __syncthreads();
+      const BinPick pk = pick_bin(sh.hist[0], krem);
+      pass = 1;
+      const uint32_t d = pk.bin;
+      krem -= pk.above;
+      // keys of bin d: one interval [lo, hi] (a block reduction; its barrier
+      // also orders this pass's histogram reads before buffer 0 is cleared)
+      kmin = 0xFFFFFFFFu;
+      kmax = 0u;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (key[e] != 0u && bin[e] == d) {
+          kmin = min(kmin, key[e]);
+          kmax = max(kmax, key[e]);
+        }
+      kmin = wave_umin(kmin);
+      kmax = wave_umax(kmax);
+      if (lane == 0) {
+        sh.red[0][wave] = kmin;
+        sh.red[1][wave] = kmax;
       }
       __syncthreads();
-      if (wave == 0) topk_pick_bin(krem, sh);
-      __syncthreads();
-      const uint32_t d = sh.sel[0];
-      krem -= sh.sel[1];
-      if (krem == sh.sel[2]) {
+      lo = 0xFFFFFFFFu;
+      hi = 0u;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) {
+        lo = min(lo, sh.red[0][w]);
+        hi = max(hi, sh.red[1][w]);
+      }
+      if (krem == pk.count) {
         // the whole bin is taken: the threshold is its smallest key
-        kmin = 0xFFFFFFFFu;
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          if (key[e] != 0u && bin[e] == d) kmin = min(kmin, key[e]);
-        kmin = wave_umin(kmin);
-        if (lane == 0) sh.red[0][wave] = kmin;
-        __syncthreads();
-        lo = 0xFFFFFFFFu;
-#pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) lo = min(lo, sh.red[0][w]);
         thr = lo;
         krem = 0xFFFFFFFFu;
         done = true;
-      } else {
-        // keys of bin d: one interval [lo, hi]
-        kmin = 0xFFFFFFFFu;
-        kmax = 0u;
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          if (key[e] != 0u && bin[e] == d) {
-            kmin = min(kmin, key[e]);
-            kmax = max(kmax, key[e]);
-          }
-        kmin = wave_umin(kmin);
-        kmax = wave_umax(kmax);
-        if (lane == 0) {
-          sh.red[0][wave] = kmin;
-          sh.red[1][wave] = kmax;
-        }
-        __syncthreads();
-        lo = 0xFFFFFFFFu;
-        hi = 0u;
-#pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) {
-          lo = min(lo, sh.red[0][w]);
-          hi = max(hi, sh.red[1][w]);
-        }
       }
     }
     while (!done && hi > lo) {
       const uint32_t diff = hi - lo;
       const int nbits = 32 - __clz(diff);
       const int shift = nbits > 8 ? nbits - 8 : 0;
+      uint32_t* hcur = sh.hist[pass % 3];
 #pragma unroll
       for (int e = 0; e < PER; ++e)
-        if (key[e] >= lo && key[e] <= hi) atomicAdd(&sh.hist[(key[e] - lo) >> shift], 1u);
+        if (key[e] >= lo && key[e] <= hi) atomicAdd(&hcur[(key[e] - lo) >> shift], 1u);
+      if (tid < 256) sh.hist[(pass + 1) % 3][tid] = 0u;  // last read two barriers ago
       __syncthreads();
-      if (wave == 0) topk_pick_bin(krem, sh);
-      __syncthreads();
-      const uint32_t d = sh.sel[0];
-      krem -= sh.sel[1];
+      const BinPick pk = pick_bin(hcur, krem);
+      ++pass;
+      const uint32_t d = pk.bin;
+      krem -= pk.above;
       const uint32_t nlo = lo + (d << shift);
-      if (krem == sh.sel[2]) {
+      if (krem == pk.count) {
         // the whole bin is taken: every key in it is >= nlo and every key
         // of a lower bin is < nlo
         thr = nlo;
