@@ -166,30 +166,52 @@ const int32_t *tls_offload_slot_map(const tls_offload_t *ctx, int32_t step);
 /* Incremental prefetch for step `step` (0, 1, 2, ... in order).
  *   dev_block_idx  M_t [B,Hkv,Kb'] int32 device buffer written by
  *                  tls_select_blocks on `side` (a hipStream_t) before this call.
- * The call enqueues a copy of M_t to host on `side`, waits for it on the
- * calling thread (the calling thread blocks; run it on a helper thread to keep
- * the main stream busy), computes T_t and the evictions, enqueues one
- * host->device copy per transferred block and the next slot map on `side`, and
- * records `copies_done` (a hipEvent_t) on `side`. Step step+1 must wait for
+ * With TLS_COPY_DEVICE the call only enqueues, on `side`, a planning kernel
+ * (T_t, evictions, slot assignment, next slot map) and a copy kernel that
+ * reads the blocks of T_t from host memory, and returns at once; M_t must stay
+ * unchanged until they ran. With the host-planned modes it enqueues a copy of
+ * M_t to host on `side`, waits for it on the calling thread (run it on a
+ * helper thread to keep the main stream busy), computes T_t and the evictions,
+ * and enqueues the block copies and the next slot map on `side`. Either way it
+ * records `copies_done` (a hipEvent_t) on `side`; step step+1 must wait for
  * that event before reading the resident cache. n_copied_opt (host, may be
- * NULL) receives |T_t| summed over all pairs. The pinned staging buffers of
- * the context are reused by the next call, which first waits for `side`. */
+ * NULL) receives |T_t| summed over all pairs, or -1 with TLS_COPY_DEVICE
+ * (read tls_offload_total_copied instead). The pinned staging buffers of the
+ * context are reused by the next call, which first waits for `side`.
+ * With TLS_COPY_DEVICE a run of calls may be captured into a HIP graph: the
+ * planning kernel counts steps on the device, so the captured launches need
+ * no host work; since the slot maps alternate by step parity, replaying the
+ * graph repeatedly needs an even number of captured steps. */
 int tls_prefetch_delta(tls_offload_t *ctx, int32_t step, const int32_t *dev_block_idx, void *side,
                        void *copies_done, int64_t *n_copied_opt);
 
-/* How tls_prefetch_delta moves the blocks of T_t.
- *   TLS_COPY_GATHER (default when host_kv, allocated with hipHostMalloc, has
- *     a device mapping): one kernel on the side stream reads every block of
- *     T_t from host memory and applies the slot-map changes;
- *   TLS_COPY_MEMCPY: one hipMemcpyAsync per block plus a full slot-map upload.
- * Returns TLS_ERR_UNSUPPORTED for GATHER when host_kv has no device mapping.
- * Either mode may be used at any step. */
-enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1 };
+/* Where tls_prefetch_delta plans the transfer of T_t and how it moves it.
+ *   TLS_COPY_DEVICE (default when host_kv, allocated with hipHostMalloc, has a
+ *     device mapping, 2*Kb' <= 1024 and NB <= 16384): planned and copied by
+ *     kernels on the side stream, the calling thread never waits;
+ *   TLS_COPY_GATHER (default when the device limits are exceeded): planned on
+ *     the host, then one kernel on the side stream reads every block of T_t
+ *     from host memory and applies the slot-map changes;
+ *   TLS_COPY_MEMCPY (default without a device mapping): planned on the host,
+ *     one hipMemcpyAsync per block plus a full slot-map upload.
+ * All three give the same slots and maps. Returns TLS_ERR_UNSUPPORTED for a
+ * mode the context cannot run, TLS_ERR_STATE for a move between device and
+ * host planning after step 0 (GATHER <-> MEMCPY may change at any step). */
+enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1, TLS_COPY_DEVICE = 2 };
 int tls_offload_set_copy_mode(tls_offload_t *ctx, int mode);
+/* The current mode, or a negative error code for a NULL context. */
+int tls_offload_get_copy_mode(const tls_offload_t *ctx);
 
 /* Host view of the last transfer (for checking): per pair the count |T_t|
- * and the transferred blocks ascending (host arrays [B*Hkv] and [B*Hkv, Kb']). */
+ * and the transferred blocks ascending (host arrays [B*Hkv] and [B*Hkv, Kb']).
+ * With TLS_COPY_DEVICE the call synchronises the device and returns
+ * TLS_ERR_STATE if a step could not be planned (M_t held a block number
+ * outside [0, NB)); such a step changed no slot and no map entry. */
 int tls_offload_last_delta(const tls_offload_t *ctx, int32_t *counts, int32_t *blocks);
+
+/* Blocks copied since creation, summed over all steps and pairs (host int64).
+ * Synchronises the device with TLS_COPY_DEVICE; errors as tls_offload_last_delta. */
+int tls_offload_total_copied(const tls_offload_t *ctx, int64_t *total);
 
 void tls_offload_destroy(tls_offload_t *ctx);
 
@@ -201,11 +223,13 @@ void tls_offload_destroy(tls_offload_t *ctx);
  *   TLS_PROFILE_BLOCK_SCORES: the block-score GEMM of tls_select_blocks
  *     (not its top-k);
  *   TLS_PROFILE_ATTENTION: the attention kernel of tls_sparse_decode (not
- *     its split merge).
+ *     its split merge);
+ *   TLS_PROFILE_HOST_COPY: the kernel of tls_prefetch_delta that reads the
+ *     blocks of T_t from host memory (TLS_COPY_DEVICE and TLS_COPY_GATHER).
  * NULL, NULL turns it off. Process-wide; set it while no other thread is
  * calling the library. TLS_ERR_INVALID_ARG if exactly one event is NULL or
  * `which` is unknown. */
-enum { TLS_PROFILE_BLOCK_SCORES = 0, TLS_PROFILE_ATTENTION = 1 };
+enum { TLS_PROFILE_BLOCK_SCORES = 0, TLS_PROFILE_ATTENTION = 1, TLS_PROFILE_HOST_COPY = 2 };
 int tls_profile_events(int which, void *start_event, void *end_event);
 
 /* Message for the last failed call on this thread ("" if none). */

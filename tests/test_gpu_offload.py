@@ -30,14 +30,14 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
     cache = Cache(s, kv, lab).build()
     host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
     sd = StaggeredDecoder(s, cache, host, bf16(q0), copy_mode=copy_mode)
-    np.testing.assert_array_equal(to_np(sd.mbuf[2]).reshape(s.pairs, -1), built.block_idx)
+    np.testing.assert_array_equal(to_np(sd.selection(-1)).reshape(s.pairs, -1), built.block_idx)
     stats = dict(moved=0, token_band=0, max_err=0.0)
     prev_blocks = built.block_idx
     for t in range(steps):
         out = sd.step(bf16(qs[t]), helper=helper)
         torch.cuda.synchronize()
         counts, blocks = sd.last_delta()
-        Mt = to_np(sd.mbuf[t % 2]).reshape(s.pairs, -1)
+        Mt = to_np(sd.selection(t)).reshape(s.pairs, -1)
         np.testing.assert_array_equal(Mt, ref.M[t])
         np.testing.assert_array_equal(counts, ref.nT[t])
         for p in range(s.pairs):
@@ -56,11 +56,12 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
         assert err <= 2e-3, (t, err)
         stats["max_err"] = max(stats["max_err"], err)
         prev_blocks = ref.M[t]
+    assert sd.total_copied() == stats["moved"]
     sd.close()
     return stats
 
 
-@pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0)])
+@pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0), (False, 2), (True, 2)])
 def test_staggered_small(helper, mode):
     s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=21)
     rng = np.random.default_rng(21)
@@ -84,3 +85,92 @@ def test_staggered_full_256k_offload():
     lab = W.label_channels(s, kv[0])
     st = run_staggered(s, q0, kv, lab, steps=8, helper=True)
     print(f"[gpu] staggered 256k: {st}", flush=True)
+
+
+def small_context():
+    from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
+    s = W.small_shape(B=1, Hq=4, Hkv=2, N=4096, bs=64, Kb=4, Kt=64, n_outlier=2, seed=5)
+    rng = np.random.default_rng(5)
+    q0 = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    kv = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32))
+    lab = np.tile(np.arange(s.r, dtype=np.int32), (s.Hkv, 1))
+    cache = Cache(s, kv, lab).build()
+    host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
+    return s, q0, StaggeredDecoder(s, cache, host, bf16(q0))
+
+
+def test_device_planning_is_the_default_and_fixed_after_step_0():
+    import two_level_sparse_amd as T
+    from two_level_sparse_amd.runtime import bf16
+    s, q0, sd = small_context()
+    assert sd.copy_mode == T.TLS_COPY_DEVICE
+    T.tls_offload_set_copy_mode(sd.ctx, T.TLS_COPY_GATHER)  # before step 0: allowed
+    T.tls_offload_set_copy_mode(sd.ctx, T.TLS_COPY_DEVICE)
+    sd.step(bf16(q0))
+    torch.cuda.synchronize()
+    with pytest.raises(T.TlsError) as ei:
+        T.tls_offload_set_copy_mode(sd.ctx, T.TLS_COPY_GATHER)
+    assert ei.value.code == T.TLS_ERR_STATE
+    sd.close()
+
+
+def test_device_planning_rejects_an_invalid_selection():
+    """A block number outside [0, NB) in M_t: the planning kernel changes
+    nothing and the next host query reports it."""
+    import two_level_sparse_amd as T
+    s, q0, sd = small_context()
+    bad = sd.selection(-1).clone()
+    bad.view(-1)[1] = s.NB + 3
+    map_before = sd.maps[1].clone()
+    ev = torch.cuda.Event()
+    ev.record()  # creates the HIP event
+    T.tls_prefetch_delta(sd.ctx, 0, bad, sd.side, ev)
+    torch.cuda.synchronize()
+    with pytest.raises(T.TlsError) as ei:
+        sd.total_copied()
+    assert ei.value.code == T.TLS_ERR_STATE
+    # the map of step 1 is the map of step 0 for every pair
+    assert torch.equal(sd.maps[1], sd.maps[0])
+    assert torch.equal(map_before, sd.maps[0])
+    sd.close()
+
+
+def test_staggered_graph_replay_matches_the_oracle():
+    """The same staggered steps captured into one HIP graph (device planning)
+    and replayed: every step's output, the last selection and delta, and the
+    total transfer match the oracle's schedule."""
+    from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=23)
+    rng = np.random.default_rng(23)
+    q0 = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    k = rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32)
+    k[..., :4] *= 8
+    kv = W.f32_to_bf16_bits(k)
+    lab = np.tile(np.arange(s.r, dtype=np.int32), (s.Hkv, 1))
+    steps = 12
+    qs = W.drift_queries(s, q0, steps)
+    ref = oracle.staggered(s, qs, kv, lab, oracle.decode(s, q0, kv, lab))
+    cache = Cache(s, kv, lab).build()
+    host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
+    sd = StaggeredDecoder(s, cache, host, bf16(q0))
+    qd = [bf16(qs[t]) for t in range(steps)]
+    outs = [torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device="cuda") for _ in range(steps)]
+    print("[gpu] staggered graph: capture", flush=True)
+    g = sd.capture(qd, outs)
+    torch.cuda.synchronize()
+    print("[gpu] staggered graph: replay", flush=True)
+    g.replay()
+    torch.cuda.synchronize()
+    errs = []
+    for t in range(steps):
+        o = to_np(outs[t]).reshape(s.pairs, s.G, s.DV)
+        errs.append(float(np.max(np.abs(o - ref.out[t]))))
+    print(f"[gpu] staggered graph: max err per step {max(errs):.2e}", flush=True)
+    assert max(errs) <= 2e-3, errs
+    np.testing.assert_array_equal(to_np(sd.selection(steps - 1)).reshape(s.pairs, -1), ref.M[steps - 1])
+    counts, blocks = sd.last_delta()
+    np.testing.assert_array_equal(counts, ref.nT[steps - 1])
+    for p in range(s.pairs):
+        assert blocks[p, : counts[p]].tolist() == ref.T[steps - 1, p, : ref.nT[steps - 1, p]].tolist()
+    assert sd.total_copied() == int(ref.nT.sum())
+    sd.close()

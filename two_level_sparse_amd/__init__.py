@@ -28,12 +28,13 @@ TLS_ERR_HIP = -4
 TLS_ERR_STATE = -5
 TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE = 0, 1, 2
 
-TLS_COPY_GATHER, TLS_COPY_MEMCPY = 0, 1
-TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION = 0, 1
+TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE = 0, 1, 2
+TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",
             "tls_sparse_decode", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
-            "tls_offload_set_copy_mode", "tls_offload_last_delta", "tls_offload_destroy", "tls_profile_events",
+            "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
+            "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
             "tls_last_error", "tls_version"]
 
 
@@ -76,6 +77,8 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_prefetch_delta": (C.c_int, [vp, i32, vp, vp, vp, C.POINTER(i64)]),
         "tls_offload_last_delta": (C.c_int, [vp, vp, vp]),
         "tls_offload_set_copy_mode": (C.c_int, [vp, C.c_int]),
+        "tls_offload_get_copy_mode": (C.c_int, [vp]),
+        "tls_offload_total_copied": (C.c_int, [vp, C.POINTER(i64)]),
         "tls_offload_destroy": (None, [vp]),
         "tls_profile_events": (C.c_int, [C.c_int, vp, vp]),
         "tls_last_error": (C.c_char_p, []),
@@ -167,6 +170,19 @@ def tls_prefetch_delta(ctx, step, dev_block_idx, side_stream, copies_done_event)
 
 def tls_offload_set_copy_mode(ctx, mode):
     _check(load_library().tls_offload_set_copy_mode(ctx, int(mode)))
+
+
+def tls_offload_get_copy_mode(ctx) -> int:
+    rc = load_library().tls_offload_get_copy_mode(ctx)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def tls_offload_total_copied(ctx) -> int:
+    n = C.c_int64(0)
+    _check(load_library().tls_offload_total_copied(ctx, C.byref(n)))
+    return n.value
 
 
 def tls_offload_last_delta(ctx, counts, blocks):

@@ -15,11 +15,15 @@
 //      writes map (t+1)%2), and records `copies_done` on the side stream.
 // Capacity 2*Kb' is the least that always fits M_{t-1} u M_t.
 //
-// Copy modes: TLS_COPY_GATHER (default when the pinned host cache has a
-// device mapping) moves the whole step's transfer with one kernel that reads
-// the host blocks directly and patches the slot map with the changes of the
-// last two steps; TLS_COPY_MEMCPY issues one hipMemcpyAsync per block plus a
-// full slot-map upload.
+// Copy modes: TLS_COPY_DEVICE (default when the pinned host cache has a
+// device mapping and the shape fits the planning kernel) applies steps 2-4 on
+// the GPU, so the call never waits: the planning kernel keeps the slot owners,
+// the last-selected steps and M_{t-1} in device memory and writes the whole
+// next slot map, and a copy kernel reads the listed blocks from host memory.
+// TLS_COPY_GATHER plans on the host and moves the whole step's transfer with
+// one kernel that reads the host blocks directly and patches the slot map with
+// the changes of the last two steps; TLS_COPY_MEMCPY plans on the host and
+// issues one hipMemcpyAsync per block plus a full slot-map upload.
 //
 // Ordering contract (the caller's streams): the side-stream work of step t
 // (stage 1 and this call) must start after the main stream finished step
@@ -29,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -63,16 +68,90 @@ struct tls_offload {
   const tls::MapItem* map_items_dev = nullptr;
   std::vector<tls::MapItem> prev_changes, cur_changes;
   std::vector<int32_t> last_pos;           // [pairs*NB] dedupe scratch, -1 when unused
+  int64_t total_copied = 0;                // host-planned blocks moved since creation
+  // device planning state (TLS_COPY_DEVICE), one allocation
+  void* dev_state = nullptr;
+  tls::DeltaArgs da{};
 };
 
 static void free_ctx(tls_offload* c) {
   if (!c) return;
+  if (c->dev_state) (void)hipFree(c->dev_state);
   if (c->items) (void)hipHostFree(c->items);
   if (c->map_items) (void)hipHostFree(c->map_items);
   if (c->host_M) (void)hipHostFree(c->host_M);
   for (int i = 0; i < 2; ++i)
     if (c->host_map[i]) (void)hipHostFree(c->host_map[i]);
   delete c;
+}
+
+// Workgroups of the device-planned copy: enough host reads in flight to fill
+// the host link, few enough to leave the memory queues to concurrent kernels.
+// TLS_OFFLOAD_COPY_WGS (1..1024) overrides it when the context is created.
+constexpr int kCopyWorkgroups = 16;
+
+// Device copy of the planning state after the prologue (TLS_COPY_DEVICE).
+static hipError_t init_device_state(tls_offload* c) {
+  const Derived& d = c->d;
+  const size_t P = d.pairs, kb = d.kb, cap = c->cap, NB = d.NB;
+  auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
+  const size_t o_items = 0, o_prev = o_items + up(P * kb * sizeof(CopyItem)), o_owner = o_prev + up(P * kb * 4),
+               o_last = o_owner + up(P * cap * 4), o_counts = o_last + up(P * NB * 4),
+               o_tblocks = o_counts + up(P * 4), o_total = o_tblocks + up(P * kb * 4), o_err = o_total + 256,
+               o_step = o_err + 256, bytes = o_step + 256;
+  hipError_t e = hipMalloc(&c->dev_state, bytes);
+  if (e != hipSuccess) return e;
+  char* base = (char*)c->dev_state;
+  DeltaArgs& a = c->da;
+  a.items = (CopyItem*)(base + o_items);
+  a.prev = (int32_t*)(base + o_prev);
+  a.owner = (int32_t*)(base + o_owner);
+  a.last = (int32_t*)(base + o_last);
+  a.counts = (int32_t*)(base + o_counts);
+  a.tblocks = (int32_t*)(base + o_tblocks);
+  a.total = (unsigned long long*)(base + o_total);
+  a.err = (int32_t*)(base + o_err);
+  a.step_ctr = (int32_t*)(base + o_step);
+  a.pairs = d.pairs;
+  a.NB = d.NB;
+  a.kb = d.kb;
+  a.cap = c->cap;
+  a.bs = d.bs;
+  a.row = d.row;
+  a.N = d.N;
+  a.block_elems = (int64_t)c->block_elems;
+  a.copy_wgs = kCopyWorkgroups;
+  if (const char* env = std::getenv("TLS_OFFLOAD_COPY_WGS")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= 1024) a.copy_wgs = v;
+  }
+  std::vector<int32_t> last32(c->last_sel.begin(), c->last_sel.end());
+  std::vector<int32_t> zeros(P, 0);
+  std::vector<int32_t> none(P * kb, -1);
+  const uint64_t zero64 = 0;
+  const int32_t zero32 = 0;
+  if (e == hipSuccess) e = hipMemcpy(a.prev, c->prev.data(), P * kb * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.owner, c->slot_owner.data(), P * cap * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.last, last32.data(), P * NB * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.counts, zeros.data(), P * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.tblocks, none.data(), P * kb * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.total, &zero64, 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.err, &zero32, 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(a.step_ctr, &zero32, 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return e;
+}
+
+// Reads the device planning results after waiting for the device; reports a
+// step the planning kernel could not apply.
+static int device_state_check(const tls_offload* c) {
+  hipError_t e = hipDeviceSynchronize();
+  int32_t err = 0;
+  if (e == hipSuccess) e = hipMemcpy(&err, c->da.err, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_error(e, "reading the offload state");
+  if (err == 2) return set_error(TLS_ERR_STATE, "M_t held a block number outside [0, NB)");
+  if (err) return set_error(TLS_ERR_STATE, "not enough evictable slots");
+  return TLS_OK;
 }
 
 extern "C" {
@@ -117,7 +196,8 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   {
     // Gather mode needs device views of the host cache and of both lists.
     void *dv = nullptr, *di = nullptr, *dm = nullptr;
-    if (hipHostGetDevicePointer(&dv, const_cast<void*>(host_kv), 0) == hipSuccess && dv &&
+    // (the copy kernels move 16-byte pieces: a block must be a whole number of them)
+    if (c->block_elems % 8 == 0 && hipHostGetDevicePointer(&dv, const_cast<void*>(host_kv), 0) == hipSuccess && dv &&
         hipHostGetDevicePointer(&di, c->items, 0) == hipSuccess && di &&
         hipHostGetDevicePointer(&dm, c->map_items, 0) == hipSuccess && dm) {
       c->host_kv_dev = (const uint16_t*)dv;
@@ -157,6 +237,14 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
     free_ctx(c);
     return hip_error(e, "initial slot map upload");
   }
+  if (c->host_kv_dev && c->cap <= kDeltaMaxCap && d.NB <= kDeltaMaxNB) {
+    e = init_device_state(c);
+    if (e != hipSuccess) {
+      free_ctx(c);
+      return hip_error(e, "device planning state");
+    }
+    c->copy_mode = TLS_COPY_DEVICE;
+  }
   *out = c;
   return TLS_OK;
 }
@@ -174,7 +262,23 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
     return set_error(TLS_ERR_STATE, "prefetch for step %d, expected step %d", step, c->next_step);
   const Derived& d = c->d;
   hipStream_t st = (hipStream_t)side;
-  hipError_t e = hipMemcpyAsync(c->host_M, dev_block_idx, (size_t)d.pairs * d.kb * sizeof(int32_t),
+  hipError_t e;
+  if (c->copy_mode == TLS_COPY_DEVICE) {
+    DeltaArgs a = c->da;
+    a.M = dev_block_idx;
+    a.map_cur = c->dev_map[step & 1];
+    a.map_next = c->dev_map[(step + 1) & 1];
+    hipEvent_t ps, pe;
+    profile_events(TLS_PROFILE_HOST_COPY, &ps, &pe);
+    e = launch_device_delta(a, c->host_kv_dev, c->dev_cache, st, ps, pe);
+    if (e != hipSuccess) return hip_error(e, "delta launch");
+    e = hipEventRecord((hipEvent_t)copies_done, st);
+    if (e != hipSuccess) return hip_error(e, "event record");
+    c->next_step = step + 1;
+    if (n_copied_opt) *n_copied_opt = -1;
+    return TLS_OK;
+  }
+  e = hipMemcpyAsync(c->host_M, dev_block_idx, (size_t)d.pairs * d.kb * sizeof(int32_t),
                                 hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_error(e, "copy of M_t to host");
@@ -263,8 +367,12 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
     for (size_t k = 0; k < both.size(); ++k)
       if (c->last_pos[both[k].index] == (int32_t)k) c->map_items[nmap++] = both[k];
     for (size_t k = 0; k < both.size(); ++k) c->last_pos[both[k].index] = -1;
+    hipEvent_t ps, pe;
+    profile_events(TLS_PROFILE_HOST_COPY, &ps, &pe);
+    if (ps) (void)hipEventRecord(ps, st);
     e = tls::launch_gather_blocks(c->host_kv_dev, c->dev_cache, c->items_dev, nitems, c->map_items_dev, nmap,
                                   c->dev_map[nxt], (int64_t)c->block_elems, st);
+    if (pe) (void)hipEventRecord(pe, st);
     if (e != hipSuccess) return hip_error(e, "gather launch");
   } else {
     std::memcpy(c->host_map[nxt], c->slot_of.data(), c->slot_of.size() * sizeof(int32_t));
@@ -276,6 +384,7 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   e = hipEventRecord((hipEvent_t)copies_done, st);
   if (e != hipSuccess) return hip_error(e, "event record");
   c->next_step = step + 1;
+  c->total_copied += total;
   if (n_copied_opt) *n_copied_opt = total;
   return TLS_OK;
 }
@@ -283,17 +392,54 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
 int tls_offload_set_copy_mode(tls_offload_t* c, int mode) {
   clear_error();
   if (!c) return set_error(TLS_ERR_INVALID_ARG, "NULL context");
-  if (mode != TLS_COPY_GATHER && mode != TLS_COPY_MEMCPY) return set_error(TLS_ERR_INVALID_ARG, "unknown copy mode");
+  if (mode != TLS_COPY_GATHER && mode != TLS_COPY_MEMCPY && mode != TLS_COPY_DEVICE)
+    return set_error(TLS_ERR_INVALID_ARG, "unknown copy mode");
   if (mode == TLS_COPY_GATHER && !c->host_kv_dev)
     return set_error(TLS_ERR_UNSUPPORTED, "host cache has no device mapping; only TLS_COPY_MEMCPY is available");
+  if (mode == TLS_COPY_DEVICE && !c->dev_state)
+    return set_error(TLS_ERR_UNSUPPORTED,
+                     "device planning needs a device-mapped host cache, 2*Kb' <= %d slots and NB <= %d blocks",
+                     kDeltaMaxCap, kDeltaMaxNB);
+  if ((mode == TLS_COPY_DEVICE) != (c->copy_mode == TLS_COPY_DEVICE) && c->next_step != 0)
+    return set_error(TLS_ERR_STATE, "planning can move between host and device only before step 0");
   c->copy_mode = mode;
   return TLS_OK;
 }
 
+int tls_offload_get_copy_mode(const tls_offload_t* c) {
+  if (!c) return set_error(TLS_ERR_INVALID_ARG, "NULL context");
+  return c->copy_mode;
+}
+
 int tls_offload_last_delta(const tls_offload_t* c, int32_t* counts, int32_t* blocks) {
+  clear_error();
   if (!c || !counts || !blocks) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
+  if (c->copy_mode == TLS_COPY_DEVICE) {
+    int rc = device_state_check(c);
+    if (rc) return rc;
+    hipError_t e = hipMemcpy(counts, c->da.counts, (size_t)c->d.pairs * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(blocks, c->da.tblocks, (size_t)c->d.pairs * c->d.kb * 4, hipMemcpyDeviceToHost);
+    return e == hipSuccess ? TLS_OK : hip_error(e, "reading the last transfer");
+  }
   std::memcpy(counts, c->last_counts.data(), c->last_counts.size() * sizeof(int32_t));
   std::memcpy(blocks, c->last_blocks.data(), c->last_blocks.size() * sizeof(int32_t));
+  return TLS_OK;
+}
+
+int tls_offload_total_copied(const tls_offload_t* c, int64_t* total) {
+  clear_error();
+  if (!c || !total) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
+  if (c->copy_mode == TLS_COPY_DEVICE) {
+    int rc = device_state_check(c);
+    if (rc) return rc;
+    unsigned long long t = 0;
+    hipError_t e = hipMemcpy(&t, c->da.total, 8, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_error(e, "reading the transfer count");
+    *total = (int64_t)t;
+    return TLS_OK;
+  }
+  *total = c->total_copied;
   return TLS_OK;
 }
 

@@ -17,7 +17,12 @@ namespace tls {
 
 static thread_local char g_err[512] = "";
 // events recorded around the profiled kernels (index: TLS_PROFILE_*)
-static std::atomic<hipEvent_t> g_prof_start[2], g_prof_end[2];
+static std::atomic<hipEvent_t> g_prof_start[3], g_prof_end[3];
+
+void tls::profile_events(int which, hipEvent_t* start, hipEvent_t* end) {
+  *start = g_prof_start[which].load(std::memory_order_relaxed);
+  *end = g_prof_end[which].load(std::memory_order_relaxed);
+}
 
 int set_error(int code, const char* fmt, ...) {
   va_list ap;
@@ -110,7 +115,7 @@ const char* tls_last_error(void) { return g_err; }
 const char* tls_version(void) { return "tls-gfx950 0.1"; }
 
 int tls_profile_events(int which, void* start_event, void* end_event) {
-  if (which != TLS_PROFILE_BLOCK_SCORES && which != TLS_PROFILE_ATTENTION)
+  if (which != TLS_PROFILE_BLOCK_SCORES && which != TLS_PROFILE_ATTENTION && which != TLS_PROFILE_HOST_COPY)
     return set_error(TLS_ERR_INVALID_ARG, "unknown profiled kernel %d", which);
   if ((start_event == nullptr) != (end_event == nullptr))
     return set_error(TLS_ERR_INVALID_ARG, "pass both events or neither");

@@ -23,6 +23,8 @@ int derive(const tls_shape_t* s, Derived* d);
 int set_error(int code, const char* fmt, ...);
 void clear_error();
 int hip_error(hipError_t e, const char* what);
+// Events registered with tls_profile_events for kernel `which` (NULL: none).
+void profile_events(int which, hipEvent_t* start, hipEvent_t* end);
 bool aligned(const void* p, size_t a);
 size_t ws_bytes(const Derived& d, int which);
 

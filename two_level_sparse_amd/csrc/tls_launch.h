@@ -74,6 +74,30 @@ struct MapItem {
   int32_t value;
   int32_t pad;
 };
+// Device-planned transfer of one step (see k_copy.hip).
+constexpr int kDeltaMaxCap = 1024;    // resident slots per pair (2*Kb')
+constexpr int kDeltaMaxNB = 16384;    // blocks per sequence
+struct DeltaArgs {
+  const int32_t* M;           // [pairs, kb] M_t, ascending
+  int32_t* prev;              // [pairs, kb] M_{t-1}; becomes M_t
+  int32_t* owner;             // [pairs, cap] block held by each slot, -1 free
+  int32_t* last;              // [pairs, NB] last step each block was selected (-2 never, -1 prologue)
+  const int32_t* map_cur;     // [pairs, NB] slot map of step t
+  int32_t* map_next;          // [pairs, NB] slot map of step t+1 (written whole)
+  CopyItem* items;            // [pairs, kb] transfers of the step
+  int32_t* counts;            // [pairs] |T_t|
+  int32_t* tblocks;           // [pairs, kb] T_t ascending, -1 padded
+  unsigned long long* total;  // blocks moved since creation
+  int32_t* err;               // set when a step cannot be planned
+  int32_t* step_ctr;          // steps planned so far (the LRU clock), advanced by the copy kernel
+  int pairs, NB, kb, cap, bs, row;
+  int copy_wgs;               // workgroups of the copy kernel
+  int64_t N, block_elems;
+};
+// prof_start/prof_end (may be null) are recorded around the copy kernel.
+hipError_t launch_device_delta(const DeltaArgs& a, const uint16_t* host_kv_dev, uint16_t* dev_cache, hipStream_t st,
+                               hipEvent_t prof_start, hipEvent_t prof_end);
+
 hipError_t launch_gather_blocks(const uint16_t* host_kv_dev, uint16_t* dev_cache, const CopyItem* items, int nitems,
                                 const MapItem* map_items, int nmap, int32_t* slot_map, int64_t block_elems,
                                 hipStream_t st);

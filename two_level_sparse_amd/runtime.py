@@ -163,13 +163,20 @@ class StaggeredDecoder:
     """Staggered decode steps over a KV cache held in pinned host memory.
 
     Step t (AsyncTLS pages, section 2B): the token stage and the attention use
-    M_{t-1}, the blocks chosen at step t-1, which are resident on the device;
-    stage 1 for step t (M_t) runs on a side stream, and a helper thread calls
-    tls_prefetch_delta, which copies only the blocks of M_t missing from the
-    resident cache and writes the slot map of step t+1. The main stream of step
-    t+1 waits for those copies. Stream order makes the side work of step t start
-    after the attention of step t-1 finished, so no slot or map entry a running
-    kernel reads is ever written.
+    M_{t-1}, the blocks chosen at step t-1, which are resident on the device,
+    while the next selection is prepared on two side streams:
+      stage stream: stage 1 for step t (M_t, from q_t and the block summaries);
+      copy stream:  tls_prefetch_delta -- T_t = M_t minus the resident blocks,
+                    evictions, and the host->device copies of T_t, which also
+                    writes the slot map of step t+1.
+    The main stream of step t+1 waits for those copies. The copy stream of step
+    t waits for the main stream of step t-1 (so no slot or map entry that a
+    running kernel reads is ever written) and for M_t. The stage stream of step
+    t waits for the main stream of step t-1 only, so stage 1 runs under the
+    copies of step t-1; M_t rotates over three buffers, and the buffer it
+    overwrites (M_{t-3}) was last read by the token stage of step t-2 and the
+    prefetch of step t-3, both finished before the main stream of step t-1
+    started.
 
     `cache` holds the summaries and label cache on the device (its `kv` is not
     read); `host_kv` is the full cache [B,Hkv,N,row] bf16 in pinned memory.
@@ -184,32 +191,56 @@ class StaggeredDecoder:
         self.cap = 2 * self.kb
         self.dev_cache = torch.empty((s.B, s.Hkv, self.cap, s.bs, s.row), dtype=torch.bfloat16, device=device)
         self.maps = [torch.full((s.B, s.Hkv, s.NB), -1, dtype=torch.int32, device=device) for _ in range(2)]
+        # M_t lives in mbuf[t % 3]; M_{-1} (the prologue's selection) in mbuf[2]
         self.mbuf = [torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device) for _ in range(3)]
+        self.stage = torch.cuda.Stream(device=device)
         self.side = torch.cuda.Stream(device=device)
+        # the first launch on a new stream sets up its hardware queue, which
+        # takes milliseconds: do it here rather than in the first step
+        for st in (self.stage, self.side):
+            with torch.cuda.stream(st):
+                torch.zeros(1, device=device)
         self.events = [torch.cuda.Event() for _ in range(2)]
-        for ev in self.events:
+        self.m_ready = torch.cuda.Event()
+        for ev in self.events + [self.m_ready]:
             ev.record()  # materialise the HIP events
         # prologue: M_{-1} = stage 1 of q_0, loaded synchronously
         self.dec.select_blocks(q0, cache, block_idx=self.mbuf[2])
         torch.cuda.synchronize()
         init = self.mbuf[2].cpu().numpy().astype(np.int32)
         self.ctx = tls_offload_create_ctx(self.dec.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
+        from . import TLS_COPY_DEVICE, tls_offload_get_copy_mode, tls_offload_set_copy_mode
         if copy_mode is not None:
-            from . import tls_offload_set_copy_mode
             tls_offload_set_copy_mode(self.ctx, copy_mode)
+        self.copy_mode = tls_offload_get_copy_mode(self.ctx)
+        self.device_planned = self.copy_mode == TLS_COPY_DEVICE
         self.t = 0
         self.copied = []
 
-    def step(self, q_t, helper=True):
-        """Enqueue step t; returns the output buffer [B, Hq, DV] (valid after sync)."""
+    def selection(self, t):
+        """Device buffer holding M_t (valid for three steps after step t)."""
+        return self.mbuf[t % 3]
+
+    def step(self, q_t, helper=None):
+        """Enqueue step t; returns the output buffer [B, Hq, DV] (valid after sync).
+
+        Host-planned modes run tls_prefetch_delta on a helper thread (it waits
+        for M_t); with device planning it only enqueues, so no thread is used
+        unless `helper` is True. `copied` gets |T_t| per step (-1 when the
+        device planned it; see total_copied)."""
         import threading
         from . import tls_offload_slot_map, tls_prefetch_delta
+        if helper is None:
+            helper = not self.device_planned
         t = self.t
         main = torch.cuda.current_stream()
-        mt = self.mbuf[t % 2]
+        mt = self.selection(t)
+        self.stage.wait_stream(main)
+        with torch.cuda.stream(self.stage):
+            self.dec.select_blocks(q_t, self.cache, stream=self.stage, block_idx=mt)
+        self.m_ready.record(self.stage)
         self.side.wait_stream(main)
-        with torch.cuda.stream(self.side):
-            self.dec.select_blocks(q_t, self.cache, stream=self.side, block_idx=mt)
+        self.side.wait_event(self.m_ready)
         res = {}
 
         def prefetch():
@@ -222,8 +253,7 @@ class StaggeredDecoder:
             prefetch()
         if t > 0:
             main.wait_event(self.events[(t - 1) % 2])
-        prev = self.mbuf[2] if t == 0 else self.mbuf[(t - 1) % 2]
-        self.dec.select_tokens(q_t, self.cache, block_idx=prev)
+        self.dec.select_tokens(q_t, self.cache, block_idx=self.selection(t - 1))
         self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t), slots=self.cap)
         if th:
             th.join()
@@ -231,12 +261,40 @@ class StaggeredDecoder:
         self.t += 1
         return self.dec.out
 
+    def capture(self, queries, outputs=None):
+        """Record the next len(queries) steps into a HIP graph and return it
+        (a torch.cuda.CUDAGraph; nothing runs until it is replayed).
+
+        Needs device planning (TLS_COPY_DEVICE): the library's planning kernel
+        keeps its own step count, so the captured launches need no host work.
+        `outputs`, if given, is one [B, Hq, DV] fp32 tensor per step that the
+        graph fills. The graph holds the buffers of those steps (selections
+        rotate over three buffers, slot maps alternate by step parity), so
+        replay it once, or repeatedly only when len(queries) is a multiple of 6."""
+        if not self.device_planned:
+            raise RuntimeError("graph capture needs device planning (TLS_COPY_DEVICE)")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            main = torch.cuda.current_stream()
+            for i, q in enumerate(queries):
+                out = self.step(q, helper=False)
+                if outputs is not None:
+                    outputs[i].copy_(out)
+            main.wait_stream(self.stage)
+            main.wait_stream(self.side)
+        return g
+
     def last_delta(self):
         from . import tls_offload_last_delta
         counts = np.zeros(self.s.pairs, dtype=np.int32)
         blocks = np.zeros((self.s.pairs, self.kb), dtype=np.int32)
         tls_offload_last_delta(self.ctx, counts, blocks)
         return counts, blocks
+
+    def total_copied(self):
+        """Blocks copied since creation over all pairs (synchronises the device)."""
+        from . import tls_offload_total_copied
+        return tls_offload_total_copied(self.ctx)
 
     def close(self):
         from . import tls_offload_destroy
