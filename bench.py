@@ -218,7 +218,7 @@ def main():
     torch.cuda.synchronize()
 
     graphs = None
-    if args.graph and args.chunks == 1:
+    if args.graph:
         graphs = []
         side = torch.cuda.Stream()
         side.wait_stream(stream)
