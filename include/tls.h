@@ -89,6 +89,8 @@ typedef struct tls_shape {
   int32_t top_kb;        /* Kb >= 1; values above NB keep every block            */
   int32_t top_kt;        /* Kt >= 1; values above Kb'*bs keep every candidate    */
   float sm_scale;        /* softmax scale applied to q.k (e.g. 1/sqrt(D))        */
+  int64_t ctx_capacity;  /* tokens allocated per sequence (>= ctx_len; 0 means   */
+                         /*    ctx_len): the stride of every per-sequence array  */
 } tls_shape_t;
 
 /* Bytes of workspace needed by tls_select_blocks (TLS_WS_BLOCKS),
@@ -107,6 +109,20 @@ size_t tls_workspace_size(const tls_shape_t *shape, int which);
  * code_i = clamp(rint(K[t,c_i] / scale), -7, 7), both divisions in double. */
 int tls_build_summaries(const tls_shape_t *shape, const void *kv, const int32_t *label_ch, void *summ,
                         uint8_t *codes, float *scale, void *stream);
+
+/* Decode-time append (the cache grows by n_new tokens per sequence).
+ *   shape->ctx_len is the length BEFORE the append; ctx_len + n_new must not
+ *   exceed ctx_capacity, the allocated length (the stride of kv, summ, codes
+ *   and scale).
+ *   new_kv [B,Hkv,n_new,row] bf16 device: the new rows, K then V (K only when
+ *   v_is_k_prefix), 16-byte aligned like kv.
+ * Writes the rows to positions ctx_len .. ctx_len+n_new-1 of kv and rebuilds
+ * the summaries of the blocks holding them, and the codes and scales of all
+ * their tokens, from the grown cache, so that summ, codes and scale equal what
+ * tls_build_summaries gives for length ctx_len + n_new. Later calls pass
+ * ctx_len + n_new. Two launches on `stream`; errors as tls_build_summaries. */
+int tls_append_kv(const tls_shape_t *shape, const void *new_kv, int32_t n_new, void *kv, const int32_t *label_ch,
+                  void *summ, uint8_t *codes, float *scale, void *stream);
 
 /* Stage 1 (section 2A, coarse block filtering).
  *   s[g, j] = sum_c max(q_gc Kmax_jc, q_gc Kmin_jc) = [q_g+, q_g-] . [Kmax_j; Kmin_j]

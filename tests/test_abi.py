@@ -97,3 +97,28 @@ def test_candidate_limit_applies_to_the_token_stage_only(lib):
     assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_BLOCKS) > 0
     rc = lib.tls_select_tokens(C.byref(sh), 16, 16, 16, 16, 16, 16, 16, 1 << 30, None)
     assert rc == T.TLS_ERR_UNSUPPORTED and b"candidate" in lib.tls_last_error()
+
+
+def test_append_checks_the_capacity_before_any_device_work(lib):
+    """tls_append_kv: the grown length must fit the allocated capacity, which
+    must itself hold the current length; offload contexts take no spare capacity."""
+    s = W.small_shape(N=1000)
+    sh = T.shape_of(s, capacity=1064)
+    rc = lib.tls_append_kv(C.byref(sh), None, 1, 16, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"NULL" in lib.tls_last_error()
+    rc = lib.tls_append_kv(C.byref(sh), 16, 0, 16, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"n_new" in lib.tls_last_error()
+    rc = lib.tls_append_kv(C.byref(sh), 16, 65, 16, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"capacity" in lib.tls_last_error()
+    rc = lib.tls_append_kv(C.byref(sh), 8, 1, 16, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG   # new_kv not 16-byte aligned
+    small = T.shape_of(s, capacity=999)
+    assert lib.tls_workspace_size(C.byref(small), T.TLS_WS_BLOCKS) == 0
+    rc = lib.tls_append_kv(C.byref(small), 16, 1, 16, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"ctx_capacity" in lib.tls_last_error()
+    # a capacity beyond the length is a valid shape for every call
+    assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_DECODE) > 0
+    h = C.c_void_p()
+    off = T.shape_of(s.with_(N=1024), capacity=1088)
+    rc = lib.tls_offload_create(C.byref(off), 16, 16, 16, 16, 16, C.byref(h))
+    assert rc == T.TLS_ERR_UNSUPPORTED and h.value is None

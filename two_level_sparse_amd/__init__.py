@@ -32,7 +32,7 @@ TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE = 0, 1, 2
 TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",
-            "tls_sparse_decode", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
+            "tls_sparse_decode", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
             "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
             "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
             "tls_last_error", "tls_version"]
@@ -42,7 +42,8 @@ class tls_shape_t(C.Structure):
     _fields_ = [("batch", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
                 ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32), ("v_is_k_prefix", C.c_int32),
                 ("ctx_len", C.c_int64), ("block_size", C.c_int32), ("num_label_ch", C.c_int32),
-                ("top_kb", C.c_int32), ("top_kt", C.c_int32), ("sm_scale", C.c_float)]
+                ("top_kb", C.c_int32), ("top_kt", C.c_int32), ("sm_scale", C.c_float),
+                ("ctx_capacity", C.c_int64)]
 
 
 class TlsError(RuntimeError):
@@ -69,6 +70,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
     sig = {
         "tls_workspace_size": (sz, [sh, C.c_int]),
         "tls_build_summaries": (C.c_int, [sh, vp, vp, vp, vp, vp, vp]),
+        "tls_append_kv": (C.c_int, [sh, vp, i32, vp, vp, vp, vp, vp, vp]),
         "tls_select_blocks": (C.c_int, [sh, vp, vp, vp, vp, vp, sz, vp]),
         "tls_select_tokens": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_sparse_decode": (C.c_int, [sh, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
@@ -116,10 +118,11 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def shape_of(s) -> tls_shape_t:
-    """tls_shape_t from any object with the workload attributes (B, Hq, Hkv, D, DV, ...)."""
+def shape_of(s, capacity: int = 0) -> tls_shape_t:
+    """tls_shape_t from any object with the workload attributes (B, Hq, Hkv, D, DV, ...);
+    `capacity`: allocated tokens per sequence (0: exactly N)."""
     return tls_shape_t(s.B, s.Hq, s.Hkv, s.D, s.DV, int(bool(s.v_is_k_prefix)), s.N, s.bs, s.r, s.Kb, s.Kt,
-                       float(s.sm_scale))
+                       float(s.sm_scale), int(capacity))
 
 
 def tls_workspace_size(shape: tls_shape_t, which: int) -> int:
@@ -129,6 +132,12 @@ def tls_workspace_size(shape: tls_shape_t, which: int) -> int:
 def tls_build_summaries(shape, kv, label_ch, summ, codes, scale, stream=None):
     _check(load_library().tls_build_summaries(C.byref(shape), _ptr(kv), _ptr(label_ch), _ptr(summ), _ptr(codes),
                                               _ptr(scale), _stream(stream)))
+
+
+def tls_append_kv(shape, new_kv, n_new, kv, label_ch, summ, codes, scale, stream=None):
+    """shape.ctx_len: the length before the append; shape.ctx_capacity: the allocated length."""
+    _check(load_library().tls_append_kv(C.byref(shape), _ptr(new_kv), int(n_new), _ptr(kv), _ptr(label_ch),
+                                        _ptr(summ), _ptr(codes), _ptr(scale), _stream(stream)))
 
 
 def tls_select_blocks(shape, q, summ, block_idx, block_score=None, ws=None, ws_bytes=0, stream=None):

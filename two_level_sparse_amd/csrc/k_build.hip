@@ -19,18 +19,18 @@ template <int RMAX>
 __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, const int32_t* __restrict__ label_ch,
                                                uint16_t* __restrict__ summ, uint8_t* __restrict__ codes,
                                                float* __restrict__ scale, int Hkv, int D, int row, int64_t N, int bs,
-                                               int r, int64_t NB) {
+                                               int r, int64_t NB, int64_t Ns, int64_t NBs, int64_t j_first) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t j = j_first + (int64_t)blockIdx.x * 4 + wave;
   const int p = blockIdx.y;
   if (j >= NB) return;
   const int h = p % Hkv;
-  const uint16_t* base = kv + (int64_t)p * N * row;
+  const uint16_t* base = kv + (int64_t)p * Ns * row;
   const int64_t t0 = j * bs;
   const int64_t t1 = t0 + bs < N ? t0 + bs : N;
 
   // Per-channel max / min over the valid tokens of block j.
-  uint16_t* smax = summ + ((int64_t)p * NB + j) * 2 * D;
+  uint16_t* smax = summ + ((int64_t)p * NBs + j) * 2 * D;
   uint16_t* smin = smax + D;
   for (int c = 2 * lane; c < D; c += 128) {
     float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
@@ -74,22 +74,39 @@ __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, 
         code[i] = (int)qv;
       }
     }
-    uint8_t* cp = codes + ((int64_t)p * N + t) * (r / 2);
+    uint8_t* cp = codes + ((int64_t)p * Ns + t) * (r / 2);
 #pragma unroll
     for (int i = 0; i < RMAX; i += 2)
       if (i < r) cp[i / 2] = (uint8_t)((code[i] & 0xF) | ((code[i + 1] & 0xF) << 4));
-    scale[(int64_t)p * N + t] = sc;
+    scale[(int64_t)p * Ns + t] = sc;
   }
 }
 
+// Appended rows: workgroup (i, p) copies new row i of pair p (row*2 bytes, a
+// multiple of 16) to position N0 + i of the pair's cache.
+__global__ __launch_bounds__(64) void k_append_rows(const uint16_t* __restrict__ src, uint16_t* __restrict__ kv,
+                                                    int n_new, int row, int64_t N0, int64_t Ns) {
+  const int i = blockIdx.x, p = blockIdx.y;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + ((int64_t)p * n_new + i) * row);
+  u32x4* d = reinterpret_cast<u32x4*>(kv + ((int64_t)p * Ns + N0 + i) * row);
+  for (int k = threadIdx.x; k < row / 8; k += 64) d[k] = s[k];
+}
+
+hipError_t launch_append_rows(const uint16_t* src, uint16_t* kv, int pairs, int n_new, int row, int64_t N0,
+                              int64_t Ns, hipStream_t st) {
+  hipLaunchKernelGGL(k_append_rows, dim3((unsigned)n_new, (unsigned)pairs), dim3(64), 0, st, src, kv, n_new, row, N0,
+                     Ns);
+  return hipGetLastError();
+}
+
 hipError_t launch_build(const BuildArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)((a.NB + 3) / 4), (unsigned)a.pairs);
+  dim3 grid((unsigned)((a.NB - a.j_first + 3) / 4), (unsigned)a.pairs);
   if (a.r <= 16)
     hipLaunchKernelGGL(k_build<16>, grid, dim3(256), 0, st, a.kv, a.label_ch, a.summ, a.codes, a.scale, a.Hkv, a.D,
-                       a.row, a.N, a.bs, a.r, a.NB);
+                       a.row, a.N, a.bs, a.r, a.NB, a.Ns, a.NBs, a.j_first);
   else
     hipLaunchKernelGGL(k_build<32>, grid, dim3(256), 0, st, a.kv, a.label_ch, a.summ, a.codes, a.scale, a.Hkv, a.D,
-                       a.row, a.N, a.bs, a.r, a.NB);
+                       a.row, a.N, a.bs, a.r, a.NB, a.Ns, a.NBs, a.j_first);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ template <int D, int DV, int HT, bool PRE, bool SMAP>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map,
                                                 const int32_t* __restrict__ token_idx, float* __restrict__ part,
-                                                int Hq, int Hkv, int G, int row, int v_off, int64_t N, int bs,
+                                                int Hq, int Hkv, int G, int row, int v_off, int64_t N, int64_t Ns, int bs,
                                                 int64_t NB, int slots, int kt, int tps, int nsplit, int nht,
                                                 float qk_scale) {
   constexpr int KSTEPS = D / 32;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, 
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
   const int32_t* tix = token_idx + (int64_t)p * kt;
-  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * Ns) * row;
   const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
 
   float m_run[4], l_run[4];
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
                                                        const int32_t* __restrict__ slot_map,
                                                        const int32_t* __restrict__ token_idx,
                                                        float* __restrict__ part, int Hq, int Hkv, int G, int row,
-                                                       int v_off, int64_t N, int bs, int64_t NB, int slots, int kt,
+                                                       int v_off, int64_t N, int64_t Ns, int bs, int64_t NB, int slots, int kt,
                                                        int tps, int nsplit, int nht, float qk_scale) {
   constexpr int KSTEPS = D / 32;
   constexpr int CPL = DV / 64;  // value channels per lane
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
   const int32_t* tix = token_idx + (int64_t)p * kt;
-  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * row;
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * Ns) * row;
   const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
 
   float m_run[4], l_run[4];
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
                                                        const int32_t* __restrict__ slot_map,
                                                        const int32_t* __restrict__ token_idx,
                                                        float* __restrict__ part, int Hq, int Hkv, int G, int64_t N,
-                                                       int bs, int64_t NB, int slots, int kt, int tps, int nsplit,
+                                                       int64_t Ns, int bs, int64_t NB, int slots, int kt, int tps, int nsplit,
                                                        int nhg, float qk_scale) {
   constexpr int D = 576, DV = 512, KS = D / 32;
   constexpr int CP = D / 8;           // 16-byte column pieces per row = LDS chunks per tile
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
   const int ntok = max(t_end - t_begin, 0);
-  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * N) * D;
+  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * Ns) * D;
 
   // rows of the split's tokens (-1: masked), and the first valid one
   if (tid == 0) first_ok = 0x7FFFFFFF;
@@ -869,11 +869,11 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
   if constexpr (D <= 128) {  // wider rows: the per-lane buffers of k_attend_gqa would spill
     if (a.slot_map)
       hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                          pl.nsplit, pl.nht, a.sm_scale * kLog2e);
     else
       hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                          pl.nsplit, pl.nht, a.sm_scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -882,11 +882,11 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
   }
   if (a.slot_map)
     hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   else
     hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -911,11 +911,11 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
   prof_mark(a.prof_start, st);
   if (a.slot_map)
     hipLaunchKernelGGL(k_attend_mla<true>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
-                       a.Hq, a.Hkv, a.G, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
+                       a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
                        a.sm_scale * kLog2e);
   else
     hipLaunchKernelGGL(k_attend_mla<false>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
-                       a.Hq, a.Hkv, a.G, a.N, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
+                       a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
                        a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -50,7 +50,7 @@ __device__ __forceinline__ void split_sign(u32x4 raw, u32x4& pos, u32x4& neg) {
 template <int MT, int NSUB, int KC, int UNR>
 __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ summ, float* __restrict__ S,
-                                                      int Hq, int Hkv, int G, int D, int64_t NB) {
+                                                      int Hq, int Hkv, int G, int D, int64_t NB, int64_t NBs) {
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
   const int64_t jbase = ((int64_t)blockIdx.x * 4 + wave) * (16 * NSUB);
   if (jbase >= NB) return;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-  const uint16_t* sp = summ + (int64_t)p * NB * 2 * D;
+  const uint16_t* sp = summ + (int64_t)p * NBs * 2 * D;
 
   const uint16_t* brow[NSUB];
 #pragma unroll
@@ -135,7 +135,7 @@ template <int MT, int KC>
 __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint16_t* __restrict__ q,
                                                                      const uint16_t* __restrict__ summ,
                                                                      float* __restrict__ S, int Hq, int Hkv, int G,
-                                                                     int64_t NB) {
+                                                                     int64_t NB, int64_t NBs) {
   constexpr int D = KC * 32;
   constexpr int MW = 2;                 // head tiles per wave
   constexpr int KH = KC / 2;            // channel chunks per wave
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint1
   // and are not stored.
   const int64_t t0 = (int64_t)tg * kLdsTiles;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-  const uint16_t* sp = summ + (int64_t)p * NB * 2 * D;
+  const uint16_t* sp = summ + (int64_t)p * NBs * 2 * D;
 
   // Direct loads of tiles [ta, tb): wave w issues pieces w, w+8, ...
   auto issue = [&](int ta, int tb) {
@@ -308,7 +308,7 @@ static void go_blocks_k(const BlockScoreArgs& a, hipStream_t st) {
   const int64_t per_wg = 4 * 16 * NSUB;
   dim3 grid((unsigned)((a.NB + per_wg - 1) / per_wg), (unsigned)a.pairs);
   hipLaunchKernelGGL((k_score_blocks<MT, NSUB, KC, UNR>), grid, dim3(256), 0, st, a.q, a.summ, a.S, a.Hq, a.Hkv, a.G,
-                     a.D, a.NB);
+                     a.D, a.NB, a.NBs);
 }
 
 // Always 8 head tiles: for G < 128 the extra tiles run on clamped q rows and
@@ -318,7 +318,7 @@ static void go_blocks_lds(const BlockScoreArgs& a, hipStream_t st) {
   const int64_t ntiles = (a.NB + 15) / 16;
   const int64_t gx = (ntiles + kLdsTiles - 1) / kLdsTiles;
   hipLaunchKernelGGL((k_score_blocks_lds<8, KC>), dim3((unsigned)(gx * a.pairs)), dim3(kLdsWaves * 64), 0, st, a.q, a.summ,
-                     a.S, a.Hq, a.Hkv, a.G, a.NB);
+                     a.S, a.Hq, a.Hkv, a.G, a.NB, a.NBs);
 }
 
 template <int MT, int NSUB>
@@ -723,8 +723,8 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
                                                       const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scale,
                                                       const int32_t* __restrict__ block_idx, float* __restrict__ A,
-                                                      int Hq, int Hkv, int G, int D, int64_t N, int bs, int bsh,
-                                                      int r, int kb) {
+                                                      int Hq, int Hkv, int G, int D, int64_t N, int64_t Ns, int bs,
+                                                      int bsh, int r, int kb) {
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kq = lane >> 4;
@@ -735,7 +735,7 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
   for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
   const int c0 = blockIdx.x * (4 * kUnitTiles * 16) + wave * (kUnitTiles * 16);
   UnitLoads L;
-  unit_loads<RB>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * N * rb, scale + (int64_t)p * N, c0, ncand, N,
+  unit_loads<RB>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N,
                  bs, bsh, rb);
   u32x4 qa[MT];
   label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
@@ -805,7 +805,7 @@ static void go_score_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) 
   const int ncand = a.kb * a.bs;
   dim3 grid((unsigned)((ncand + 1023) / 1024), (unsigned)a.pairs);
   hipLaunchKernelGGL((k_score_tokens<MT, RB>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, a.block_idx,
-                     A, a.Hq, a.Hkv, a.G, a.D, a.N, a.bs, log2_or_neg(a.bs), a.r, a.kb);
+                     A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, a.kb);
 }
 
 template <int MT>

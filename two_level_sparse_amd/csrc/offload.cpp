@@ -167,6 +167,7 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   if (!host_kv || !dev_cache || !dev_slot_map0 || !dev_slot_map1 || !initial_blocks)
     return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
   if (d.N % d.bs != 0) return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_len to be a multiple of block_size");
+  if (d.Ns != d.N) return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_capacity equal to ctx_len (no appends)");
   tls_offload* c = new tls_offload;
   c->d = d;
   c->host_kv = (const uint16_t*)host_kv;

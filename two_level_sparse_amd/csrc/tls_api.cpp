@@ -69,6 +69,11 @@ int derive(const tls_shape_t* s, Derived* d) {
   d->bs = s->block_size;
   d->r = s->num_label_ch;
   d->NB = (d->N + d->bs - 1) / d->bs;
+  if (s->ctx_capacity != 0 && s->ctx_capacity < s->ctx_len)
+    return set_error(TLS_ERR_INVALID_ARG, "ctx_capacity (%lld) is below ctx_len (%lld)", (long long)s->ctx_capacity,
+                     (long long)s->ctx_len);
+  d->Ns = s->ctx_capacity ? s->ctx_capacity : d->N;
+  d->NBs = (d->Ns + d->bs - 1) / d->bs;
   d->kb = (int)(s->top_kb < d->NB ? s->top_kb : d->NB);
   const int64_t cand = (int64_t)d->kb * d->bs;
   d->kt = (int)(s->top_kt < cand ? s->top_kt : cand);
@@ -81,7 +86,7 @@ int derive(const tls_shape_t* s, Derived* d) {
   if (d->bs > 64) return set_error(TLS_ERR_UNSUPPORTED, "block_size above 64");
   if (d->r > 32) return set_error(TLS_ERR_UNSUPPORTED, "more than 32 label channels");
   if (d->NB > 16384) return set_error(TLS_ERR_UNSUPPORTED, "more than 16384 blocks per sequence");
-  if (d->N > (int64_t)0x7FFFFFFF) return set_error(TLS_ERR_UNSUPPORTED, "ctx_len above 2^31-1");
+  if (d->Ns > (int64_t)0x7FFFFFFF) return set_error(TLS_ERR_UNSUPPORTED, "ctx_capacity above 2^31-1");
   return TLS_OK;
 }
 
@@ -140,9 +145,33 @@ int tls_build_summaries(const tls_shape_t* shape, const void* kv, const int32_t*
   if (!aligned(kv, 4) || !aligned(summ, 4) || !aligned(scale, 4) || !aligned(label_ch, 4))
     return set_error(TLS_ERR_INVALID_ARG, "kv, summ, scale and label_ch must be 4-byte aligned");
   BuildArgs a{(const uint16_t*)kv, label_ch, (uint16_t*)summ, codes, scale, d.pairs, d.Hkv, d.D, d.row, d.bs, d.r,
-              d.N, d.NB};
+              d.N, d.NB, d.Ns, d.NBs, 0};
   hipError_t e = launch_build(a, (hipStream_t)stream);
   return e == hipSuccess ? TLS_OK : hip_error(e, "build_summaries launch");
+}
+
+int tls_append_kv(const tls_shape_t* shape, const void* new_kv, int32_t n_new, void* kv, const int32_t* label_ch,
+                  void* summ, uint8_t* codes, float* scale, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!new_kv || !kv || !label_ch || !summ || !codes || !scale) return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (n_new < 1) return set_error(TLS_ERR_INVALID_ARG, "n_new must be >= 1");
+  if (d.N + n_new > d.Ns)
+    return set_error(TLS_ERR_INVALID_ARG, "ctx_len + n_new (%lld) exceeds ctx_capacity (%lld)",
+                     (long long)(d.N + n_new), (long long)d.Ns);
+  if (!aligned(new_kv, 16) || !aligned(kv, 16) || !aligned(summ, 4) || !aligned(scale, 4) || !aligned(label_ch, 4))
+    return set_error(TLS_ERR_INVALID_ARG, "new_kv and kv must be 16-byte aligned, summ, scale and label_ch 4-byte");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_append_rows((const uint16_t*)new_kv, (uint16_t*)kv, d.pairs, n_new, d.row, d.N, d.Ns, st);
+  if (e != hipSuccess) return hip_error(e, "append_rows launch");
+  // the blocks holding the new tokens, built over all their tokens
+  const int64_t N1 = d.N + n_new, NB1 = (N1 + d.bs - 1) / d.bs;
+  BuildArgs a{(const uint16_t*)kv, label_ch, (uint16_t*)summ, codes, scale, d.pairs, d.Hkv, d.D, d.row, d.bs, d.r,
+              N1, NB1, d.Ns, d.NBs, d.N / d.bs};
+  e = launch_build(a, st);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "build_summaries launch (appended blocks)");
 }
 
 int tls_select_blocks(const tls_shape_t* shape, const void* q, const void* summ, int32_t* block_idx,
@@ -161,7 +190,7 @@ int tls_select_blocks(const tls_shape_t* shape, const void* q, const void* summ,
     S = (float*)ws;
   }
   hipStream_t st = (hipStream_t)stream;
-  BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB};
+  BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB, d.NBs};
   const hipEvent_t pb = g_prof_start[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
   const hipEvent_t pe = g_prof_end[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
   if (pb) (void)hipEventRecord(pb, st);
@@ -186,7 +215,7 @@ int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* la
   if (!ws || ws_len < ws_bytes(d, TLS_WS_TOKENS))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_TOKENS));
   TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
-                    d.bs, d.r, d.kb, d.kt, d.N};
+                    d.bs, d.r, d.kb, d.kt, d.N, d.Ns};
   hipError_t e = launch_select_tokens(a, (float*)ws, (hipStream_t)stream);
   return e == hipSuccess ? TLS_OK : hip_error(e, "select_tokens launch");
 }
@@ -212,7 +241,7 @@ int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_ca
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
   DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, ws, out, lse_opt,
                d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
-               slot_map ? slots_per_pair : 0, d.N, d.NB, d.sm,
+               slot_map ? slots_per_pair : 0, d.N, d.NB, d.Ns, d.sm,
                g_prof_start[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed),
                g_prof_end[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed)};
   hipError_t e = launch_decode(a, pl, (hipStream_t)stream);

@@ -15,7 +15,8 @@ constexpr int64_t kMaxCandidates = 16384;
 
 struct Derived {
   int B, Hq, Hkv, G, D, DV, row, v_off, bs, r, kb, kt, pairs;
-  int64_t N, NB;
+  int64_t N, NB;    // tokens and blocks of every sequence
+  int64_t Ns, NBs;  // allocated tokens and blocks per sequence (the strides)
   float sm;
 };
 

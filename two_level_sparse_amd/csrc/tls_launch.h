@@ -13,16 +13,21 @@ struct BuildArgs {
   uint8_t* codes;
   float* scale;
   int pairs, Hkv, D, row, bs, r;
-  int64_t N, NB;
+  int64_t N, NB;     // tokens and blocks of every sequence
+  int64_t Ns, NBs;   // per-sequence strides (allocated tokens, blocks)
+  int64_t j_first;   // first block to build (blocks j_first .. NB-1)
 };
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
+// Copies n_new rows per pair from src [pairs, n_new, row] to positions N0.. of kv (stride Ns tokens).
+hipError_t launch_append_rows(const uint16_t* src, uint16_t* kv, int pairs, int n_new, int row, int64_t N0,
+                              int64_t Ns, hipStream_t st);
 
 struct BlockScoreArgs {
   const uint16_t* q;
   const uint16_t* summ;
   float* S;  // [pairs, NB]
   int pairs, Hq, Hkv, G, D;
-  int64_t NB;
+  int64_t NB, NBs;  // blocks, and the summaries' per-sequence stride in blocks
 };
 hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st);
 
@@ -35,7 +40,7 @@ struct TokenSelectArgs {
   const int32_t* block_idx;  // [pairs, kb]
   int32_t* token_idx;        // [pairs, kt], -1 padded
   int pairs, Hq, Hkv, G, D, bs, r, kb, kt;
-  int64_t N;
+  int64_t N, Ns;  // tokens, and the label cache's per-sequence stride
 };
 hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A /* [pairs, kb*bs] scores */, hipStream_t st);
 
@@ -51,7 +56,7 @@ struct DecodeArgs {
   float* out;
   float* lse;               // may be NULL
   int pairs, B, Hq, Hkv, G, D, DV, row, v_off, bs, kt, slots;
-  int64_t N, NB;
+  int64_t N, NB, Ns;  // Ns: per-sequence stride of kv in tokens (no slot map)
   float sm_scale;
   hipEvent_t prof_start, prof_end;  // recorded around the attention kernel when not null
 };

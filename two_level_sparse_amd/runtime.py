@@ -11,8 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (TLS_WS_BLOCKS, TLS_WS_DECODE, TLS_WS_TOKENS, shape_of, tls_build_summaries, tls_select_blocks,
-               tls_select_tokens, tls_sparse_decode, tls_workspace_size)
+from . import (TLS_WS_BLOCKS, TLS_WS_DECODE, TLS_WS_TOKENS, shape_of, tls_append_kv, tls_build_summaries,
+               tls_select_blocks, tls_select_tokens, tls_sparse_decode, tls_workspace_size)
 
 
 def _dev(x, dtype=None, device="cuda"):
@@ -42,6 +42,41 @@ class Cache:
 
     def build(self, stream=None):
         tls_build_summaries(self.shape, self.kv, self.label_ch, self.summ, self.codes, self.scale, stream)
+        return self
+
+
+class GrowingCache:
+    """A KV cache allocated for `capacity` tokens per sequence that grows at
+    decode time: `append(rows)` writes new rows after the current length and
+    updates the summaries and label cache of the blocks they fall in
+    (tls_append_kv). Every per-sequence buffer is strided by `capacity`;
+    `shape` describes the current length."""
+
+    def __init__(self, s, kv, label_ch, capacity, device="cuda"):
+        assert capacity >= s.N
+        self.s, self.capacity, self.n = s, int(capacity), s.N
+        nb_cap = (self.capacity + s.bs - 1) // s.bs
+        self.kv = torch.zeros((s.B, s.Hkv, self.capacity, s.row), dtype=torch.bfloat16, device=device)
+        self.kv[:, :, : s.N] = kv if isinstance(kv, torch.Tensor) else bf16(kv, device)
+        self.label_ch = torch.as_tensor(np.ascontiguousarray(label_ch, dtype=np.int32)).to(device)
+        self.summ = torch.zeros((s.B, s.Hkv, nb_cap, 2, s.D), dtype=torch.bfloat16, device=device)
+        self.codes = torch.zeros((s.B, s.Hkv, self.capacity, s.r // 2), dtype=torch.uint8, device=device)
+        self.scale = torch.zeros((s.B, s.Hkv, self.capacity), dtype=torch.float32, device=device)
+
+    @property
+    def shape(self):
+        return shape_of(self.s.with_(N=self.n), self.capacity)
+
+    def build(self, stream=None):
+        tls_build_summaries(self.shape, self.kv, self.label_ch, self.summ, self.codes, self.scale, stream)
+        return self
+
+    def append(self, rows, stream=None):
+        """rows: [B, Hkv, n, row] bf16 device tensor (contiguous)."""
+        n = rows.shape[2]
+        tls_append_kv(self.shape, rows.contiguous(), n, self.kv, self.label_ch, self.summ, self.codes, self.scale,
+                      stream)
+        self.n += n
         return self
 
 
@@ -79,25 +114,29 @@ class Decoder:
         # (a zero TOKENS size: more candidates than the token stage takes; select_tokens then fails)
         self.ws = {w: torch.zeros(max(n, 256), dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
 
-    def select_blocks(self, q, cache, stream=None, keep_scores=False, block_idx=None):
+    # `shape`: the calls' shape when it differs from the decoder's (a growing
+    # cache: current length and capacity; Kb' and Kt' must not change)
+    def select_blocks(self, q, cache, stream=None, keep_scores=False, block_idx=None, shape=None):
         bi = self.block_idx if block_idx is None else block_idx
-        tls_select_blocks(self.shape, q, cache.summ, bi, self.block_score if keep_scores else None,
+        tls_select_blocks(shape or self.shape, q, cache.summ, bi, self.block_score if keep_scores else None,
                           self.ws[TLS_WS_BLOCKS], self.ws_sizes[TLS_WS_BLOCKS], stream)
 
-    def select_tokens(self, q, cache, stream=None, block_idx=None):
+    def select_tokens(self, q, cache, stream=None, block_idx=None, shape=None):
         bi = self.block_idx if block_idx is None else block_idx
-        tls_select_tokens(self.shape, q, cache.label_ch, cache.codes, cache.scale, bi, self.token_idx,
+        tls_select_tokens(shape or self.shape, q, cache.label_ch, cache.codes, cache.scale, bi, self.token_idx,
                           self.ws[TLS_WS_TOKENS], self.ws_sizes[TLS_WS_TOKENS], stream)
 
-    def decode(self, q, kv_cache, stream=None, slot_map=None, slots=0, token_idx=None):
+    def decode(self, q, kv_cache, stream=None, slot_map=None, slots=0, token_idx=None, shape=None):
         ti = self.token_idx if token_idx is None else token_idx
-        tls_sparse_decode(self.shape, q, kv_cache, slot_map, slots, ti, self.out, self.lse,
+        tls_sparse_decode(shape or self.shape, q, kv_cache, slot_map, slots, ti, self.out, self.lse,
                           self.ws[TLS_WS_DECODE], self.ws_sizes[TLS_WS_DECODE], stream)
 
     def step(self, q, cache, stream=None, keep_scores=False):
-        self.select_blocks(q, cache, stream, keep_scores)
-        self.select_tokens(q, cache, stream)
-        self.decode(q, cache.kv, stream)
+        """One decode step over `cache` (a Cache, CacheView or GrowingCache)."""
+        sh = cache.shape if isinstance(cache, GrowingCache) else None
+        self.select_blocks(q, cache, stream, keep_scores, shape=sh)
+        self.select_tokens(q, cache, stream, shape=sh)
+        self.decode(q, cache.kv, stream, shape=sh)
         return self.out
 
 
