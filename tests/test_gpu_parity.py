@@ -60,6 +60,9 @@ SMALL = {
     "k_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1024, bs=64, Kb=1, Kt=1),
     "many_splits": W.small_shape(B=1, Hq=8, Hkv=1, N=65536, bs=64, Kb=200, Kt=9000),
     "bs1": W.small_shape(B=1, Hq=4, Hkv=1, N=300, bs=1, D=64, DV=64, r=8, Kb=40, Kt=17),
+    # degenerate lengths: one cached token; fewer tokens than one block
+    "n_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1, bs=64, Kb=4, Kt=16),
+    "n_below_block": W.small_shape(B=1, Hq=8, Hkv=1, N=37, bs=64, Kb=3, Kt=20),
     # head groups above 48 take the LDS-staged block scorer: 4 tiles of 16
     # blocks per workgroup, ragged tile counts and head tiles past G
     "g64_lds": W.small_shape(B=1, Hq=128, Hkv=2, N=3000, bs=32, Kb=12, Kt=200),
