@@ -94,7 +94,22 @@ __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
   for (int i = tid; i < (NB + 31) / 32; i += 256) inm[i] = 0u;
   for (int i = tid; i < kDeltaMaxCap / 32; i += 256) freeb[i] = 0u;
   if (tid == 0) nfree_sh = bad_sh = 0u;
-  for (int i = tid; i < NB; i += 256) map_next[i] = map_cur[i];
+  {
+    // the map of step t+1 starts as the map of step t: all loads of a round
+    // in flight before its stores (the two maps are distinct buffers)
+    const int32_t* __restrict__ src = map_cur;
+    int32_t* __restrict__ dst = map_next;
+    constexpr int R = 16;
+    int base = 0;
+    for (; base + 256 * R <= NB; base += 256 * R) {  // whole rounds, no per-element branches
+      int32_t v[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) v[u] = src[base + u * 256 + tid];
+#pragma unroll
+      for (int u = 0; u < R; ++u) dst[base + u * 256 + tid] = v[u];
+    }
+    for (int i = base + tid; i < NB; i += 256) dst[i] = src[i];
+  }
   __syncthreads();
   for (int i = tid; i < kb; i += 256) {
     const int b = M[i], bp = prev[i];
