@@ -129,6 +129,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(s, q, kv, lab, budget_s=15.0):
     """The fp64 oracle (O3..O9 of one step; summaries/label cache prebuilt,
     untimed) on a bounded sample of pairs, scaled to queries/sec of a full step."""
@@ -147,7 +157,7 @@ def cpu_baseline(s, q, kv, lab, budget_s=15.0):
             break
     per_sample = el / reps
     step_s = per_sample * s.pairs / n
-    return {"value": s.B / step_s, "unit": "queries/s", "cores": nth, "kind": "oracle",
+    return {"value": s.B / step_s, "unit": "queries/s", "cores": nth, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} of {s.pairs} (batch, kv-head) pairs of one step, {reps} repetitions, "
                       f"{per_sample * 1e3:.1f} ms each, scaled by {s.pairs}/{n}; summaries and label cache "
                       f"prebuilt (untimed); fp64 C oracle with OpenMP over pairs"}
@@ -167,8 +177,11 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy before timing (counter calibration for profiles)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--copy-mode", default=None, choices=["device", "gather", "memcpy"],
-                    help="offloaded workload: where the transfer is planned and how blocks move (default: library's)")
+    ap.add_argument("--copy-mode", default=None, choices=["device", "gather", "memcpy", "full"],
+                    help="offloaded workload: where the transfer is planned and how blocks move (default: library's; "
+                         "full = every selected block every step, the baseline without reuse)")
+    ap.add_argument("--no-stagger", action="store_true",
+                    help="offloaded workload: the baseline without staggering (select, transfer, attend in order)")
     ap.add_argument("--mode", default="tls", choices=["tls", "quest", "dense"],
                     help="tls: the two-level step; quest: block stage only (every token of the kept blocks); "
                          "dense: attention over every cached token, no selection (baselines at the same shape)")
@@ -359,7 +372,7 @@ def cpu_baseline_staggered(s, qs, kv, lab, budget_s):
         if k >= qs.shape[0] or el * 2 > budget_s:
             break
         k = min(qs.shape[0], 2 * k)
-    return {"value": s.B * k / el, "unit": "queries/s", "cores": nth, "kind": "oracle",
+    return {"value": s.B * k / el, "unit": "queries/s", "cores": nth, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"the first {k} of {qs.shape[0]} staggered steps, all {s.pairs} pairs, {el:.2f} s; summaries, "
                       f"label cache and the prologue selection prebuilt (untimed); fp64 C oracle with OpenMP over "
                       f"pairs"}
@@ -392,12 +405,12 @@ def bench_offload(args, s):
     qd = [bf16(qs[t]) for t in range(steps)]
     block_bytes = s.bs * s.row * 2
     kb = min(s.Kb, s.NB)
-    modes = {"gather": 0, "memcpy": 1, "device": 2}
+    modes = {"gather": 0, "memcpy": 1, "device": 2, "full": 3}
     mode = modes[args.copy_mode] if args.copy_mode else None
     stream = torch.cuda.current_stream()
 
     def run(n, graph):
-        sd = StaggeredDecoder(s, cache, host, qd[0], copy_mode=mode)
+        sd = StaggeredDecoder(s, cache, host, qd[0], copy_mode=mode, stagger=not args.no_stagger)
         g = sd.capture(qd[:n]) if graph and sd.device_planned else None
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -432,7 +445,7 @@ def bench_offload(args, s):
     # the drift steps launched one call at a time behind a spin kernel (the
     # host queues them all first, so the GPU runs them back to back).
     log("[bench] host-copy kernel events")
-    sd = StaggeredDecoder(s, cache, host, qd[0], copy_mode=mode)
+    sd = StaggeredDecoder(s, cache, host, qd[0], copy_mode=mode, stagger=not args.no_stagger)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda._sleep(int(6e7))
@@ -467,7 +480,7 @@ def bench_offload(args, s):
         cus = float(np.mean(copy_ms)) * 1e3
         ach = h2d_step / cus / 1e3
         roof = {"bound": "pcie", "kernel": "k_copy_listed (host->device block copy of tls_prefetch_delta)"
-                if used == "device" else "k_gather_blocks (host->device block copy of tls_prefetch_delta)",
+                if used in ("device", "full") else "k_gather_blocks (host->device block copy of tls_prefetch_delta)",
                 "achieved": round(ach, 2), "peak": PCIE5_X16_GBS, "unit": "GB/s", "frac": round(ach / PCIE5_X16_GBS, 4),
                 "traffic": None, "launch_us": round(cus, 2), "bytes_per_launch": int(h2d_step),
                 "measured_link_GBps": round(link_GBps, 2),
@@ -488,11 +501,14 @@ def bench_offload(args, s):
         "data": "synthetic",
         "config": {"workload": f"{s.name}: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim {s.D}, context "
                                f"{s.N}, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, {s.r} INT4 label channels, full KV in "
-                               f"pinned host memory, {steps} staggered steps with query drift 0.1",
+                               f"pinned host memory, {steps} {'in-order' if args.no_stagger else 'staggered'} steps "
+                               f"with query drift 0.1",
                    "batch": s.B, "ctx_len": s.N, "offload": True, "graph": graphed,
                    "repetitions": reps},
         "ms_per_step_each_repetition": [round(x, 5) for x in per],
-        "offload": {"planning": "device" if used == "device" else f"host ({used} copies)",
+        "offload": {"planning": {"device": "device", "full": "device, every selected block (no reuse)"}.get(
+                        used, f"host ({used} copies)"),
+                    "staggered": not args.no_stagger,
                     "blocks_copied_per_step": round(moved / steps, 1),
                     "delta_fraction": round(moved / (steps * s.pairs * kb), 4),
                     "h2d_bytes_per_step": int(h2d_step),
@@ -502,7 +518,7 @@ def bench_offload(args, s):
         "roofline": roof,
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not args.no_stagger and used != "full":
         log("[bench] oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline_staggered(s, qs, kv, lab, args.cpu_budget)
     print(json.dumps(res), flush=True)

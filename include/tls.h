@@ -182,7 +182,7 @@ const int32_t *tls_offload_slot_map(const tls_offload_t *ctx, int32_t step);
 /* Incremental prefetch for step `step` (0, 1, 2, ... in order).
  *   dev_block_idx  M_t [B,Hkv,Kb'] int32 device buffer written by
  *                  tls_select_blocks on `side` (a hipStream_t) before this call.
- * With TLS_COPY_DEVICE the call only enqueues, on `side`, a planning kernel
+ * With TLS_COPY_DEVICE (or TLS_COPY_FULL) the call only enqueues, on `side`, a planning kernel
  * (T_t, evictions, slot assignment, next slot map) and a copy kernel that
  * reads the blocks of T_t from host memory, and returns at once; M_t must stay
  * unchanged until they ran. With the host-planned modes it enqueues a copy of
@@ -191,10 +191,10 @@ const int32_t *tls_offload_slot_map(const tls_offload_t *ctx, int32_t step);
  * and enqueues the block copies and the next slot map on `side`. Either way it
  * records `copies_done` (a hipEvent_t) on `side`; step step+1 must wait for
  * that event before reading the resident cache. n_copied_opt (host, may be
- * NULL) receives |T_t| summed over all pairs, or -1 with TLS_COPY_DEVICE
+ * NULL) receives |T_t| summed over all pairs, or -1 when planned on the GPU
  * (read tls_offload_total_copied instead). The pinned staging buffers of the
  * context are reused by the next call, which first waits for `side`.
- * With TLS_COPY_DEVICE a run of calls may be captured into a HIP graph: the
+ * When planned on the GPU a run of calls may be captured into a HIP graph: the
  * planning kernel counts steps on the device, so the captured launches need
  * no host work; since the slot maps alternate by step parity, replaying the
  * graph repeatedly needs an even number of captured steps. */
@@ -210,23 +210,28 @@ int tls_prefetch_delta(tls_offload_t *ctx, int32_t step, const int32_t *dev_bloc
  *     from host memory and applies the slot-map changes;
  *   TLS_COPY_MEMCPY (default without a device mapping): planned on the host,
  *     one hipMemcpyAsync per block plus a full slot-map upload.
- * All three give the same slots and maps. Returns TLS_ERR_UNSUPPORTED for a
- * mode the context cannot run, TLS_ERR_STATE for a move between device and
- * host planning after step 0 (GATHER <-> MEMCPY may change at any step). */
-enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1, TLS_COPY_DEVICE = 2 };
+ * All three give the same slots and maps.
+ *   TLS_COPY_FULL (a baseline for comparison, not the method): planned on the
+ *     GPU like TLS_COPY_DEVICE but without reuse: every block of M_t is copied
+ *     at every step, into the half of the resident cache that the step
+ *     reading M_{t-1} does not use (T_t = M_t; nothing is evicted).
+ * Returns TLS_ERR_UNSUPPORTED for a mode the context cannot run, TLS_ERR_STATE
+ * for a change to or from a GPU-planned mode after step 0 (GATHER <-> MEMCPY
+ * may change at any step). */
+enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1, TLS_COPY_DEVICE = 2, TLS_COPY_FULL = 3 };
 int tls_offload_set_copy_mode(tls_offload_t *ctx, int mode);
 /* The current mode, or a negative error code for a NULL context. */
 int tls_offload_get_copy_mode(const tls_offload_t *ctx);
 
 /* Host view of the last transfer (for checking): per pair the count |T_t|
  * and the transferred blocks ascending (host arrays [B*Hkv] and [B*Hkv, Kb']).
- * With TLS_COPY_DEVICE the call synchronises the device and returns
+ * With TLS_COPY_DEVICE or TLS_COPY_FULL the call synchronises the device and returns
  * TLS_ERR_STATE if a step could not be planned (M_t held a block number
  * outside [0, NB)); such a step changed no slot and no map entry. */
 int tls_offload_last_delta(const tls_offload_t *ctx, int32_t *counts, int32_t *blocks);
 
 /* Blocks copied since creation, summed over all steps and pairs (host int64).
- * Synchronises the device with TLS_COPY_DEVICE; errors as tls_offload_last_delta. */
+ * Synchronises the device when planned on the GPU; errors as tls_offload_last_delta. */
 int tls_offload_total_copied(const tls_offload_t *ctx, int64_t *total);
 
 void tls_offload_destroy(tls_offload_t *ctx);
@@ -241,7 +246,7 @@ void tls_offload_destroy(tls_offload_t *ctx);
  *   TLS_PROFILE_ATTENTION: the attention kernel of tls_sparse_decode (not
  *     its split merge);
  *   TLS_PROFILE_HOST_COPY: the kernel of tls_prefetch_delta that reads the
- *     blocks of T_t from host memory (TLS_COPY_DEVICE and TLS_COPY_GATHER).
+ *     blocks of T_t from host memory (all modes but TLS_COPY_MEMCPY).
  * NULL, NULL turns it off. Process-wide; set it while no other thread is
  * calling the library. TLS_ERR_INVALID_ARG if exactly one event is NULL or
  * `which` is unknown. */

@@ -23,6 +23,8 @@ def need_gpu():
 
 
 def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
+    """copy_mode 3 (TLS_COPY_FULL, no reuse): the same outputs and selections,
+    while every block of M_t is transferred at every step."""
     from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
     qs = W.drift_queries(s, q0, steps)
     built = oracle.decode(s, q0, kv, lab)
@@ -39,9 +41,13 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
         counts, blocks = sd.last_delta()
         Mt = to_np(sd.selection(t)).reshape(s.pairs, -1)
         np.testing.assert_array_equal(Mt, ref.M[t])
-        np.testing.assert_array_equal(counts, ref.nT[t])
-        for p in range(s.pairs):
-            assert blocks[p, : counts[p]].tolist() == ref.T[t, p, : ref.nT[t, p]].tolist()
+        if copy_mode == 3:
+            np.testing.assert_array_equal(counts, np.full(s.pairs, Mt.shape[1]))
+            np.testing.assert_array_equal(blocks, Mt)
+        else:
+            np.testing.assert_array_equal(counts, ref.nT[t])
+            for p in range(s.pairs):
+                assert blocks[p, : counts[p]].tolist() == ref.T[t, p, : ref.nT[t, p]].tolist()
         stats["moved"] += int(counts.sum())
         # token sets inside M_{t-1}, scored with q_t
         ti = to_np(sd.dec.token_idx).reshape(s.pairs, -1)
@@ -61,7 +67,7 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None):
     return stats
 
 
-@pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0), (False, 2), (True, 2)])
+@pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0), (False, 2), (True, 2), (False, 3)])
 def test_staggered_small(helper, mode):
     s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=21)
     rng = np.random.default_rng(21)
@@ -173,4 +179,47 @@ def test_staggered_graph_replay_matches_the_oracle():
     for p in range(s.pairs):
         assert blocks[p, : counts[p]].tolist() == ref.T[steps - 1, p, : ref.nT[steps - 1, p]].tolist()
     assert sd.total_copied() == int(ref.nT.sum())
+    sd.close()
+
+
+@pytest.mark.parametrize("mode", [2, 0])
+def test_in_order_steps_match_the_synchronous_decode(mode):
+    """The baseline without staggering: step t selects M_t, moves the same delta
+    T_t as the staggered schedule, and attends over tokens of M_t -- the
+    synchronous decode of q_t (oracle) at every step."""
+    from two_level_sparse_amd.runtime import Cache, StaggeredDecoder, bf16
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=24)
+    rng = np.random.default_rng(24)
+    q0 = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    k = rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32)
+    k[..., :4] *= 8
+    kv = W.f32_to_bf16_bits(k)
+    lab = np.tile(np.arange(s.r, dtype=np.int32), (s.Hkv, 1))
+    steps = 10
+    qs = W.drift_queries(s, q0, steps)
+    built = oracle.decode(s, q0, kv, lab)
+    ref = oracle.staggered(s, qs, kv, lab, built)
+    cache = Cache(s, kv, lab).build()
+    host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
+    sd = StaggeredDecoder(s, cache, host, bf16(q0), copy_mode=mode, stagger=False)
+    worst = 0.0
+    for t in range(steps):
+        out = sd.step(bf16(qs[t]))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(sd.selection(t)).reshape(s.pairs, -1), ref.M[t])
+        counts, blocks = sd.last_delta()
+        np.testing.assert_array_equal(counts, ref.nT[t])
+        for p in range(s.pairs):
+            assert blocks[p, : counts[p]].tolist() == ref.T[t, p, : ref.nT[t, p]].tolist()
+        ti = to_np(sd.dec.token_idx).reshape(s.pairs, -1)
+        o = to_np(out).reshape(s.pairs, s.G, s.DV)
+        for p in range(s.pairs):
+            b, h = divmod(p, s.Hkv)
+            qp = qs[t, b, h * s.G:(h + 1) * s.G]
+            _, cand, cs = oracle.select_tokens_pair(s, qp, lab[h], built.codes[p], built.scale[p], ref.M[t][p])
+            band_check(ti[p], cand, cs, s.Kt)
+            ref_o, _ = oracle.attend_pair(s, qp, kv[b, h], ti[p][ti[p] >= 0])
+            worst = max(worst, float(np.max(np.abs(o[p] - ref_o))))
+    print(f"[gpu] in-order steps mode {mode}: max err {worst:.2e}", flush=True)
+    assert worst <= 2e-3
     sd.close()

@@ -28,7 +28,7 @@ TLS_ERR_HIP = -4
 TLS_ERR_STATE = -5
 TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE = 0, 1, 2
 
-TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE = 0, 1, 2
+TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE, TLS_COPY_FULL = 0, 1, 2, 3
 TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",

@@ -72,7 +72,23 @@ hipError_t launch_gather_blocks(const uint16_t* host_kv_dev, uint16_t* dev_cache
 //   M_{t-1} u M_t in order of (last step selected, block number) -- a bitonic
 //   sort of at most kDeltaMaxCap keys in LDS; T_t[i] goes to the i-th free slot
 //   in ascending order; the slot map of step t+1 is map t with these changes.
-// k_copy_listed then moves the listed blocks, one workgroup per block.
+// k_copy_listed then moves the listed blocks.
+
+// The map of step t+1 starts as the map of step t: all loads of a round in
+// flight before its stores (the two maps are distinct buffers).
+__device__ __forceinline__ void copy_map(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int NB, int tid) {
+  constexpr int R = 16;
+  int base = 0;
+  for (; base + 256 * R <= NB; base += 256 * R) {  // whole rounds, no per-element branches
+    int32_t v[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) v[u] = src[base + u * 256 + tid];
+#pragma unroll
+    for (int u = 0; u < R; ++u) dst[base + u * 256 + tid] = v[u];
+  }
+  for (int i = base + tid; i < NB; i += 256) dst[i] = src[i];
+}
+
 __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
   __shared__ uint32_t inm[kDeltaMaxNB / 32];      // M_{t-1} u M_t
   __shared__ uint32_t freeb[kDeltaMaxCap / 32];   // free slots
@@ -94,22 +110,7 @@ __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
   for (int i = tid; i < (NB + 31) / 32; i += 256) inm[i] = 0u;
   for (int i = tid; i < kDeltaMaxCap / 32; i += 256) freeb[i] = 0u;
   if (tid == 0) nfree_sh = bad_sh = 0u;
-  {
-    // the map of step t+1 starts as the map of step t: all loads of a round
-    // in flight before its stores (the two maps are distinct buffers)
-    const int32_t* __restrict__ src = map_cur;
-    int32_t* __restrict__ dst = map_next;
-    constexpr int R = 16;
-    int base = 0;
-    for (; base + 256 * R <= NB; base += 256 * R) {  // whole rounds, no per-element branches
-      int32_t v[R];
-#pragma unroll
-      for (int u = 0; u < R; ++u) v[u] = src[base + u * 256 + tid];
-#pragma unroll
-      for (int u = 0; u < R; ++u) dst[base + u * 256 + tid] = v[u];
-    }
-    for (int i = base + tid; i < NB; i += 256) dst[i] = src[i];
-  }
+  copy_map(map_cur, map_next, NB, tid);
   __syncthreads();
   for (int i = tid; i < kb; i += 256) {
     const int b = M[i], bp = prev[i];
@@ -227,6 +228,49 @@ __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
   }
 }
 
+// Full transfer (TLS_COPY_FULL, the baseline without reuse): every block of
+// M_t is copied, block i into slot h*kb + i of the half h = (t+1)&1 of the
+// resident cache -- the half the step reading M_{t-1} does not use (the
+// prologue's M_{-1} sits in half 0) -- and the map of step t+1 holds exactly
+// M_t.
+__global__ __launch_bounds__(256) void k_full_plan(DeltaArgs a) {
+  __shared__ uint32_t bad_sh;
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const int NB = a.NB, kb = a.kb;
+  const int32_t step = *a.step_ctr;
+  const int h = (step + 1) & 1;
+  const int32_t* M = a.M + (int64_t)p * kb;
+  int32_t* prev = a.prev + (int64_t)p * kb;
+  int32_t* map_next = a.map_next + (int64_t)p * NB;
+  if (tid == 0) bad_sh = 0u;
+  copy_map(a.map_cur + (int64_t)p * NB, map_next, NB, tid);
+  __syncthreads();
+  for (int i = tid; i < kb; i += 256)
+    if ((unsigned)M[i] >= (unsigned)NB) bad_sh = 1u;
+  __syncthreads();
+  if (bad_sh) {  // M_t holds a block number outside [0, NB): the map stays that of M_{t-1}
+    if (tid == 0) {
+      *a.err = 2;
+      a.counts[p] = 0;
+    }
+    return;
+  }
+  for (int i = tid; i < kb; i += 256) map_next[prev[i]] = -1;
+  __syncthreads();
+  for (int i = tid; i < kb; i += 256) {
+    const int blk = M[i], sl = h * kb + i;
+    map_next[blk] = sl;
+    a.items[(int64_t)p * kb + i] =
+        CopyItem{((int64_t)p * a.N + (int64_t)blk * a.bs) * a.row, ((int64_t)p * a.cap + sl) * a.block_elems};
+    a.tblocks[(int64_t)p * kb + i] = blk;
+    prev[i] = blk;
+  }
+  if (tid == 0) {
+    a.counts[p] = kb;
+    atomicAdd(a.total, (unsigned long long)kb);
+  }
+}
+
 // The listed blocks of all pairs, taken in pair order as one list, by a small
 // persistent grid: workgroup w moves list entries w, w+G, w+2G, ... . Reads of
 // host memory wait on the host link for microseconds; a few workgroups already
@@ -276,7 +320,10 @@ __global__ __launch_bounds__(256) void k_copy_listed(const uint16_t* __restrict_
 
 hipError_t launch_device_delta(const DeltaArgs& a, const uint16_t* host_kv_dev, uint16_t* dev_cache, hipStream_t st,
                                hipEvent_t prof_start, hipEvent_t prof_end) {
-  hipLaunchKernelGGL(k_delta_plan, dim3(a.pairs), dim3(256), 0, st, a);
+  if (a.full)
+    hipLaunchKernelGGL(k_full_plan, dim3(a.pairs), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_delta_plan, dim3(a.pairs), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prof_start) (void)hipEventRecord(prof_start, st);

@@ -74,6 +74,9 @@ struct tls_offload {
   tls::DeltaArgs da{};
 };
 
+// TLS_COPY_DEVICE and TLS_COPY_FULL plan on the GPU; the others on the host.
+static bool device_planned(int mode) { return mode == TLS_COPY_DEVICE || mode == TLS_COPY_FULL; }
+
 static void free_ctx(tls_offload* c) {
   if (!c) return;
   if (c->dev_state) (void)hipFree(c->dev_state);
@@ -264,8 +267,9 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   const Derived& d = c->d;
   hipStream_t st = (hipStream_t)side;
   hipError_t e;
-  if (c->copy_mode == TLS_COPY_DEVICE) {
+  if (device_planned(c->copy_mode)) {
     DeltaArgs a = c->da;
+    a.full = c->copy_mode == TLS_COPY_FULL;
     a.M = dev_block_idx;
     a.map_cur = c->dev_map[step & 1];
     a.map_next = c->dev_map[(step + 1) & 1];
@@ -393,16 +397,17 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
 int tls_offload_set_copy_mode(tls_offload_t* c, int mode) {
   clear_error();
   if (!c) return set_error(TLS_ERR_INVALID_ARG, "NULL context");
-  if (mode != TLS_COPY_GATHER && mode != TLS_COPY_MEMCPY && mode != TLS_COPY_DEVICE)
+  if (mode != TLS_COPY_GATHER && mode != TLS_COPY_MEMCPY && mode != TLS_COPY_DEVICE && mode != TLS_COPY_FULL)
     return set_error(TLS_ERR_INVALID_ARG, "unknown copy mode");
   if (mode == TLS_COPY_GATHER && !c->host_kv_dev)
     return set_error(TLS_ERR_UNSUPPORTED, "host cache has no device mapping; only TLS_COPY_MEMCPY is available");
-  if (mode == TLS_COPY_DEVICE && !c->dev_state)
+  if (device_planned(mode) && !c->dev_state)
     return set_error(TLS_ERR_UNSUPPORTED,
                      "device planning needs a device-mapped host cache, 2*Kb' <= %d slots and NB <= %d blocks",
                      kDeltaMaxCap, kDeltaMaxNB);
-  if ((mode == TLS_COPY_DEVICE) != (c->copy_mode == TLS_COPY_DEVICE) && c->next_step != 0)
-    return set_error(TLS_ERR_STATE, "planning can move between host and device only before step 0");
+  if (mode != c->copy_mode && (device_planned(mode) || device_planned(c->copy_mode)) && c->next_step != 0)
+    return set_error(TLS_ERR_STATE, "planning can move between host and device, or to or from full transfers, "
+                                    "only before step 0");
   c->copy_mode = mode;
   return TLS_OK;
 }
@@ -415,7 +420,7 @@ int tls_offload_get_copy_mode(const tls_offload_t* c) {
 int tls_offload_last_delta(const tls_offload_t* c, int32_t* counts, int32_t* blocks) {
   clear_error();
   if (!c || !counts || !blocks) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
-  if (c->copy_mode == TLS_COPY_DEVICE) {
+  if (device_planned(c->copy_mode)) {
     int rc = device_state_check(c);
     if (rc) return rc;
     hipError_t e = hipMemcpy(counts, c->da.counts, (size_t)c->d.pairs * 4, hipMemcpyDeviceToHost);
@@ -431,7 +436,7 @@ int tls_offload_last_delta(const tls_offload_t* c, int32_t* counts, int32_t* blo
 int tls_offload_total_copied(const tls_offload_t* c, int64_t* total) {
   clear_error();
   if (!c || !total) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
-  if (c->copy_mode == TLS_COPY_DEVICE) {
+  if (device_planned(c->copy_mode)) {
     int rc = device_state_check(c);
     if (rc) return rc;
     unsigned long long t = 0;

@@ -97,6 +97,7 @@ struct DeltaArgs {
   int32_t* step_ctr;          // steps planned so far (the LRU clock), advanced by the copy kernel
   int pairs, NB, kb, cap, bs, row;
   int copy_wgs;               // workgroups of the copy kernel
+  int full;                   // 1: transfer every block of M_t (no reuse)
   int64_t N, block_elems;
 };
 // prof_start/prof_end (may be null) are recorded around the copy kernel.

@@ -221,8 +221,12 @@ class StaggeredDecoder:
     read); `host_kv` is the full cache [B,Hkv,N,row] bf16 in pinned memory.
     """
 
-    def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None):
+    def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None, stagger=True):
         self.s = s
+        # stagger=False: the baseline without staggering -- each step selects
+        # M_t, moves T_t and then attends over tokens of M_t, in order on the
+        # caller's stream (the transfers are the same; their time is not hidden)
+        self.stagger = stagger
         self.cache = cache
         self.host_kv = host_kv
         self.dec = Decoder(s, device)
@@ -248,11 +252,11 @@ class StaggeredDecoder:
         torch.cuda.synchronize()
         init = self.mbuf[2].cpu().numpy().astype(np.int32)
         self.ctx = tls_offload_create_ctx(self.dec.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
-        from . import TLS_COPY_DEVICE, tls_offload_get_copy_mode, tls_offload_set_copy_mode
+        from . import TLS_COPY_DEVICE, TLS_COPY_FULL, tls_offload_get_copy_mode, tls_offload_set_copy_mode
         if copy_mode is not None:
             tls_offload_set_copy_mode(self.ctx, copy_mode)
         self.copy_mode = tls_offload_get_copy_mode(self.ctx)
-        self.device_planned = self.copy_mode == TLS_COPY_DEVICE
+        self.device_planned = self.copy_mode in (TLS_COPY_DEVICE, TLS_COPY_FULL)
         self.t = 0
         self.copied = []
 
@@ -269,6 +273,8 @@ class StaggeredDecoder:
         device planned it; see total_copied)."""
         import threading
         from . import tls_offload_slot_map, tls_prefetch_delta
+        if not self.stagger:
+            return self._step_in_order(q_t)
         if helper is None:
             helper = not self.device_planned
         t = self.t
@@ -300,18 +306,31 @@ class StaggeredDecoder:
         self.t += 1
         return self.dec.out
 
+    def _step_in_order(self, q_t):
+        from . import tls_offload_slot_map, tls_prefetch_delta
+        t = self.t
+        main = torch.cuda.current_stream()
+        mt = self.selection(t)
+        self.dec.select_blocks(q_t, self.cache, block_idx=mt)
+        self.copied.append(tls_prefetch_delta(self.ctx, t, mt, main, self.events[t % 2]))
+        self.dec.select_tokens(q_t, self.cache, block_idx=mt)
+        # the map written by this step's transfer (that of step t+1) holds M_t
+        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t + 1), slots=self.cap)
+        self.t += 1
+        return self.dec.out
+
     def capture(self, queries, outputs=None):
         """Record the next len(queries) steps into a HIP graph and return it
         (a torch.cuda.CUDAGraph; nothing runs until it is replayed).
 
-        Needs device planning (TLS_COPY_DEVICE): the library's planning kernel
+        Needs planning on the GPU (TLS_COPY_DEVICE or TLS_COPY_FULL): the planning kernel
         keeps its own step count, so the captured launches need no host work.
         `outputs`, if given, is one [B, Hq, DV] fp32 tensor per step that the
         graph fills. The graph holds the buffers of those steps (selections
         rotate over three buffers, slot maps alternate by step parity), so
         replay it once, or repeatedly only when len(queries) is a multiple of 6."""
         if not self.device_planned:
-            raise RuntimeError("graph capture needs device planning (TLS_COPY_DEVICE)")
+            raise RuntimeError("graph capture needs planning on the GPU (TLS_COPY_DEVICE or TLS_COPY_FULL)")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             main = torch.cuda.current_stream()
@@ -319,8 +338,9 @@ class StaggeredDecoder:
                 out = self.step(q, helper=False)
                 if outputs is not None:
                     outputs[i].copy_(out)
-            main.wait_stream(self.stage)
-            main.wait_stream(self.side)
+            if self.stagger:
+                main.wait_stream(self.stage)
+                main.wait_stream(self.side)
         return g
 
     def last_delta(self):
