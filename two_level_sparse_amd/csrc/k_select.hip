@@ -586,40 +586,41 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_blocks(const float* __res
 // so the order of max and scale is immaterial). A unit's loads go out in two
 // dependent batches (block numbers, then codes and scales) before its MFMAs;
 // the label-channel -> query chain runs beside them.
-constexpr int kUnitTiles = 16;               // tiles of 16 candidates per unit
-constexpr int kUnitGroups = kUnitTiles / 4;  // groups of four tiles; one score per lane each
+// A unit is UT tiles of 16 candidates (one wave); UT/4 groups of four tiles,
+// one score per lane each.
 
+template <int UT>
 struct UnitLoads {
-  uint32_t cw[kUnitTiles];  // lane (n, kq): code bytes 4kq..4kq+3 of candidate c0 + 16u + n
-  float tsc[kUnitGroups];   // scale of candidate c0 + 64j + lane
-  bool ok[kUnitGroups];     // that candidate exists
+  uint32_t cw[UT];  // lane (n, kq): code bytes 4kq..4kq+3 of candidate c0 + 16u + n
+  float tsc[UT / 4];   // scale of candidate c0 + 64j + lane
+  bool ok[UT / 4];     // that candidate exists
 };
 
 // Issues the loads of the unit starting at candidate c0. `bidx` is the pair's
 // block list (global or LDS).
-template <int RB>
-__device__ __forceinline__ void unit_loads(UnitLoads& L, const int32_t* bidx, const uint8_t* cbase,
+template <int RB, int UT>
+__device__ __forceinline__ void unit_loads(UnitLoads<UT>& L, const int32_t* bidx, const uint8_t* cbase,
                                            const float* sbase, int c0, int ncand, int64_t N, int bs, int bsh,
                                            int rb) {
   const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
-  int cq[kUnitTiles], sq[kUnitGroups], cid[kUnitTiles], sid[kUnitGroups];
+  int cq[UT], sq[UT / 4], cid[UT], sid[UT / 4];
   if (bsh >= 0) {
 #pragma unroll
-    for (int u = 0; u < kUnitTiles; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) >> bsh;
+    for (int u = 0; u < UT; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) >> bsh;
 #pragma unroll
-    for (int j = 0; j < kUnitGroups; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) >> bsh;
+    for (int j = 0; j < UT / 4; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) >> bsh;
   } else {
 #pragma unroll
-    for (int u = 0; u < kUnitTiles; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) / bs;
+    for (int u = 0; u < UT; ++u) cq[u] = min(c0 + u * 16 + n, ncand - 1) / bs;
 #pragma unroll
-    for (int j = 0; j < kUnitGroups; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) / bs;
+    for (int j = 0; j < UT / 4; ++j) sq[j] = min(c0 + 64 * j + lane, ncand - 1) / bs;
   }
 #pragma unroll
-  for (int u = 0; u < kUnitTiles; ++u) cid[u] = bidx[cq[u]];
+  for (int u = 0; u < UT; ++u) cid[u] = bidx[cq[u]];
 #pragma unroll
-  for (int j = 0; j < kUnitGroups; ++j) sid[j] = bidx[sq[j]];
+  for (int j = 0; j < UT / 4; ++j) sid[j] = bidx[sq[j]];
 #pragma unroll
-  for (int u = 0; u < kUnitTiles; ++u) {
+  for (int u = 0; u < UT; ++u) {
     const int c = c0 + u * 16 + n;
     const int64_t t = (int64_t)cid[u] * bs + (c - cq[u] * bs);
     const int64_t ts = (c < ncand && t >= 0 && t < N) ? t : 0;  // masked candidates read token 0
@@ -634,7 +635,7 @@ __device__ __forceinline__ void unit_loads(UnitLoads& L, const int32_t* bidx, co
     }
   }
 #pragma unroll
-  for (int j = 0; j < kUnitGroups; ++j) {
+  for (int j = 0; j < UT / 4; ++j) {
     const int c = c0 + 64 * j + lane;
     const int64_t t = (int64_t)sid[j] * bs + (c - sq[j] * bs);
     L.ok[j] = c < ncand && t >= 0 && t < N;
@@ -665,12 +666,12 @@ __device__ __forceinline__ void label_q(u32x4 (&qa)[MT], const int (&ch)[8], con
 
 // Scores of the unit: val[j] for candidate c0 + 64j + lane (0 if it does not
 // exist).
-template <int MT, int RB>
-__device__ __forceinline__ void unit_scores(float (&val)[kUnitGroups], const UnitLoads& L, const u32x4 (&qa)[MT],
+template <int MT, int RB, int UT>
+__device__ __forceinline__ void unit_scores(float (&val)[UT / 4], const UnitLoads<UT>& L, const u32x4 (&qa)[MT],
                                             int G, int rb) {
   const int lane = threadIdx.x & 63, kq = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < kUnitGroups; ++j) {
+  for (int j = 0; j < UT / 4; ++j) {
     // x[jj]: max over the heads this lane holds (rows 4kq .. 4kq+3 of every
     // head tile) for candidate n of tile 4j + jj.
     float x[4];
@@ -715,9 +716,10 @@ __device__ __forceinline__ void unit_scores(float (&val)[kUnitGroups], const Uni
   }
 }
 
-// Token scores of 1024 candidates per workgroup (one unit per wave), spread
-// over the chip; the scores go to A[pair, candidate] for k_topk_tokens.
-template <int MT, int RB>
+// Token scores of 4 units per workgroup (one unit of UT*16 candidates per
+// wave), spread over the chip; the scores go to A[pair, candidate] for
+// k_topk_tokens.
+template <int MT, int RB, int UT>
 __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
                                                       const int32_t* __restrict__ label_ch,
                                                       const uint8_t* __restrict__ codes,
@@ -733,18 +735,18 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
   int ch[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
-  const int c0 = blockIdx.x * (4 * kUnitTiles * 16) + wave * (kUnitTiles * 16);
-  UnitLoads L;
-  unit_loads<RB>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N,
+  const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  UnitLoads<UT> L;
+  unit_loads<RB, UT>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N,
                  bs, bsh, rb);
   u32x4 qa[MT];
   label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
-  float val[kUnitGroups];
-  unit_scores<MT, RB>(val, L, qa, G, rb);
+  float val[UT / 4];
+  unit_scores<MT, RB, UT>(val, L, qa, G, rb);
   // bounded buffer stores: the hardware drops candidates >= ncand
   const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
-  for (int j = 0; j < kUnitGroups; ++j)
+  for (int j = 0; j < UT / 4; ++j)
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
 }
 
@@ -800,12 +802,24 @@ hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* o
 }
 
 
+template <int MT, int RB, int UT>
+static void go_score_tokens_ut(const TokenSelectArgs& a, float* A, hipStream_t st) {
+  const int ncand = a.kb * a.bs;
+  dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
+  hipLaunchKernelGGL((k_score_tokens<MT, RB, UT>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale,
+                     a.block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, a.kb);
+}
+
+// Units of 16 tiles for few head tiles (the unit's loads are its latency);
+// units of 4 tiles for many (8 MFMAs per tile: 64-candidate units put four
+// times the waves on the chip, 12.7 vs 20.1 us for 128 heads at 4096
+// candidates per pair).
 template <int MT, int RB>
 static void go_score_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
-  const int ncand = a.kb * a.bs;
-  dim3 grid((unsigned)((ncand + 1023) / 1024), (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_score_tokens<MT, RB>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, a.block_idx,
-                     A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, a.kb);
+  if constexpr (MT >= 4)
+    go_score_tokens_ut<MT, RB, 4>(a, A, st);
+  else
+    go_score_tokens_ut<MT, RB, 16>(a, A, st);
 }
 
 template <int MT>
