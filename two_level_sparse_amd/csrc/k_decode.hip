@@ -514,11 +514,14 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
 //     patterns below free of bank conflicts. A masked token loads the row of
 //     the split's first valid token (finite data) and is masked in softmax.
 //   - Wave w owns head tile w&1 (16 heads) and value channels 256*(w>>1) ..
-//     +255. S^T = K q^T on MFMA (A = 16 staged key rows, B = the wave's query
-//     fragments, kept in registers), for both 16-token halves of the tile; the
-//     lane holding head n then has tokens 4kq+i of each half, which is exactly
-//     an A-operand row of P for the next product when the k-slots of P.V are
-//     ordered (half, i) -- so P never leaves the registers.
+//     +255. S^T = K q^T on MFMA (A = 16 staged key rows, B = query fragments
+//     kept in registers), for both 16-token halves of the tile. The two waves
+//     of a head tile split the contraction: each multiplies half of the key
+//     steps, the second half hands its sums to the first through LDS, which
+//     adds them and hands the totals back, so both continue from the same
+//     scores. The lane holding head n then has tokens 4kq+i of each half,
+//     which is exactly an A-operand row of P for the next product when the
+//     k-slots of P.V are ordered (half, i) -- so P never leaves the registers.
 //   - Online softmax per head in the exp2 domain; the running max is made
 //     common across the lanes of a head with cross-row swaps.
 //   - O += P V on MFMA. P is carried as two bf16 terms (hi + lo, each exact
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
 // The partial (m, l, o) of the 32 heads goes to the workspace for k_merge.
 constexpr int kMlaHeads = 32;
 constexpr int kMlaTile = 32;
-constexpr int kMlaMaxTps = 1024;
+constexpr int kMlaMaxTps = 512;
 
 template <bool SMAP>
 __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restrict__ q,
@@ -548,6 +551,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   __shared__ __attribute__((aligned(1024))) uint8_t tA[CP * CHUNK];
   __shared__ __attribute__((aligned(1024))) uint8_t tB[CP * CHUNK];
   __shared__ int32_t rows[kMlaMaxTps];
+  __shared__ f32x4 sx[2][64][2];  // [head tile][lane][token half]: the score exchange
   __shared__ float c_lds[4][16];
   __shared__ int first_ok;
 
@@ -582,13 +586,15 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
       if (r >= 0) atomicMin(&first_ok, k);
     }
   }
-  // query fragments of the wave's 16 heads (rows past G repeat row G-1)
-  u32x4 qf[KS];
+  // query fragments of the wave's 16 heads over its half of the key steps
+  // (rows past G repeat row G-1)
+  constexpr int KH = KS / 2;
+  u32x4 qf[KH];
   {
     const int g = min(hg * kMlaHeads + mt * 16 + n, G - 1);
-    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq;
+    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq + 32 * KH * chh;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = ld16(qr + 32 * k);
+    for (int k = 0; k < KH; ++k) qf[k] = ld16(qr + 32 * k);
   }
   __syncthreads();
   const int fb = first_ok < tps ? rows[first_ok] : -1;
@@ -615,18 +621,18 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   for (int t = 0; t < 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const uint8_t* tb, int j) {
-    // ---- S^T for the two 16-token halves ----
+    // ---- S^T for the two 16-token halves, this wave's half of the key steps ----
     // key fragments in groups of KG steps: all reads of a group are issued
     // before its MFMAs
-    constexpr int KG = 6;
-    static_assert(KS % KG == 0, "key step groups");
+    constexpr int KG = 3;
+    static_assert(KH % KG == 0, "key step groups");
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kg = 0; kg < KS; kg += KG) {
+    for (int kg = 0; kg < KH; kg += KG) {
       u32x4 k0[KG], k1[KG];
 #pragma unroll
       for (int u = 0; u < KG; ++u) {
-        const int cp = 4 * (kg + u) + kq;
+        const int cp = 4 * (KH * chh + kg + u) + kq;
         const uint8_t* cb = tb + cp * CHUNK;
         const int sw = 4 * (cp & 1);
         k0[u] = *reinterpret_cast<const u32x4*>(cb + (n ^ sw) * 16);
@@ -638,6 +644,25 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
         s0 = mfma16x16x32(k0[u], qf[kg + u], s0);
         s1 = mfma16x16x32(k1[u], qf[kg + u], s1);
       }
+    }
+    // the halves meet: the second hands its sums over, the first adds them
+    // and hands the totals back (barriers without a memory fence, which would
+    // also wait for the next tile's loads)
+    if (chh == 1) {
+      sx[mt][lane][0] = s0;
+      sx[mt][lane][1] = s1;
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (chh == 0) {
+      s0 += sx[mt][lane][0];
+      s1 += sx[mt][lane][1];
+      sx[mt][lane][0] = s0;
+      sx[mt][lane][1] = s1;
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (chh == 1) {
+      s0 = sx[mt][lane][0];
+      s1 = sx[mt][lane][1];
     }
     // ---- online softmax: this lane has tokens 4kq+i and 16+4kq+i of head n ----
     float z[8];
