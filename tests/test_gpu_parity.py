@@ -86,6 +86,31 @@ def test_small_shapes(name):
     log(f"[gpu] {name}: {st}")
 
 
+def test_latent_attention_over_every_token():
+    """The latent-attention kernel at its split limit: 32 heads on one 576-dim
+    kv row attend over all 49152 cached tokens (128 splits of 384 tokens, the
+    dense baseline's shape), against the oracle's attention over the same
+    tokens."""
+    from two_level_sparse_amd.runtime import Decoder, bf16
+    s = W.small_shape(B=1, Hq=32, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=49152, bs=64, r=32, Kb=768,
+                      Kt=49152, n_outlier=0, seed=41)
+    log(f"[gpu] latent attention over every token: {s}")
+    rng = np.random.default_rng(41)
+    q = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    kv = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32))
+    dec = Decoder(s)
+    idx = torch.arange(s.N, dtype=torch.int32, device="cuda").view(1, 1, -1).contiguous()
+    dec.decode(bf16(q), bf16(kv), token_idx=idx)
+    torch.cuda.synchronize()
+    out = to_np(dec.out).reshape(s.G, s.DV)
+    lse = to_np(dec.lse).reshape(s.G)
+    o_ref, l_ref = oracle.attend_pair(s, q[0], kv[0, 0], np.arange(s.N))
+    err = float(np.max(np.abs(out - o_ref)))
+    log(f"[gpu] latent attention over every token: max err {err:.2e}")
+    assert err <= 2e-3
+    assert np.max(np.abs(lse - l_ref)) <= 2e-3
+
+
 def test_select_all_equals_dense_attention():
     """Kb >= NB and Kt >= N: the GPU step equals dense attention over the whole cache."""
     s = SMALL["select_all"]

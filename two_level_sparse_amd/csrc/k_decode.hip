@@ -760,21 +760,22 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
 // weights 2^(m_s - M) / L of the tile's heads are formed in LDS while every
 // thread's float4 of o from the first kMergePre splits is already in flight;
 // then a weighted sum.
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 64;      // split limit of the general attention kernels
+constexpr int kMlaMaxSplits = 128;  // of the latent attention (512 tokens per split at most)
 constexpr int kMergePre = 8;
-template <int DV, int HT>
+template <int DV, int HT, int MAXS>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
                                                float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
-  __shared__ float ml_lds[kMaxSplits][HT][2];
-  __shared__ float w_lds[kMaxSplits][HT];
+  __shared__ float ml_lds[MAXS][HT][2];
+  __shared__ float w_lds[MAXS][HT];
   const int ht = blockIdx.y, p = blockIdx.z, tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
   constexpr int PS = DV + kPartHdr;  // floats per head in a partial
   const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * PS;
   // (m, l) of the splits first, then this thread's o loads, all in flight together
-  float2 ml[(kMaxSplits * HT + 255) / 256];
+  float2 ml[(MAXS * HT + 255) / 256];
 #pragma unroll
-  for (int k = 0; k < (kMaxSplits * HT + 255) / 256; ++k) {
+  for (int k = 0; k < (MAXS * HT + 255) / 256; ++k) {
     const int e = tid + 256 * k;
     if (e < nsplit * HT) {
       const int s = e / HT, hh = e % HT;
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, f
 #pragma unroll
   for (int s = 0; s < kMergePre; ++s) ov[s] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(s, nsplit - 1) * HT * PS);
 #pragma unroll
-  for (int k = 0; k < (kMaxSplits * HT + 255) / 256; ++k) {
+  for (int k = 0; k < (MAXS * HT + 255) / 256; ++k) {
     const int e2 = tid + 256 * k;
     if (e2 < nsplit * HT) {
       ml_lds[e2 / HT][e2 % HT][0] = ml[k].x;
@@ -834,7 +835,7 @@ static constexpr int head_tile(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 
 static constexpr bool prefetch_rows(int D) { return D <= 256; }
 
 void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, DecodePlan* plan) {
-  if (D == 576 && DV == 512 && v_is_k_prefix && G > 16 && kt <= kMaxSplits * kMlaMaxTps) {
+  if (D == 576 && DV == 512 && v_is_k_prefix && G > 16 && kt <= kMlaMaxSplits * kMlaMaxTps) {
     // latent attention: 32-head groups, 32-token tiles; about 512 workgroups
     // (two per CU, so that one's loads and barriers overlap the other's
     // MFMAs); the partials cost 2 KB per head and split
@@ -843,10 +844,10 @@ void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, De
     const int want = (512 + units - 1) / units;
     int tps = (kt + want - 1) / want;
     tps = ((tps + kMlaTile - 1) / kMlaTile) * kMlaTile;
-    const int min_tps = ((kt + kMaxSplits - 1) / kMaxSplits + kMlaTile - 1) / kMlaTile * kMlaTile;
+    const int min_tps = ((kt + kMlaMaxSplits - 1) / kMlaMaxSplits + kMlaTile - 1) / kMlaTile * kMlaTile;
     if (tps < min_tps) tps = min_tps;
     if (tps < kMlaTile) tps = kMlaTile;
-    if (tps > kMlaMaxTps) tps = kMlaMaxTps;  // kt <= kMaxSplits * kMlaMaxTps keeps nsplit in range
+    if (tps > kMlaMaxTps) tps = kMlaMaxTps;  // kt <= kMlaMaxSplits * kMlaMaxTps keeps nsplit in range
     plan->mla = 1;
     plan->HT = kMlaHeads;
     plan->nht = nht;
@@ -878,11 +879,11 @@ static void prof_mark(hipEvent_t ev, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev, st);
 }
 
-template <int DV, int HT>
+template <int DV, int HT, int MAXS = kMaxSplits>
 static hipError_t launch_merge(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 mgrid((unsigned)((HT * DV / 4 + 255) / 256), (unsigned)pl.nht, (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv, a.G,
-                     pl.nht, pl.nsplit);
+  hipLaunchKernelGGL((k_merge<DV, HT, MAXS>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv,
+                     a.G, pl.nht, pl.nsplit);
   return hipGetLastError();
 }
 
@@ -945,7 +946,7 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(a.prof_end, st);
-  return launch_merge<512, kMlaHeads>(a, pl, st);
+  return launch_merge<512, kMlaHeads, kMlaMaxSplits>(a, pl, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
