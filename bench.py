@@ -182,8 +182,9 @@ def main():
                          "full = every selected block every step, the baseline without reuse)")
     ap.add_argument("--no-stagger", action="store_true",
                     help="offloaded workload: the baseline without staggering (select, transfer, attend in order)")
-    ap.add_argument("--mode", default="tls", choices=["tls", "quest", "dense"],
+    ap.add_argument("--mode", default="tls", choices=["tls", "quest", "ds", "dense"],
                     help="tls: the two-level step; quest: block stage only (every token of the kept blocks); "
+                         "ds: token stage only (Kt tokens selected over the whole cache); "
                          "dense: attention over every cached token, no selection (baselines at the same shape)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -203,6 +204,8 @@ def main():
     s_data = s  # the cache and queries; s below is the shape the calls run with
     if args.mode == "quest":
         s = s.with_(Kt=min(s.Kb, s.NB) * s.bs)
+    elif args.mode == "ds":
+        s = s.with_(Kb=s.NB)
     elif args.mode == "dense":
         s = s.with_(Kb=s.NB, Kt=s.N)
     ab = algorithmic_bytes(s, dense=args.mode == "dense")

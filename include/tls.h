@@ -96,8 +96,10 @@ typedef struct tls_shape {
 /* Bytes of workspace needed by tls_select_blocks (TLS_WS_BLOCKS),
  * tls_select_tokens (TLS_WS_TOKENS) or tls_sparse_decode (TLS_WS_DECODE) for
  * this shape; 0 if the shape is invalid for that call. tls_select_tokens
- * handles at most 16384 candidates per pair (Kb' * bs); the other calls have
- * no such limit (attention over every token is Kb >= NB, Kt >= N). */
+ * takes any Kt' up to 16384 candidates per pair (Kb' * bs); beyond that (up
+ * to 2^20 candidates, e.g. Kb >= NB: token selection over the whole cache)
+ * it selects in passes over chunks and needs Kt' <= 8192. The other calls
+ * have no such limit (attention over every token is Kb >= NB, Kt >= N). */
 size_t tls_workspace_size(const tls_shape_t *shape, int which);
 
 /* Block summaries and the INT4 label cache (section 2A: the block-level index

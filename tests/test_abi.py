@@ -99,6 +99,21 @@ def test_candidate_limit_applies_to_the_token_stage_only(lib):
     assert rc == T.TLS_ERR_UNSUPPORTED and b"candidate" in lib.tls_last_error()
 
 
+def test_token_selection_over_the_whole_cache_takes_passes(lib):
+    """Kb >= NB with Kt' <= 8192 (DS-style selection over every token): the token
+    stage selects in passes over chunks of 16384 candidates, with room for the
+    scores and two (key, id) lists in its workspace."""
+    s = W.CONFIGS["c3_128k_gqa"].with_(Kb=2048)        # 131072 candidates, Kt = 4096
+    ws = lib.tls_workspace_size(C.byref(T.shape_of(s)), T.TLS_WS_TOKENS)
+    scores = s.pairs * s.N * 4
+    lists = s.pairs * (s.N // 16384) * s.Kt * 4
+    assert ws >= scores + 4 * lists
+    too_many = s.with_(Kt=8193)
+    assert lib.tls_workspace_size(C.byref(T.shape_of(too_many)), T.TLS_WS_TOKENS) == 0
+    within = W.CONFIGS["c3_128k_gqa"].with_(Kb=256, Kt=16384)  # 16384 candidates: one pass, any Kt
+    assert lib.tls_workspace_size(C.byref(T.shape_of(within)), T.TLS_WS_TOKENS) == within.pairs * 16384 * 4
+
+
 def test_append_checks_the_capacity_before_any_device_work(lib):
     """tls_append_kv: the grown length must fit the allocated capacity, which
     must itself hold the current length; offload contexts take no spare capacity."""

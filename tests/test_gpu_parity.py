@@ -60,6 +60,10 @@ SMALL = {
     "k_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1024, bs=64, Kb=1, Kt=1),
     "many_splits": W.small_shape(B=1, Hq=8, Hkv=1, N=65536, bs=64, Kb=200, Kt=9000),
     "bs1": W.small_shape(B=1, Hq=4, Hkv=1, N=300, bs=1, D=64, DV=64, r=8, Kb=40, Kt=17),
+    # token selection over more than 16384 candidates (passes over chunks):
+    # two passes; four passes (70016 -> 40000 -> 24000 -> 16000 -> 8000)
+    "ds_two_pass": W.small_shape(B=1, Hq=8, Hkv=2, N=40000, bs=64, Kb=1000, Kt=3000),
+    "ds_four_pass": W.small_shape(B=1, Hq=4, Hkv=1, N=70000, bs=64, Kb=2000, Kt=8000),
     # degenerate lengths: one cached token; fewer tokens than one block
     "n_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1, bs=64, Kb=4, Kt=16),
     "n_below_block": W.small_shape(B=1, Hq=8, Hkv=1, N=37, bs=64, Kb=3, Kt=20),

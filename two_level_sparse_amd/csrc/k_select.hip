@@ -421,7 +421,7 @@ __device__ __forceinline__ BinPick pick_bin(const uint32_t* hist, uint32_t krem)
 // cleared two passes after its last read), and every wave picks the bin.
 template <int PER, int NT>
 __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER], uint32_t K, int32_t* out,
-                           int out_len, TopkLds<NT>& sh) {
+                           int out_len, TopkLds<NT>& sh, uint32_t* out_key = nullptr) {
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nval = 0u;
@@ -549,11 +549,17 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
       ++eq_before;
     }
     if (take) {
-      if (pos < kk) out[pos] = id[e];  // never more than kk entries
+      if (pos < kk) {  // never more than kk entries
+        out[pos] = id[e];
+        if (out_key) out_key[pos] = key[e];
+      }
       ++pos;
     }
   }
-  for (int i = (int)kk + tid; i < out_len; i += NT) out[i] = -1;
+  for (int i = (int)kk + tid; i < out_len; i += NT) {
+    out[i] = -1;
+    if (out_key) out_key[i] = 0u;  // key 0: no element
+  }
 }
 
 // Top-Kb of the block scores of one pair per workgroup.
@@ -785,6 +791,72 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(const float* __restrict__ A,
   block_topk<PER, NT>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh);
 }
 
+// More candidates than one workgroup holds (16384): an exact top-k in passes.
+// Pass 1 keeps the top-Kt' of every chunk of kTopkChunk candidates, as (key,
+// token) lists in candidate order; each later pass does the same over chunks
+// of the concatenated lists, until one chunk remains, whose selection is the
+// result. A chunk's selection is in element order and chunks follow each
+// other, so the lists stay in token order and the lower-index tie rule holds
+// across passes. With Kt' <= kTopkChunk / 2 every pass at least halves the list.
+constexpr int kTopkChunk = 16384;
+
+template <int PER, int NT>
+__global__ __launch_bounds__(NT) void k_topk_tokens_chunk(const float* __restrict__ A,
+                                                          const int32_t* __restrict__ block_idx,
+                                                          uint32_t* __restrict__ okey, int32_t* __restrict__ oid,
+                                                          int64_t ostride, int64_t N, int bs, int bsh, int kb, int kt) {
+  __shared__ TopkLds<NT> sh;
+  const int ch = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int ncand = kb * bs, c0 = ch * kTopkChunk, n = min(kTopkChunk, ncand - c0);
+  const int32_t* bidx = block_idx + (int64_t)p * kb;
+  float v[PER];
+  load_row_f32<PER>(A + (int64_t)p * ncand + c0, n, tid * PER, v);
+  int bq[PER], bid[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = c0 + min(tid * PER + e, n - 1);
+    bq[e] = bsh >= 0 ? (c >> bsh) : c / bs;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) bid[e] = bidx[bq[e]];
+  uint32_t key[PER];
+  int32_t id[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = c0 + tid * PER + e;
+    const int64_t t = (int64_t)bid[e] * bs + (c - bq[e] * bs);
+    const bool ok = tid * PER + e < n && t >= 0 && t < N;
+    key[e] = ok ? order_key(v[e]) : 0u;
+    id[e] = ok ? (int32_t)t : -1;
+  }
+  const int64_t o = (int64_t)p * ostride + (int64_t)ch * kt;
+  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, okey + o);
+}
+
+// A later pass: chunk blockIdx.x of the (key, id) list of pair blockIdx.y.
+// okey == NULL: the last pass, writing the result.
+template <int PER, int NT>
+__global__ __launch_bounds__(NT) void k_topk_lists(const uint32_t* __restrict__ ikey,
+                                                   const int32_t* __restrict__ iid, int64_t istride, int64_t n_in,
+                                                   uint32_t* __restrict__ okey, int32_t* __restrict__ oid,
+                                                   int64_t ostride, int kt) {
+  __shared__ TopkLds<NT> sh;
+  const int ch = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int64_t c0 = (int64_t)ch * kTopkChunk;
+  uint32_t key[PER];
+  int32_t id[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int64_t i = c0 + tid * PER + e;
+    const bool ok = tid * PER + e < kTopkChunk && i < n_in;
+    const int64_t j = (int64_t)p * istride + (ok ? i : 0);
+    key[e] = ok ? ikey[j] : 0u;
+    id[e] = ok ? iid[j] : -1;
+  }
+  const int64_t o = (int64_t)p * ostride + (int64_t)ch * kt;
+  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, okey ? okey + o : nullptr);
+}
+
 static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }
 // Workgroup size for a row of n keys: the fewest threads with at most 8 keys
 // each (up to 16 with 1024 threads). Measured on the 128k workload: 2048
@@ -848,6 +920,16 @@ static void go_score_tokens_rb(const TokenSelectArgs& a, float* A, hipStream_t s
   }
 }
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t token_ws_bytes(int pairs, int64_t ncand, int kt) {
+  const size_t scores = round256((size_t)pairs * ncand * sizeof(float));
+  if (ncand <= kTopkChunk) return scores;
+  if (ncand > kMaxTokenCandidates || kt > kTopkChunk / 2) return 0;
+  const int64_t list = (ncand + kTopkChunk - 1) / kTopkChunk * kt;
+  return scores + 4 * round256((size_t)pairs * list * 4);  // two (key, id) lists
+}
+
 hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
   switch ((a.G + 15) / 16) {
     case 1: go_score_tokens_rb<1>(a, A, st); break;
@@ -863,12 +945,41 @@ hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ncand = a.kb * a.bs;
+  if (ncand <= kTopkChunk) {
 #define TLS_GO(P, NT)                                                                                          \
   hipLaunchKernelGGL((k_topk_tokens<P, NT>), dim3(a.pairs), dim3(NT), 0, st, A, a.block_idx, a.token_idx, a.N, \
                      a.bs, log2_or_neg(a.bs), a.kb, a.kt)
-  TLS_NT_SWITCH(ncand, TLS_GO)
+    TLS_NT_SWITCH(ncand, TLS_GO)
 #undef TLS_GO
-  return hipGetLastError();
+    return hipGetLastError();
+  }
+  // passes over chunks (workspace: scores, then two (key, id) lists)
+  constexpr int NT = kTopkThreads, PER = kTopkChunk / kTopkThreads;
+  int64_t nch = (ncand + kTopkChunk - 1) / kTopkChunk;
+  const int64_t list = nch * a.kt;
+  const size_t lb = round256((size_t)a.pairs * list * 4);
+  char* base = reinterpret_cast<char*>(A) + round256((size_t)a.pairs * ncand * sizeof(float));
+  uint32_t* key[2] = {reinterpret_cast<uint32_t*>(base), reinterpret_cast<uint32_t*>(base + 2 * lb)};
+  int32_t* id[2] = {reinterpret_cast<int32_t*>(base + lb), reinterpret_cast<int32_t*>(base + 3 * lb)};
+  hipLaunchKernelGGL((k_topk_tokens_chunk<PER, NT>), dim3((unsigned)nch, (unsigned)a.pairs), dim3(NT), 0, st, A,
+                     a.block_idx, key[0], id[0], list, a.N, a.bs, log2_or_neg(a.bs), a.kb, a.kt);
+  e = hipGetLastError();
+  int64_t n = list;
+  int cur = 0;
+  while (e == hipSuccess) {
+    nch = (n + kTopkChunk - 1) / kTopkChunk;
+    if (nch == 1) {  // the last pass writes the result
+      hipLaunchKernelGGL((k_topk_lists<PER, NT>), dim3(1, (unsigned)a.pairs), dim3(NT), 0, st, key[cur], id[cur], list,
+                         n, nullptr, a.token_idx, (int64_t)a.kt, a.kt);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_topk_lists<PER, NT>), dim3((unsigned)nch, (unsigned)a.pairs), dim3(NT), 0, st, key[cur],
+                       id[cur], list, n, key[cur ^ 1], id[cur ^ 1], list, a.kt);
+    e = hipGetLastError();
+    n = nch * a.kt;
+    cur ^= 1;
+  }
+  return e;
 }
 
 }  // namespace tls

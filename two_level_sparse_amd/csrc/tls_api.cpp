@@ -98,8 +98,7 @@ size_t ws_bytes(const Derived& d, int which) {
   switch (which) {
     case TLS_WS_BLOCKS: return round_up((size_t)d.pairs * d.NB * sizeof(float));
     case TLS_WS_TOKENS:
-      if ((int64_t)d.kb * d.bs > kMaxCandidates) return 0;
-      return round_up((size_t)d.pairs * d.kb * d.bs * sizeof(float));
+      return token_ws_bytes(d.pairs, (int64_t)d.kb * d.bs, d.kt);
     case TLS_WS_DECODE: {
       DecodePlan pl;
       plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
@@ -210,8 +209,10 @@ int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* la
   if (rc) return rc;
   if (!q || !label_ch || !codes || !scale || !block_idx || !token_idx)
     return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
-  if ((int64_t)d.kb * d.bs > kMaxCandidates)
-    return set_error(TLS_ERR_UNSUPPORTED, "more than %lld candidate tokens (Kb*bs)", (long long)kMaxCandidates);
+  if (token_ws_bytes(d.pairs, (int64_t)d.kb * d.bs, d.kt) == 0)
+    return set_error(TLS_ERR_UNSUPPORTED,
+                     "more than 16384 candidate tokens (Kb*bs) need Kt' <= 8192 and at most %lld candidates",
+                     (long long)kMaxTokenCandidates);
   if (!ws || ws_len < ws_bytes(d, TLS_WS_TOKENS))
     return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_TOKENS));
   TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,

@@ -11,7 +11,6 @@ namespace tls {
 
 // Candidate tokens per pair the token stage handles (Kb'*bs): one 1024-thread
 // workgroup keeps at most 16 keys per thread.
-constexpr int64_t kMaxCandidates = 16384;
 
 struct Derived {
   int B, Hq, Hkv, G, D, DV, row, v_off, bs, r, kb, kt, pairs;

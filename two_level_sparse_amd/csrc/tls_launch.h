@@ -42,7 +42,12 @@ struct TokenSelectArgs {
   int pairs, Hq, Hkv, G, D, bs, r, kb, kt;
   int64_t N, Ns;  // tokens, and the label cache's per-sequence stride
 };
-hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A /* [pairs, kb*bs] scores */, hipStream_t st);
+// Workspace of the token stage (0: unsupported): candidate scores; above
+// 16384 candidates per pair also two lists for the top-k passes, which need
+// Kt' <= 8192 and at most kMaxTokenCandidates candidates.
+constexpr int64_t kMaxTokenCandidates = (int64_t)1 << 20;
+size_t token_ws_bytes(int pairs, int64_t ncand, int kt);
+hipError_t launch_select_tokens(const TokenSelectArgs& a, float* ws /* token_ws_bytes */, hipStream_t st);
 
 // Exact top-K per row of S ([rows, n] float); ids are column numbers.
 hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* out, hipStream_t st);
