@@ -259,8 +259,7 @@ def main():
             dec.step(qs[r], caches[r])
             return
         if args.mode != "dense":
-            dec.select_blocks(qs[r], caches[r])
-            dec.select_tokens(qs[r], caches[r])
+            dec.select(qs[r], caches[r])
         if ev is not None:  # the library records these around its attention kernel
             T.tls_profile_events(T.TLS_PROFILE_ATTENTION, ev[0], ev[1])
         dec.decode(qs[r], caches[r].kv)

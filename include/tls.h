@@ -73,7 +73,7 @@ enum {
   TLS_ERR_STATE = -5        /* offload context used out of order                */
 };
 
-enum { TLS_WS_BLOCKS = 0, TLS_WS_TOKENS = 1, TLS_WS_DECODE = 2 };
+enum { TLS_WS_BLOCKS = 0, TLS_WS_TOKENS = 1, TLS_WS_DECODE = 2, TLS_WS_SELECT = 3 };
 
 typedef struct tls_shape {
   int32_t batch;         /* B                                                    */
@@ -94,8 +94,9 @@ typedef struct tls_shape {
 } tls_shape_t;
 
 /* Bytes of workspace needed by tls_select_blocks (TLS_WS_BLOCKS),
- * tls_select_tokens (TLS_WS_TOKENS) or tls_sparse_decode (TLS_WS_DECODE) for
- * this shape; 0 if the shape is invalid for that call. tls_select_tokens
+ * tls_select_tokens (TLS_WS_TOKENS), tls_select (TLS_WS_SELECT: the other
+ * two together) or tls_sparse_decode (TLS_WS_DECODE) for this shape; 0 if
+ * the shape is invalid for that call. tls_select_tokens
  * takes any Kt' up to 16384 candidates per pair (Kb' * bs); beyond that (up
  * to 2^20 candidates, e.g. Kb >= NB: token selection over the whole cache)
  * it selects in passes over chunks and needs Kt' <= 8192. The other calls
@@ -141,6 +142,18 @@ int tls_select_blocks(const tls_shape_t *shape, const void *q, const void *summ,
 int tls_select_tokens(const tls_shape_t *shape, const void *q, const int32_t *label_ch, const uint8_t *codes,
                       const float *scale, const int32_t *block_idx, int32_t *token_idx, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* Both stages (section 2A) in one call, with the results of
+ * tls_select_blocks followed by tls_select_tokens: block_idx [B,Hkv,Kb'] and
+ * token_idx [B,Hkv,Kt'], both ascending. Up to 4096 blocks per sequence the
+ * block top-k runs inside the token-scoring kernel (each of a pair's scoring
+ * workgroups selects the pair's blocks from the block scores; one of them
+ * writes block_idx), which saves a launch; above that it runs as in
+ * tls_select_blocks. ws: tls_workspace_size(shape, TLS_WS_SELECT) bytes.
+ * Errors as the two calls. */
+int tls_select(const tls_shape_t *shape, const void *q, const void *summ, const int32_t *label_ch,
+               const uint8_t *codes, const float *scale, int32_t *block_idx, int32_t *token_idx, void *ws,
+               size_t ws_bytes, void *stream);
 
 /* Attention over the kept tokens only (section 2A), split over the token
  * list and merged with log-sum-exp.

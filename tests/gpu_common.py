@@ -161,5 +161,14 @@ def check_all(s, q, kv, lab, pairs=None, expect_exact=False):
         chain_err = max(chain_err, float(np.max(np.abs(out2[p] - o_ref))))
     assert chain_err <= OUT_TOL, chain_err
     stats["chain_err"] = chain_err
+
+    # both stages in one call (tls_select): the same sets as the two calls
+    bi_sep = to_np(run.dec.block_idx).copy()
+    run.dec.block_idx.fill_(-7)
+    run.dec.token_idx.fill_(-7)
+    run.dec.select(run.qd, run.cache)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(run.dec.block_idx), bi_sep)
+    np.testing.assert_array_equal(to_np(run.dec.token_idx).reshape(s.pairs, -1), gt2)
     stats["kt"] = kt
     return stats

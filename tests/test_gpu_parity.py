@@ -64,6 +64,18 @@ SMALL = {
     # two passes; four passes (70016 -> 40000 -> 24000 -> 16000 -> 8000)
     "ds_two_pass": W.small_shape(B=1, Hq=8, Hkv=2, N=40000, bs=64, Kb=1000, Kt=3000),
     "ds_four_pass": W.small_shape(B=1, Hq=4, Hkv=1, N=70000, bs=64, Kb=2000, Kt=8000),
+    # token selection at its limits: exactly 16384 candidates (16 per thread
+    # of one 1024-thread selection); label-channel counts whose codes load
+    # byte by byte (r = 12 with 8 heads, r = 20 with 128); 1100 kept blocks of 8
+    "cand_16384": W.small_shape(B=1, Hq=8, Hkv=2, N=20000, bs=64, Kb=256, Kt=5000),
+    "r12": W.small_shape(B=2, Hq=16, Hkv=2, N=3000, bs=64, r=12, Kb=10, Kt=300),
+    "g128_r20": W.small_shape(B=1, Hq=128, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=3000, bs=64, r=20,
+                              Kb=12, Kt=400, n_outlier=0),
+    "bs8_1100_blocks": W.small_shape(B=1, Hq=8, Hkv=1, N=10000, bs=8, Kb=1100, Kt=2000),
+    # tls_select's block top-k inside the token scorer: up to 4096 blocks (16
+    # per thread at most; 9 at 2188), and the separate block top-k above (4375)
+    "nb_2188": W.small_shape(B=1, Hq=8, Hkv=1, N=140000, bs=64, Kb=40, Kt=1000),
+    "nb_4375_bs16": W.small_shape(B=1, Hq=8, Hkv=1, N=70000, bs=16, Kb=100, Kt=800),
     # degenerate lengths: one cached token; fewer tokens than one block
     "n_one": W.small_shape(B=2, Hq=8, Hkv=2, N=1, bs=64, Kb=4, Kt=16),
     "n_below_block": W.small_shape(B=1, Hq=8, Hkv=1, N=37, bs=64, Kb=3, Kt=20),
@@ -210,7 +222,7 @@ def full_inputs(s):
     ("c4_64k_mla", [0, 9, 15]),
 ])
 def test_full_workloads_sampled(name, pairs):
-    """BASELINE-size workloads in the launch configuration the benchmark uses;
+    """The benchmark's full-size workloads in the launch configuration it uses;
     the oracle checks the sampled (batch, kv-head) pairs."""
     s = W.CONFIGS[name]
     log(f"[gpu] full workload {name}: generating inputs")

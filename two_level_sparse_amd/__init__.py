@@ -26,12 +26,12 @@ TLS_ERR_UNSUPPORTED = -2
 TLS_ERR_WORKSPACE = -3
 TLS_ERR_HIP = -4
 TLS_ERR_STATE = -5
-TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE = 0, 1, 2
+TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE, TLS_WS_SELECT = 0, 1, 2, 3
 
 TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE, TLS_COPY_FULL = 0, 1, 2, 3
 TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
 
-EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens",
+EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens", "tls_select",
             "tls_sparse_decode", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
             "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
             "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
@@ -73,6 +73,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_append_kv": (C.c_int, [sh, vp, i32, vp, vp, vp, vp, vp, vp]),
         "tls_select_blocks": (C.c_int, [sh, vp, vp, vp, vp, vp, sz, vp]),
         "tls_select_tokens": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "tls_select": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_sparse_decode": (C.c_int, [sh, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
         "tls_offload_create": (C.c_int, [sh, vp, vp, vp, vp, vp, C.POINTER(vp)]),
         "tls_offload_slot_map": (vp, [vp, i32]),
@@ -148,6 +149,11 @@ def tls_select_blocks(shape, q, summ, block_idx, block_score=None, ws=None, ws_b
 def tls_select_tokens(shape, q, label_ch, codes, scale, block_idx, token_idx, ws=None, ws_bytes=0, stream=None):
     _check(load_library().tls_select_tokens(C.byref(shape), _ptr(q), _ptr(label_ch), _ptr(codes), _ptr(scale),
                                             _ptr(block_idx), _ptr(token_idx), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tls_select(shape, q, summ, label_ch, codes, scale, block_idx, token_idx, ws=None, ws_bytes=0, stream=None):
+    _check(load_library().tls_select(C.byref(shape), _ptr(q), _ptr(summ), _ptr(label_ch), _ptr(codes), _ptr(scale),
+                                     _ptr(block_idx), _ptr(token_idx), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tls_sparse_decode(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, out, lse=None, ws=None, ws_bytes=0,

@@ -361,6 +361,7 @@ hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st) {
 // keys in registers, thread t owning elements [t*PER, t*PER+PER). Invalid
 // elements carry key 0, below every valid key.
 constexpr int kTopkThreads = 1024;  // the largest workgroup: 16 keys per thread up to 16384
+constexpr int kTopkChunk = 16384;   // the most keys one workgroup selects from
 
 template <int NT>
 struct alignas(16) TopkLds {
@@ -531,7 +532,11 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
     }
     if (!done) thr = lo;
   }
-// Elements above the threshold, plus the first krem equal to it (index order).
+// Elements above the threshold, plus the first krem equal to it (index
+// order), placed by one block-wide scan into an LDS row that goes out in
+// coalesced stores (placing straight into global memory would scatter every
+// store instruction over the wave's whole output range).
+  __shared__ uint32_t stage[NT * PER];
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -539,26 +544,30 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
     eq += (key[e] == thr && key[e] != 0u) ? 1u : 0u;
   }
   const uint32_t pre = block_exclusive_scan(gt | (eq << 16), sh.scan);
-  uint32_t eq_before = pre >> 16;
-  uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem);
+  auto place = [&](bool ids) {
+    uint32_t eq_before = pre >> 16;
+    uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    bool take = key[e] > thr;
-    if (key[e] == thr && key[e] != 0u) {
-      take = eq_before < krem;
-      ++eq_before;
-    }
-    if (take) {
-      if (pos < kk) {  // never more than kk entries
-        out[pos] = id[e];
-        if (out_key) out_key[pos] = key[e];
+    for (int e = 0; e < PER; ++e) {
+      bool take = key[e] > thr;
+      if (key[e] == thr && key[e] != 0u) {
+        take = eq_before < krem;
+        ++eq_before;
       }
-      ++pos;
+      if (take) {
+        if (pos < kk) stage[pos] = ids ? (uint32_t)id[e] : key[e];  // never more than kk entries
+        ++pos;
+      }
     }
-  }
-  for (int i = (int)kk + tid; i < out_len; i += NT) {
-    out[i] = -1;
-    if (out_key) out_key[i] = 0u;  // key 0: no element
+  };
+  place(true);
+  __syncthreads();
+  for (int i = tid; i < out_len; i += NT) out[i] = i < (int)kk ? (int32_t)stage[i] : -1;
+  if (out_key) {
+    __syncthreads();
+    place(false);
+    __syncthreads();
+    for (int i = tid; i < out_len; i += NT) out_key[i] = i < (int)kk ? stage[i] : 0u;  // key 0: no element
   }
 }
 
@@ -757,6 +766,65 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
 }
 
+// Both selection stages of a pair in one launch after the block scores: every
+// token-scoring workgroup first selects its pair's top-Kb blocks from the
+// block-score row itself (the same radix select as k_topk_blocks, thread t
+// holding blocks [t*per, t*per + per)), keeps the list in LDS for its
+// candidate loads, and workgroup 0 of the pair writes it out. The selection
+// is repeated by the pair's few scoring workgroups instead of costing a launch
+// of its own, which would keep all but one workgroup per pair of the chip idle.
+constexpr int kSelMaxBlocks = 4096;  // block-score row per workgroup: 16 per thread
+
+template <int MT, int RB, int UT, int PERB>
+__global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __restrict__ q,
+                                                          const int32_t* __restrict__ label_ch,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scale,
+                                                          const float* __restrict__ S, int NB,
+                                                          int32_t* __restrict__ block_idx, float* __restrict__ A,
+                                                          int Hq, int Hkv, int G, int D, int64_t N, int64_t Ns, int bs,
+                                                          int bsh, int r, int kb) {
+  __shared__ TopkLds<256> sh;
+  __shared__ int32_t sblk[kSelMaxBlocks];
+  const int p = blockIdx.y, tid = threadIdx.x;
+  const int b = p / Hkv, h = p % Hkv;
+  const int lane = tid & 63, wave = tid >> 6, kq = lane >> 4;
+  const int ncand = kb * bs, rb = r / 2;
+  // the query's label channels first: their loads do not wait for the blocks
+  const int32_t* lab = label_ch + (int64_t)h * r;
+  int ch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+  u32x4 qa[MT];
+  label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
+  {
+    const int per = (NB + 255) / 256;
+    float v[PERB];
+    load_row_f32<PERB>(S + (int64_t)p * NB, NB, tid * per, v);
+    uint32_t key[PERB];
+    int32_t id[PERB];
+#pragma unroll
+    for (int e = 0; e < PERB; ++e) {
+      const int c = tid * per + e;
+      id[e] = c;
+      key[e] = (e < per && c < NB) ? order_key(v[e]) : 0u;
+    }
+    block_topk<PERB, 256>(key, id, (uint32_t)kb, sblk, kb, sh);
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = tid; i < kb; i += 256) block_idx[(int64_t)p * kb + i] = sblk[i];
+  const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  UnitLoads<UT> L;
+  unit_loads<RB, UT>(L, sblk, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N, bs, bsh, rb);
+  float val[UT / 4];
+  unit_scores<MT, RB, UT>(val, L, qa, G, rb);
+  const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
+#pragma unroll
+  for (int j = 0; j < UT / 4; ++j)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
+}
+
 // Top-Kt' of the candidate scores of one pair per workgroup; ids are tokens.
 template <int PER, int NT>
 __global__ __launch_bounds__(NT) void k_topk_tokens(const float* __restrict__ A,
@@ -798,7 +866,6 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(const float* __restrict__ A,
 // result. A chunk's selection is in element order and chunks follow each
 // other, so the lists stay in token order and the lower-index tie rule holds
 // across passes. With Kt' <= kTopkChunk / 2 every pass at least halves the list.
-constexpr int kTopkChunk = 16384;
 
 template <int PER, int NT>
 __global__ __launch_bounds__(NT) void k_topk_tokens_chunk(const float* __restrict__ A,
@@ -920,6 +987,42 @@ static void go_score_tokens_rb(const TokenSelectArgs& a, float* A, hipStream_t s
   }
 }
 
+template <int MT, int RB, int UT>
+static void go_score_tokens_sel_ut(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx, float* A,
+                                   hipStream_t st) {
+  const int ncand = a.kb * a.bs;
+  dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
+#define TLS_GO(PB)                                                                                                  \
+  hipLaunchKernelGGL((k_score_tokens_sel<MT, RB, UT, PB>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes,       \
+                     a.scale, S, NB, block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, \
+                     a.kb)
+  if (NB <= 256 * 8)
+    TLS_GO(8);
+  else
+    TLS_GO(16);
+#undef TLS_GO
+}
+
+template <int MT, int RB>
+static void go_score_tokens_sel(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx, float* A,
+                                hipStream_t st) {
+  if constexpr (MT >= 4)
+    go_score_tokens_sel_ut<MT, RB, 4>(a, S, NB, block_idx, A, st);
+  else
+    go_score_tokens_sel_ut<MT, RB, 16>(a, S, NB, block_idx, A, st);
+}
+
+template <int MT>
+static void go_score_tokens_sel_rb(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx, float* A,
+                                   hipStream_t st) {
+  switch (a.r) {
+    case 8: go_score_tokens_sel<MT, 4>(a, S, NB, block_idx, A, st); break;
+    case 16: go_score_tokens_sel<MT, 8>(a, S, NB, block_idx, A, st); break;
+    case 32: go_score_tokens_sel<MT, 16>(a, S, NB, block_idx, A, st); break;
+    default: go_score_tokens_sel<MT, 0>(a, S, NB, block_idx, A, st); break;
+  }
+}
+
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t token_ws_bytes(int pairs, int64_t ncand, int kt) {
@@ -929,6 +1032,8 @@ size_t token_ws_bytes(int pairs, int64_t ncand, int kt) {
   const int64_t list = (ncand + kTopkChunk - 1) / kTopkChunk * kt;
   return scores + 4 * round256((size_t)pairs * list * 4);  // two (key, id) lists
 }
+
+static hipError_t launch_topk_tokens(const TokenSelectArgs& a, float* A, hipStream_t st);
 
 hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
   switch ((a.G + 15) / 16) {
@@ -942,8 +1047,33 @@ hipError_t launch_select_tokens(const TokenSelectArgs& a, float* A, hipStream_t 
     case 8: go_score_tokens_rb<8>(a, A, st); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_topk_tokens(a, A, st);
+}
+
+bool select_fused_ok(int NB, int kb) { return NB <= kSelMaxBlocks && kb <= NB; }
+
+hipError_t launch_select_fused(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx, float* A,
+                               hipStream_t st) {
+  if (!select_fused_ok(NB, a.kb)) return hipErrorInvalidValue;
+  switch ((a.G + 15) / 16) {
+    case 1: go_score_tokens_sel_rb<1>(a, S, NB, block_idx, A, st); break;
+    case 2: go_score_tokens_sel_rb<2>(a, S, NB, block_idx, A, st); break;
+    case 3: go_score_tokens_sel_rb<3>(a, S, NB, block_idx, A, st); break;
+    case 4: go_score_tokens_sel_rb<4>(a, S, NB, block_idx, A, st); break;
+    case 5: go_score_tokens_sel_rb<5>(a, S, NB, block_idx, A, st); break;
+    case 6: go_score_tokens_sel_rb<6>(a, S, NB, block_idx, A, st); break;
+    case 7: go_score_tokens_sel_rb<7>(a, S, NB, block_idx, A, st); break;
+    case 8: go_score_tokens_sel_rb<8>(a, S, NB, block_idx, A, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_topk_tokens(a, A, st);
+}
+
+// The token top-k over the scores in A (one launch, or passes over chunks).
+static hipError_t launch_topk_tokens(const TokenSelectArgs& a, float* A, hipStream_t st) {
+  hipError_t e = hipSuccess;
   const int ncand = a.kb * a.bs;
   if (ncand <= kTopkChunk) {
 #define TLS_GO(P, NT)                                                                                          \

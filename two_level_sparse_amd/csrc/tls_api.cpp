@@ -99,6 +99,10 @@ size_t ws_bytes(const Derived& d, int which) {
     case TLS_WS_BLOCKS: return round_up((size_t)d.pairs * d.NB * sizeof(float));
     case TLS_WS_TOKENS:
       return token_ws_bytes(d.pairs, (int64_t)d.kb * d.bs, d.kt);
+    case TLS_WS_SELECT: {
+      const size_t t = token_ws_bytes(d.pairs, (int64_t)d.kb * d.bs, d.kt);
+      return t == 0 ? 0 : ws_bytes(d, TLS_WS_BLOCKS) + t;
+    }
     case TLS_WS_DECODE: {
       DecodePlan pl;
       plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
@@ -218,6 +222,46 @@ int tls_select_tokens(const tls_shape_t* shape, const void* q, const int32_t* la
   TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
                     d.bs, d.r, d.kb, d.kt, d.N, d.Ns};
   hipError_t e = launch_select_tokens(a, (float*)ws, (hipStream_t)stream);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "select_tokens launch");
+}
+
+int tls_select(const tls_shape_t* shape, const void* q, const void* summ, const int32_t* label_ch,
+               const uint8_t* codes, const float* scale, int32_t* block_idx, int32_t* token_idx, void* ws,
+               size_t ws_len, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!q || !summ || !label_ch || !codes || !scale || !block_idx || !token_idx)
+    return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(q, 16) || !aligned(summ, 16))
+    return set_error(TLS_ERR_INVALID_ARG, "q and summ must be 16-byte aligned");
+  const size_t need = ws_bytes(d, TLS_WS_SELECT);
+  if (need == 0)
+    return set_error(TLS_ERR_UNSUPPORTED,
+                     "more than 16384 candidate tokens (Kb*bs) need Kt' <= 8192 and at most %lld candidates",
+                     (long long)kMaxTokenCandidates);
+  if (!ws || ws_len < need) return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return set_error(TLS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  float* S = (float*)ws;
+  float* A = (float*)((char*)ws + ws_bytes(d, TLS_WS_BLOCKS));
+  BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB, d.NBs};
+  const hipEvent_t pb = g_prof_start[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
+  const hipEvent_t pe = g_prof_end[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
+  if (pb) (void)hipEventRecord(pb, st);
+  hipError_t e = launch_score_blocks(sa, st);
+  if (pe) (void)hipEventRecord(pe, st);
+  if (e != hipSuccess) return hip_error(e, "score_blocks launch");
+  TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
+                    d.bs, d.r, d.kb, d.kt, d.N, d.Ns};
+  if (select_fused_ok((int)d.NB, d.kb)) {
+    e = launch_select_fused(a, S, (int)d.NB, block_idx, A, st);
+    return e == hipSuccess ? TLS_OK : hip_error(e, "select (fused token stage) launch");
+  }
+  e = launch_topk_blocks(S, d.pairs, (int)d.NB, d.kb, block_idx, st);
+  if (e != hipSuccess) return hip_error(e, "topk(blocks) launch");
+  e = launch_select_tokens(a, A, st);
   return e == hipSuccess ? TLS_OK : hip_error(e, "select_tokens launch");
 }
 

@@ -48,6 +48,12 @@ struct TokenSelectArgs {
 constexpr int64_t kMaxTokenCandidates = (int64_t)1 << 20;
 size_t token_ws_bytes(int pairs, int64_t ncand, int kt);
 hipError_t launch_select_tokens(const TokenSelectArgs& a, float* ws /* token_ws_bytes */, hipStream_t st);
+// The token stage with the block top-k folded into its scoring kernel: reads
+// the block scores S [pairs, NB], writes block_idx (= a.block_idx) and
+// token_idx. Only where select_fused_ok(NB, kb).
+bool select_fused_ok(int NB, int kb);
+hipError_t launch_select_fused(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx,
+                               float* ws /* token_ws_bytes */, hipStream_t st);
 
 // Exact top-K per row of S ([rows, n] float); ids are column numbers.
 hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* out, hipStream_t st);

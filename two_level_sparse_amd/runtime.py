@@ -4,15 +4,17 @@ PyTorch allocates device memory and provides streams; all computation is in
 the library's HIP kernels. A `Cache` holds one KV cache with its block
 summaries and INT4 label cache (built once by tls_build_summaries); a
 `Decoder` owns the per-step buffers and workspaces and enqueues one decode
-step (tls_select_blocks -> tls_select_tokens -> tls_sparse_decode).
+step (tls_select -> tls_sparse_decode; tls_select is tls_select_blocks and
+tls_select_tokens in one call).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (TLS_WS_BLOCKS, TLS_WS_DECODE, TLS_WS_TOKENS, shape_of, tls_append_kv, tls_build_summaries,
-               tls_select_blocks, tls_select_tokens, tls_sparse_decode, tls_workspace_size)
+from . import (TLS_WS_BLOCKS, TLS_WS_DECODE, TLS_WS_SELECT, TLS_WS_TOKENS, shape_of, tls_append_kv,
+               tls_build_summaries, tls_select, tls_select_blocks, tls_select_tokens, tls_sparse_decode,
+               tls_workspace_size)
 
 
 def _dev(x, dtype=None, device="cuda"):
@@ -108,10 +110,11 @@ class Decoder:
         self.token_idx = o.get("token_idx", torch.empty((s.B, s.Hkv, self.kt), dtype=torch.int32, device=device))
         self.out = o.get("out", torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device=device))
         self.lse = o.get("lse", torch.empty((s.B, s.Hq), dtype=torch.float32, device=device))
-        self.ws_sizes = {w: tls_workspace_size(self.shape, w) for w in (TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE)}
+        self.ws_sizes = {w: tls_workspace_size(self.shape, w)
+                         for w in (TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_SELECT, TLS_WS_DECODE)}
         if self.ws_sizes[TLS_WS_BLOCKS] == 0 or self.ws_sizes[TLS_WS_DECODE] == 0:
             raise ValueError(f"invalid shape for libtls: {s}")
-        # (a zero TOKENS size: more candidates than the token stage takes; select_tokens then fails)
+        # (a zero TOKENS/SELECT size: more candidates than the token stage takes; select_tokens then fails)
         self.ws = {w: torch.zeros(max(n, 256), dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
 
     # `shape`: the calls' shape when it differs from the decoder's (a growing
@@ -126,6 +129,11 @@ class Decoder:
         tls_select_tokens(shape or self.shape, q, cache.label_ch, cache.codes, cache.scale, bi, self.token_idx,
                           self.ws[TLS_WS_TOKENS], self.ws_sizes[TLS_WS_TOKENS], stream)
 
+    def select(self, q, cache, stream=None, shape=None):
+        """Both selection stages (block_idx and token_idx) in one call."""
+        tls_select(shape or self.shape, q, cache.summ, cache.label_ch, cache.codes, cache.scale, self.block_idx,
+                   self.token_idx, self.ws[TLS_WS_SELECT], self.ws_sizes[TLS_WS_SELECT], stream)
+
     def decode(self, q, kv_cache, stream=None, slot_map=None, slots=0, token_idx=None, shape=None):
         ti = self.token_idx if token_idx is None else token_idx
         tls_sparse_decode(shape or self.shape, q, kv_cache, slot_map, slots, ti, self.out, self.lse,
@@ -134,8 +142,11 @@ class Decoder:
     def step(self, q, cache, stream=None, keep_scores=False):
         """One decode step over `cache` (a Cache, CacheView or GrowingCache)."""
         sh = cache.shape if isinstance(cache, GrowingCache) else None
-        self.select_blocks(q, cache, stream, keep_scores, shape=sh)
-        self.select_tokens(q, cache, stream, shape=sh)
+        if keep_scores:  # the block scores go to self.block_score
+            self.select_blocks(q, cache, stream, keep_scores, shape=sh)
+            self.select_tokens(q, cache, stream, shape=sh)
+        else:
+            self.select(q, cache, stream, shape=sh)
         self.decode(q, cache.kv, stream, shape=sh)
         return self.out
 
