@@ -72,6 +72,9 @@ SMALL = {
     "g128_r20": W.small_shape(B=1, Hq=128, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=3000, bs=64, r=20,
                               Kb=12, Kt=400, n_outlier=0),
     "bs8_1100_blocks": W.small_shape(B=1, Hq=8, Hkv=1, N=10000, bs=8, Kb=1100, Kt=2000),
+    # folded token scores (two candidate tiles per MFMA) with 8 label channels
+    # and 4 heads, a ragged last block
+    "r8_g4_fold": W.small_shape(B=2, Hq=8, Hkv=2, N=3000, bs=64, r=8, Kb=10, Kt=300),
     # tls_select's block top-k inside the token scorer: up to 4096 blocks (16
     # per thread at most; 9 at 2188), and the separate block top-k above (4375)
     "nb_2188": W.small_shape(B=1, Hq=8, Hkv=1, N=140000, bs=64, Kb=40, Kt=1000),

@@ -660,7 +660,8 @@ __device__ __forceinline__ void unit_loads(UnitLoads<UT>& L, const int32_t* bidx
 }
 
 // A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7, from the label
-// channel numbers ch[] (clamped loads, out-of-range entries zeroed after).
+// channel numbers ch[] (clamped loads, channels past r zeroed after). Rows
+// past G repeat head G-1, so the maximum over all rows is the heads' maximum.
 template <int MT>
 __device__ __forceinline__ void label_q(u32x4 (&qa)[MT], const int (&ch)[8], const uint16_t* qp, int G, int D,
                                         int r) {
@@ -674,9 +675,93 @@ __device__ __forceinline__ void label_q(u32x4 (&qa)[MT], const int (&ch)[8], con
     for (int e = 0; e < 8; ++e) hv[e] = qr[ch[e]];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (g >= G || 8 * kq + e >= r) hv[e] = 0u;
+      if (8 * kq + e >= r) hv[e] = 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
+  }
+}
+
+// Eight INT4 codes (one byte per channel pair, low nibble first) widened to
+// bf16, exact: the B fragment of one lane.
+__device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
+  u32x4 bop;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // channel 2e of the word
+    const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // channel 2e + 1
+    bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
+  }
+  return bop;
+}
+
+// ---- folded scores: up to 8 heads on 8 or 16 label channels, blocks of 64 ----
+// One 16x16x32 MFMA carries two tiles of 16 candidates: rows 0-7 are the
+// heads on k 0-15 (tile X's channels), rows 8-15 the same heads on k 16-31
+// (tile Y's); B holds tile X's codes on k 0-15 and tile Y's on k 16-31.
+// With G <= 8 and r <= 16 none of the product is padding, so every lane
+// unpacks codes that count (a plain tile leaves half of k and half of the
+// rows empty, and its lanes unpack zeros). A group of 64 candidates is one
+// whole block: its codes and scales sit at a block-uniform offset (scalar)
+// plus a per-lane constant, so the loads need no per-candidate address
+// arithmetic. Rows past G repeat head G-1, which leaves every maximum as it is.
+// A fragment of lane (n, kq): row n = head n&7 of half n>>3, k = 8kq..8kq+7.
+template <int RB>
+__device__ __forceinline__ u32x4 fold_q(const int32_t* lab, const uint16_t* qp, int G, int D, int r) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
+  const uint16_t* qr = qp + (int64_t)min(n & 7, G - 1) * D;
+  const bool mine = (kq >> 1) == (n >> 3);
+  const int cb = 8 * (kq & 1);
+  uint32_t hv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hv[e] = qr[lab[min(cb + e, r - 1)]];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (!mine || cb + e >= r) hv[e] = 0u;
+  u32x4 qa;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qa[e] = hv[2 * e] | (hv[2 * e + 1] << 16);
+  return qa;
+}
+
+// NG groups of 64 candidates from candidate c0 (a multiple of 64): val[g] is
+// the score of candidate cand[g] (0 if it does not exist). Lane (n, kq) ends
+// with tile 2(kq&1) + (kq>>1) of its group: the MFMA of tiles 0/1 leaves
+// tile 0 on rows 0-1 and tile 1 on rows 2-3, the one of tiles 2/3 likewise,
+// and one 16-lane swap of the two (odd rows of the first with even rows of the
+// second) pairs each tile's two row halves. `bidx` is the pair's block list.
+template <int RB, int NG>
+__device__ __forceinline__ void fold_unit(float (&val)[NG], int (&cand)[NG], const int32_t* bidx,
+                                          __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int c0, int kb,
+                                          int64_t N, u32x4 qa) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
+  const int tile = 2 * (kq & 1) + (kq >> 1);
+  const int voff = (n + 16 * (kq >> 1)) * RB + 4 * (kq & 1);  // tiles 0/1; +32 rows for tiles 2/3
+  uint32_t cwa[NG], cwb[NG];
+  float tsc[NG];
+  int tok0[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int blk = c0 / 64 + g;
+    tok0[g] = __builtin_amdgcn_readfirstlane(blk < kb ? bidx[blk] : 0) * 64;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    cwa[g] = __builtin_amdgcn_raw_buffer_load_b32(cr, voff, tok0[g] * RB, 0);
+    cwb[g] = __builtin_amdgcn_raw_buffer_load_b32(cr, voff + 32 * RB, tok0[g] * RB, 0);
+    tsc[g] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (16 * tile + n) * 4, tok0[g] * 4, 0));
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const f32x4 a = mfma16x16x32(qa, codes_to_bf16(cwa[g]), f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 c = mfma16x16x32(qa, codes_to_bf16(cwb[g]), f32x4{0.f, 0.f, 0.f, 0.f});
+    const float xa = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    const float xc = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xa), __float_as_uint(xc), false, false);
+    const float best = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const int within = 16 * tile + n;
+    const bool ok = c0 / 64 + g < kb && (int64_t)tok0[g] + within < N;
+    val[g] = ok ? tsc[g] * best : 0.0f;
+    cand[g] = c0 + 64 * g + within;
   }
 }
 
@@ -701,20 +786,14 @@ __device__ __forceinline__ void unit_scores(float (&val)[UT / 4], const UnitLoad
         for (int e = 0; e < 4; ++e)
           if (4 * kq + e >= rb) w &= ~(0xFFu << (8 * e));
       }
-      u32x4 bop;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // code of channel 8kq + 2e
-        const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // code of channel 8kq + 2e + 1
-        bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
-      }
+      const u32x4 bop = codes_to_bf16(w);  // channels 8kq .. 8kq+7
       float best = -INFINITY;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const f32x4 a = mfma16x16x32(qa[m], bop, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (m * 16 + 4 * kq + i < G) best = fmaxf(best, a[i]);
+          best = fmaxf(best, a[i]);  // rows past G repeat head G-1
       }
       x[jj] = best;
     }
@@ -735,7 +814,36 @@ __device__ __forceinline__ void unit_scores(float (&val)[UT / 4], const UnitLoad
 // Token scores of 4 units per workgroup (one unit of UT*16 candidates per
 // wave), spread over the chip; the scores go to A[pair, candidate] for
 // k_topk_tokens.
-template <int MT, int RB, int UT>
+// The scores of one wave's unit (UT*16 candidates from c0): val[j] belongs to
+// candidate cand[j]. FOLD: the folded form (G <= 8, r = 8 or 16, bs = 64).
+template <int MT, int RB, int UT, bool FOLD>
+__device__ __forceinline__ void score_unit(float (&val)[UT / 4], int (&cand)[UT / 4], const int32_t* bidx,
+                                           const int32_t* lab, const uint16_t* qp, const uint8_t* cbase,
+                                           const float* sbase, int c0, int kb, int64_t N, int64_t Ns, int G, int D,
+                                           int bs, int bsh, int r) {
+  const int lane = threadIdx.x & 63, kq = lane >> 4;
+  const int rb = r / 2, ncand = kb * bs;
+  if constexpr (FOLD) {
+    static_assert(MT == 1 && (RB == 4 || RB == 8), "folded scores: G <= 8, r = 8 or 16");
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(cbase, (int)(Ns * RB));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase, (int)(Ns * 4));
+    const u32x4 qa = fold_q<RB>(lab, qp, G, D, r);
+    fold_unit<RB, UT / 4>(val, cand, bidx, cr, sr, c0, kb, N, qa);
+  } else {
+    int ch[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+    UnitLoads<UT> L;
+    unit_loads<RB, UT>(L, bidx, cbase, sbase, c0, ncand, N, bs, bsh, rb);
+    u32x4 qa[MT];
+    label_q<MT>(qa, ch, qp, G, D, r);
+    unit_scores<MT, RB, UT>(val, L, qa, G, rb);
+#pragma unroll
+    for (int j = 0; j < UT / 4; ++j) cand[j] = c0 + 64 * j + lane;
+  }
+}
+
+template <int MT, int RB, int UT, bool FOLD>
 __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
                                                       const int32_t* __restrict__ label_ch,
                                                       const uint8_t* __restrict__ codes,
@@ -745,25 +853,19 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
                                                       int bsh, int r, int kb) {
   const int p = blockIdx.y;
   const int b = p / Hkv, h = p % Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kq = lane >> 4;
+  const int wave = threadIdx.x >> 6;
   const int ncand = kb * bs, rb = r / 2;
-  const int32_t* lab = label_ch + (int64_t)h * r;
-  int ch[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
-  UnitLoads<UT> L;
-  unit_loads<RB, UT>(L, block_idx + (int64_t)p * kb, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N,
-                 bs, bsh, rb);
-  u32x4 qa[MT];
-  label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
   float val[UT / 4];
-  unit_scores<MT, RB, UT>(val, L, qa, G, rb);
+  int cand[UT / 4];
+  score_unit<MT, RB, UT, FOLD>(val, cand, block_idx + (int64_t)p * kb, label_ch + (int64_t)h * r,
+                               q + ((int64_t)b * Hq + (int64_t)h * G) * D, codes + (int64_t)p * Ns * rb,
+                               scale + (int64_t)p * Ns, c0, kb, N, Ns, G, D, bs, bsh, r);
   // bounded buffer stores: the hardware drops candidates >= ncand
   const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
   for (int j = 0; j < UT / 4; ++j)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, cand[j] * 4, 0, 0);
 }
 
 // Both selection stages of a pair in one launch after the block scores: every
@@ -775,7 +877,7 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
 // of its own, which would keep all but one workgroup per pair of the chip idle.
 constexpr int kSelMaxBlocks = 4096;  // block-score row per workgroup: 16 per thread
 
-template <int MT, int RB, int UT, int PERB>
+template <int MT, int RB, int UT, int PERB, bool FOLD>
 __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ label_ch,
                                                           const uint8_t* __restrict__ codes,
@@ -788,15 +890,8 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   __shared__ int32_t sblk[kSelMaxBlocks];
   const int p = blockIdx.y, tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
-  const int lane = tid & 63, wave = tid >> 6, kq = lane >> 4;
+  const int wave = tid >> 6;
   const int ncand = kb * bs, rb = r / 2;
-  // the query's label channels first: their loads do not wait for the blocks
-  const int32_t* lab = label_ch + (int64_t)h * r;
-  int ch[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
-  u32x4 qa[MT];
-  label_q<MT>(qa, ch, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
   {
     const int per = (NB + 255) / 256;
     float v[PERB];
@@ -815,14 +910,14 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   if (blockIdx.x == 0)
     for (int i = tid; i < kb; i += 256) block_idx[(int64_t)p * kb + i] = sblk[i];
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
-  UnitLoads<UT> L;
-  unit_loads<RB, UT>(L, sblk, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, ncand, N, bs, bsh, rb);
   float val[UT / 4];
-  unit_scores<MT, RB, UT>(val, L, qa, G, rb);
+  int cand[UT / 4];
+  score_unit<MT, RB, UT, FOLD>(val, cand, sblk, label_ch + (int64_t)h * r, q + ((int64_t)b * Hq + (int64_t)h * G) * D,
+                               codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, kb, N, Ns, G, D, bs, bsh, r);
   const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
   for (int j = 0; j < UT / 4; ++j)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, (c0 + 64 * j + lane) * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[j]), arow, cand[j] * 4, 0, 0);
 }
 
 // Top-Kt' of the candidate scores of one pair per workgroup; ids are tokens.
@@ -957,12 +1052,32 @@ hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* o
 }
 
 
+// The folded token scores apply: up to 8 heads (one head tile), 8 or 16
+// label channels, blocks of 64, and per-pair codes and scales that a buffer
+// resource spans.
+template <int MT, int RB>
+static bool fold_ok(const TokenSelectArgs& a) {
+  if constexpr (MT == 1 && (RB == 4 || RB == 8))
+    return a.G <= 8 && a.bs == 64 && a.Ns <= (int64_t)0x7FFFFFFF / 4;
+  else
+    return false;
+}
+
 template <int MT, int RB, int UT>
 static void go_score_tokens_ut(const TokenSelectArgs& a, float* A, hipStream_t st) {
   const int ncand = a.kb * a.bs;
   dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_score_tokens<MT, RB, UT>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale,
-                     a.block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, a.kb);
+#define TLS_GO(F)                                                                                                 \
+  hipLaunchKernelGGL((k_score_tokens<MT, RB, UT, F>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, a.scale, \
+                     a.block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, a.kb)
+  if constexpr (MT == 1 && (RB == 4 || RB == 8)) {
+    if (fold_ok<MT, RB>(a)) {
+      TLS_GO(true);
+      return;
+    }
+  }
+  TLS_GO(false);
+#undef TLS_GO
 }
 
 // Units of 16 tiles for few head tiles (the unit's loads are its latency);
@@ -992,14 +1107,23 @@ static void go_score_tokens_sel_ut(const TokenSelectArgs& a, const float* S, int
                                    hipStream_t st) {
   const int ncand = a.kb * a.bs;
   dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
-#define TLS_GO(PB)                                                                                                  \
-  hipLaunchKernelGGL((k_score_tokens_sel<MT, RB, UT, PB>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes,       \
+#define TLS_GO(PB, F)                                                                                               \
+  hipLaunchKernelGGL((k_score_tokens_sel<MT, RB, UT, PB, F>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes,    \
                      a.scale, S, NB, block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, \
                      a.kb)
+  if constexpr (MT == 1 && (RB == 4 || RB == 8)) {
+    if (fold_ok<MT, RB>(a)) {
+      if (NB <= 256 * 8)
+        TLS_GO(8, true);
+      else
+        TLS_GO(16, true);
+      return;
+    }
+  }
   if (NB <= 256 * 8)
-    TLS_GO(8);
+    TLS_GO(8, false);
   else
-    TLS_GO(16);
+    TLS_GO(16, false);
 #undef TLS_GO
 }
 
