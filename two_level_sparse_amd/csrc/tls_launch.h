@@ -74,6 +74,7 @@ struct DecodeArgs {
 struct DecodePlan {
   int HT, nht, tps, nsplit;
   int mla;            // 1: the MFMA latent-attention kernel (D 576, DV 512, HT 32)
+  int pv;             // 1: the MFMA kernel for 128-channel K and V rows (k_attend_pv)
   size_t part_bytes;  // partial results (m, l, o) per split
 };
 // Always succeeds for the shapes the API accepts.
