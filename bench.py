@@ -60,6 +60,8 @@ def attention_kernel(s):
     """Name of the attention kernel tls_sparse_decode launches for this shape."""
     if s.D == 576 and s.DV == 512 and s.v_is_k_prefix and s.G > 16:
         return "k_attend_mla"
+    if s.D == 128 and s.DV == 128 and not s.v_is_k_prefix:
+        return "k_attend_pv"
     return "k_attend_gqa" if s.D <= 128 else "k_attend"
 
 
