@@ -693,11 +693,9 @@ __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict
     ml_lds[wave][n][0] = m_run;
     ml_lds[wave][n][1] = l_tot;
   }
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  // this wave's o scaled to the common max, into its own (now idle) buffer:
-  // [16 heads][DV] floats
-  float* ow = reinterpret_cast<float*>(tA[wave]);
+  // this wave's o scaled to the common max, into its own (now idle) buffer
+  // as [channel][16 heads]: one 16-byte write per lane and channel tile
   {
     float f[4];
 #pragma unroll
@@ -709,37 +707,39 @@ __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict
       const float mw = ml_lds[wave][hh][0];
       f[i] = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
     }
+    f32x4* ow = reinterpret_cast<f32x4*>(tA[wave]);
 #pragma unroll
     for (int t = 0; t < DV / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ow[(4 * kq + i) * DV + 16 * t + n] = f[i] * o[t][i];
+      ow[(16 * t + n) * 4 + kq] = f32x4{f[0] * o[t][0], f[1] * o[t][1], f[2] * o[t][2], f[3] * o[t][3]};
   }
   __syncthreads();
   float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + kPartHdr);
-  for (int e = tid; e < HT * (DV + kPartHdr); e += 256) {
-    const int hh = e / (DV + kPartHdr), c = e % (DV + kPartHdr);
+  if (tid < HT) {
     float ms = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
-    float val;
-    if (c == 0) {
-      val = ms;
-    } else if (c == 1) {
-      float l = 0.0f;
+    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][tid][0]);
+    float l = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = ml_lds[w][hh][0];
-        l += mw == -INFINITY ? 0.0f : ml_lds[w][hh][1] * exp2f(mw - ms);
-      }
-      val = l;
-    } else if (c < kPartHdr) {
-      val = 0.0f;
-    } else {
-      val = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) val += reinterpret_cast<const float*>(tA[w])[hh * DV + c - kPartHdr];
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ml_lds[w][tid][0];
+      l += mw == -INFINITY ? 0.0f : ml_lds[w][tid][1] * exp2f(mw - ms);
     }
-    dst[e] = val;
+    *reinterpret_cast<f32x4*>(dst + tid * (DV + kPartHdr)) = f32x4{ms, l, 0.0f, 0.0f};
+  }
+  // thread (channel c, heads 8*(tid/128) ..): the sum over the four waves
+  {
+    const int c = tid & (DV - 1);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g4 = 2 * (tid >> 7) + gg;  // heads 4*g4 .. 4*g4+3
+      if (4 * g4 >= HT) continue;
+      f32x4 acc = reinterpret_cast<const f32x4*>(tA[0])[c * 4 + g4];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) acc += reinterpret_cast<const f32x4*>(tA[w])[c * 4 + g4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g4 + i < HT) dst[(4 * g4 + i) * (DV + kPartHdr) + kPartHdr + c] = acc[i];
+    }
   }
 }
 
