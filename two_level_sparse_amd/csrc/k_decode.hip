@@ -1222,6 +1222,9 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(a.prof_end, st);
+  // split tables sized to the splits there are (the LDS of the 128-split
+  // tables keeps fewer merge workgroups on a CU)
+  if (pl.nsplit <= 32) return launch_merge<512, kMlaHeads, 32>(a, pl, st);
   return launch_merge<512, kMlaHeads, kMlaMaxSplits>(a, pl, st);
 }
 
