@@ -130,6 +130,30 @@ def test_latent_attention_over_every_token():
     assert np.max(np.abs(lse - l_ref)) <= 2e-3
 
 
+def test_gqa_attention_over_every_token():
+    """The 128-channel attention kernel at its split limits: 8 heads on one kv
+    head attend over all 131072 cached tokens (64 splits of 2048 tokens, the
+    dense baseline's per-pair shape at 128k), against the oracle's attention
+    over the same tokens."""
+    from two_level_sparse_amd.runtime import Decoder, bf16
+    s = W.small_shape(B=1, Hq=8, Hkv=1, D=128, DV=128, N=131072, bs=64, r=16, Kb=2048, Kt=131072, seed=43)
+    log(f"[gpu] 128-channel attention over every token: {s}")
+    rng = np.random.default_rng(43)
+    q = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hq, s.D)).astype(np.float32))
+    kv = W.f32_to_bf16_bits(rng.standard_normal((s.B, s.Hkv, s.N, s.row)).astype(np.float32))
+    dec = Decoder(s)
+    idx = torch.arange(s.N, dtype=torch.int32, device="cuda").view(1, 1, -1).contiguous()
+    dec.decode(bf16(q), bf16(kv), token_idx=idx)
+    torch.cuda.synchronize()
+    out = to_np(dec.out).reshape(s.G, s.DV)
+    lse = to_np(dec.lse).reshape(s.G)
+    o_ref, l_ref = oracle.attend_pair(s, q[0], kv[0, 0], np.arange(s.N))
+    err = float(np.max(np.abs(out - o_ref)))
+    log(f"[gpu] 128-channel attention over every token: max err {err:.2e}")
+    assert err <= 2e-3
+    assert np.max(np.abs(lse - l_ref)) <= 2e-3
+
+
 def test_select_all_equals_dense_attention():
     """Kb >= NB and Kt >= N: the GPU step equals dense attention over the whole cache."""
     s = SMALL["select_all"]
