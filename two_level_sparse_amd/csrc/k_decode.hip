@@ -997,76 +997,61 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
       dst[(mt * 16 + 4 * kq + i) * (DV + kPartHdr) + kPartHdr + chh * 256 + t * 16 + n] = o[t][i];
 }
 
-// Split merge. Workgroup = (256 float4 outputs, head tile, pair): the split
-// weights 2^(m_s - M) / L of the tile's heads are formed in LDS while every
-// thread's float4 of o from the first kMergePre splits is already in flight;
-// then a weighted sum.
+// Split merge. Workgroup = (256 float4 outputs, head tile, pair); every
+// thread forms its head's split weights 2^(m_s - M) itself from the splits'
+// (m, l), loaded together with its float4 of o, kMergePre splits per round:
+// no LDS and no barrier.
 constexpr int kMaxSplits = 64;      // split limit of the general attention kernels
 constexpr int kMlaMaxSplits = 128;  // of the latent attention (512 tokens per split at most)
 constexpr int kMergePre = 8;
-template <int DV, int HT, int MAXS>
+template <int DV, int HT>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
                                                float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
-  __shared__ float ml_lds[MAXS][HT][2];
-  __shared__ float w_lds[MAXS][HT];
   const int ht = blockIdx.y, p = blockIdx.z, tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
   constexpr int PS = DV + kPartHdr;  // floats per head in a partial
-  const float* base = part + ((int64_t)p * nht + ht) * nsplit * HT * PS;
-  // (m, l) of the splits first, then this thread's o loads, all in flight together
-  float2 ml[(MAXS * HT + 255) / 256];
-#pragma unroll
-  for (int k = 0; k < (MAXS * HT + 255) / 256; ++k) {
-    const int e = tid + 256 * k;
-    if (e < nsplit * HT) {
-      const int s = e / HT, hh = e % HT;
-      ml[k] = *reinterpret_cast<const float2*>(base + ((int64_t)s * HT + hh) * PS);
-    }
-  }
+  constexpr int SP = HT * PS;        // floats per split
   const int e = blockIdx.x * 256 + tid;  // float4 index in [HT, DV/4]
   const int ee = min(e, HT * (DV / 4) - 1);
   const int hh = ee / (DV / 4), c = (ee % (DV / 4)) * 4;
   const int g = ht * HT + hh;
   const bool active = e < HT * (DV / 4) && g < G;
-  const float* src = base + (int64_t)hh * PS + kPartHdr + c;
-  f32x4 ov[kMergePre];
-#pragma unroll
-  for (int s = 0; s < kMergePre; ++s) ov[s] = *reinterpret_cast<const f32x4*>(src + (int64_t)min(s, nsplit - 1) * HT * PS);
-#pragma unroll
-  for (int k = 0; k < (MAXS * HT + 255) / 256; ++k) {
-    const int e2 = tid + 256 * k;
-    if (e2 < nsplit * HT) {
-      ml_lds[e2 / HT][e2 % HT][0] = ml[k].x;
-      ml_lds[e2 / HT][e2 % HT][1] = ml[k].y;
-    }
-  }
-  __syncthreads();
-  if (tid < HT) {
-    const int hd = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_lds[s][hd][0]);
-    float L = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = ml_lds[s][hd][0];
-      const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-      L += ml_lds[s][hd][1] * w;
-      w_lds[s][hd] = w;
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int s = 0; s < nsplit; ++s) w_lds[s][hd] *= inv;
-    const int gg = ht * HT + hd;
-    if (lse && blockIdx.x == 0 && gg < G)
-      lse[(int64_t)b * Hq + (int64_t)h * G + gg] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  if (!active) return;
+  // head hh of split 0: (m, l, -, -, o[DV])
+  const float* hd = part + ((int64_t)p * nht + ht) * nsplit * SP + (int64_t)hh * PS;
+  // kMergePre splits per round, all their loads in flight together; the
+  // running max and sums are rescaled when a round raises the max
+  float M = -INFINITY, L = 0.0f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += kMergePre) {
+    float2 ml[kMergePre];
+    f32x4 ov[kMergePre];
 #pragma unroll
-  for (int s = 0; s < kMergePre; ++s)
-    if (s < nsplit) o += ov[s] * w_lds[s][hh];
-  for (int s = kMergePre; s < nsplit; ++s)
-    o += *reinterpret_cast<const f32x4*>(src + (int64_t)s * HT * PS) * w_lds[s][hh];
-  *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + (int64_t)h * G + g) * DV + c) = o;
+    for (int u = 0; u < kMergePre; ++u) {
+      const int64_t off = (int64_t)min(s0 + u, nsplit - 1) * SP;
+      ml[u] = *reinterpret_cast<const float2*>(hd + off);
+      ov[u] = *reinterpret_cast<const f32x4*>(hd + off + kPartHdr + c);
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) cm = fmaxf(cm, ml[u].x);  // clamped repeats leave the max as it is
+    if (cm != M) {
+      const float r = M == -INFINITY ? 0.0f : exp2f(M - cm);
+      L *= r;
+      o *= r;
+      M = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u)
+      if (s0 + u < nsplit) {
+        const float w = ml[u].x == -INFINITY ? 0.0f : exp2f(ml[u].x - M);
+        L += ml[u].y * w;
+        o += ov[u] * w;
+      }
+  }
+  if (!active) return;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  if (lse && c == 0) lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + (int64_t)h * G + g) * DV + c) = o * inv;
 }
 
 // Launch shape: head tiles of HT <= 16 heads; a workgroup takes 256-token
@@ -1139,10 +1124,10 @@ static void prof_mark(hipEvent_t ev, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev, st);
 }
 
-template <int DV, int HT, int MAXS = kMaxSplits>
+template <int DV, int HT>
 static hipError_t launch_merge(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 mgrid((unsigned)((HT * DV / 4 + 255) / 256), (unsigned)pl.nht, (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_merge<DV, HT, MAXS>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv,
+  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv,
                      a.G, pl.nht, pl.nsplit);
   return hipGetLastError();
 }
@@ -1222,10 +1207,7 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(a.prof_end, st);
-  // split tables sized to the splits there are (the LDS of the 128-split
-  // tables keeps fewer merge workgroups on a CU)
-  if (pl.nsplit <= 32) return launch_merge<512, kMlaHeads, 32>(a, pl, st);
-  return launch_merge<512, kMlaHeads, kMlaMaxSplits>(a, pl, st);
+  return launch_merge<512, kMlaHeads>(a, pl, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
