@@ -87,6 +87,31 @@ def test_argument_errors_before_any_device_work(lib):
     assert lib.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES, None, None) == T.TLS_OK
 
 
+def test_select_both_stages_arguments_and_workspace(lib):
+    """tls_select (both selection stages in one call): its workspace holds the
+    block scores and the token stage's workspace; it rejects what either
+    stage rejects, before any device work."""
+    for name in W.CONFIGS:
+        sh = T.shape_of(W.CONFIGS[name])
+        blocks = lib.tls_workspace_size(C.byref(sh), T.TLS_WS_BLOCKS)
+        tokens = lib.tls_workspace_size(C.byref(sh), T.TLS_WS_TOKENS)
+        sel = lib.tls_workspace_size(C.byref(sh), T.TLS_WS_SELECT)
+        assert sel >= blocks + tokens > 0, name
+    s = W.CONFIGS["c1_8k_gqa8"]
+    sh = T.shape_of(s)
+    rc = lib.tls_select(C.byref(sh), 16, 16, 16, 16, 16, None, 16, 16, 1 << 30, None)
+    assert rc == T.TLS_ERR_INVALID_ARG and b"NULL" in lib.tls_last_error()
+    rc = lib.tls_select(C.byref(sh), 16, 16, 16, 16, 16, 16, 16, 256, 8, None)
+    assert rc == T.TLS_ERR_WORKSPACE
+    rc = lib.tls_select(C.byref(sh), 8, 16, 16, 16, 16, 16, 16, 256, 1 << 30, None)
+    assert rc == T.TLS_ERR_INVALID_ARG   # q not 16-byte aligned
+    # more candidates than the token stage takes: no workspace size, and the call says why
+    big = T.shape_of(W.CONFIGS["c3_128k_gqa"].with_(Kb=2048, Kt=131072))
+    assert lib.tls_workspace_size(C.byref(big), T.TLS_WS_SELECT) == 0
+    rc = lib.tls_select(C.byref(big), 16, 16, 16, 16, 16, 16, 16, 256, 1 << 30, None)
+    assert rc == T.TLS_ERR_UNSUPPORTED and b"candidate" in lib.tls_last_error()
+
+
 def test_candidate_limit_applies_to_the_token_stage_only(lib):
     """Attention over every token (Kb >= NB, Kt >= N) is a valid decode shape even
     when Kb*bs exceeds what the token stage takes (16384 candidates per pair)."""
