@@ -794,7 +794,7 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   __shared__ int32_t rows[kMlaMaxTps];
   __shared__ f32x4 sx[2][64][2];  // [head tile][lane][token half]: the score exchange
   __shared__ float c_lds[4][16];
-  __shared__ int first_ok;
+  __shared__ uint32_t wfirst[4];
 
   const int split = blockIdx.x, hg = blockIdx.y, p = blockIdx.z;
   const int b = p / Hkv, h = p % Hkv;
@@ -806,9 +806,19 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
   const int ntok = max(t_end - t_begin, 0);
   const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * Ns) * D;
 
-  // rows of the split's tokens (-1: masked), and the first valid one
-  if (tid == 0) first_ok = 0x7FFFFFFF;
-  __syncthreads();
+  // query fragments of the wave's 16 heads over its half of the key steps
+  // (rows past G repeat row G-1), loaded together with the token lists below
+  constexpr int KH = KS / 2;
+  u32x4 qf[KH];
+  {
+    const int g = min(hg * kMlaHeads + mt * 16 + n, G - 1);
+    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq + 32 * KH * chh;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) qf[k] = ld16(qr + 32 * k);
+  }
+  // rows of the split's tokens (-1: masked), and the first valid one (the
+  // smallest valid position over the waves)
+  uint32_t kmin = 0xFFFFFFFFu;
   {
     const int32_t* tix = token_idx + (int64_t)p * kt + t_begin;
     const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
@@ -824,21 +834,14 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
         }
       }
       rows[k] = r;
-      if (r >= 0) atomicMin(&first_ok, k);
+      if (r >= 0) kmin = min(kmin, (uint32_t)k);
     }
   }
-  // query fragments of the wave's 16 heads over its half of the key steps
-  // (rows past G repeat row G-1)
-  constexpr int KH = KS / 2;
-  u32x4 qf[KH];
-  {
-    const int g = min(hg * kMlaHeads + mt * 16 + n, G - 1);
-    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq + 32 * KH * chh;
-#pragma unroll
-    for (int k = 0; k < KH; ++k) qf[k] = ld16(qr + 32 * k);
-  }
+  kmin = wave_umin(kmin);
+  if (lane == 0) wfirst[wave] = kmin;
   __syncthreads();
-  const int fb = first_ok < tps ? rows[first_ok] : -1;
+  const uint32_t first_ok = min(min(wfirst[0], wfirst[1]), min(wfirst[2], wfirst[3]));
+  const int fb = first_ok < (uint32_t)tps ? rows[first_ok] : -1;
   const int ntiles = fb < 0 ? 0 : (ntok + kMlaTile - 1) / kMlaTile;  // nothing valid: empty partial
 
   // direct loads of tile j into `dst`: wave w issues loads w, w+4, ..; lane L
