@@ -375,7 +375,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wave] = x;
-  __syncthreads();
+  lds_sync();
   uint32_t before = 0u;
   for (int w = 0; w < wave; ++w) before += sh[w];
   return before + x - v;
@@ -442,7 +442,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
     sh.red[2][wave] = nval;
   }
   for (int i = tid; i < 512; i += NT) sh.hist[i >> 8][i & 255] = 0u;  // buffers 0 and 1
-  __syncthreads();
+  lds_sync();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, total = 0u;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -467,7 +467,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
         if (key[e] != 0u) atomicAdd(&sh.hist[0][bin[e]], 1u);
       }
       if (tid < 256) sh.hist[2][tid] = 0u;  // (buffer 1 was cleared at the start)
-      __syncthreads();
+      lds_sync();
       const BinPick pk = pick_bin(sh.hist[0], krem);
       pass = 1;
       const uint32_t d = pk.bin;
@@ -488,7 +488,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
         sh.red[0][wave] = kmin;
         sh.red[1][wave] = kmax;
       }
-      __syncthreads();
+      lds_sync();
       lo = 0xFFFFFFFFu;
       hi = 0u;
 #pragma unroll
@@ -512,7 +512,7 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
       for (int e = 0; e < PER; ++e)
         if (key[e] >= lo && key[e] <= hi) atomicAdd(&hcur[(key[e] - lo) >> shift], 1u);
       if (tid < 256) sh.hist[(pass + 1) % 3][tid] = 0u;  // last read two barriers ago
-      __syncthreads();
+      lds_sync();
       const BinPick pk = pick_bin(hcur, krem);
       ++pass;
       const uint32_t d = pk.bin;
@@ -561,12 +561,12 @@ __device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER],
     }
   };
   place(true);
-  __syncthreads();
+  lds_sync();
   for (int i = tid; i < out_len; i += NT) out[i] = i < (int)kk ? (int32_t)stage[i] : -1;
   if (out_key) {
-    __syncthreads();
+    lds_sync();
     place(false);
-    __syncthreads();
+    lds_sync();
     for (int i = tid; i < out_len; i += NT) out_key[i] = i < (int)kk ? stage[i] : 0u;  // key 0: no element
   }
 }
@@ -659,25 +659,51 @@ __device__ __forceinline__ void unit_loads(UnitLoads<UT>& L, const int32_t* bidx
   }
 }
 
-// A fragments: head m*16 + n, label channels 8*kq .. 8*kq+7, from the label
-// channel numbers ch[] (clamped loads, channels past r zeroed after). Rows
-// past G repeat head G-1, so the maximum over all rows is the heads' maximum.
-template <int MT>
-__device__ __forceinline__ void label_q(u32x4 (&qa)[MT], const int (&ch)[8], const uint16_t* qp, int G, int D,
-                                        int r) {
+// A fragments of q on the label channels, in two steps so that the gathers
+// can be issued long before the fragments are needed: gather_q loads the raw
+// bf16 values hv[m][e], pack_q zeroes the padding and pairs them.
+// Plain form: head m*16 + n on label channels 8*kq .. 8*kq+7 (clamped loads,
+// channels past r zeroed). Rows past G repeat head G-1, so the maximum over
+// all rows is the heads' maximum.
+// Folded form (one tile): lane (n, kq) holds head n&7 of half n>>3 on
+// k = 8kq .. 8kq+7; half 0 takes channels 0-15 on k 0-15 and half 1 the same
+// channels on k 16-31, the other quarter of each row is zero.
+template <int MT, bool FOLD>
+__device__ __forceinline__ void gather_q(uint32_t (&hv)[MT][8], const int32_t* lab, const uint16_t* qp, int G,
+                                         int D, int r) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
+  if constexpr (FOLD) {
+    static_assert(MT == 1, "folded scores: one head tile");
+    const uint16_t* qr = qp + (int64_t)min(n & 7, G - 1) * D;
+    const int cb = 8 * (kq & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[0][e] = qr[lab[min(cb + e, r - 1)]];
+  } else {
+    int ch[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint16_t* qr = qp + (int64_t)min(m * 16 + n, G - 1) * D;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[m][e] = qr[ch[e]];
+    }
+  }
+}
+
+template <int MT, bool FOLD>
+__device__ __forceinline__ void pack_q(u32x4 (&qa)[MT], const uint32_t (&hv)[MT][8], int r) {
   const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int g = m * 16 + n;
-    const uint16_t* qr = qp + (int64_t)min(g, G - 1) * D;
-    uint32_t hv[8];
+    uint32_t h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hv[e] = qr[ch[e]];
+    for (int e = 0; e < 8; ++e) {
+      const bool pad = FOLD ? ((kq >> 1) != (n >> 3) || 8 * (kq & 1) + e >= r) : (8 * kq + e >= r);
+      h[e] = pad ? 0u : hv[m][e];
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (8 * kq + e >= r) hv[e] = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qa[m][e] = hv[2 * e] | (hv[2 * e + 1] << 16);
+    for (int e = 0; e < 4; ++e) qa[m][e] = h[2 * e] | (h[2 * e + 1] << 16);
   }
 }
 
@@ -704,25 +730,6 @@ __device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
 // whole block: its codes and scales sit at a block-uniform offset (scalar)
 // plus a per-lane constant, so the loads need no per-candidate address
 // arithmetic. Rows past G repeat head G-1, which leaves every maximum as it is.
-// A fragment of lane (n, kq): row n = head n&7 of half n>>3, k = 8kq..8kq+7.
-template <int RB>
-__device__ __forceinline__ u32x4 fold_q(const int32_t* lab, const uint16_t* qp, int G, int D, int r) {
-  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
-  const uint16_t* qr = qp + (int64_t)min(n & 7, G - 1) * D;
-  const bool mine = (kq >> 1) == (n >> 3);
-  const int cb = 8 * (kq & 1);
-  uint32_t hv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hv[e] = qr[lab[min(cb + e, r - 1)]];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (!mine || cb + e >= r) hv[e] = 0u;
-  u32x4 qa;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qa[e] = hv[2 * e] | (hv[2 * e + 1] << 16);
-  return qa;
-}
-
 // NG groups of 64 candidates from candidate c0 (a multiple of 64): val[g] is
 // the score of candidate cand[g] (0 if it does not exist). Lane (n, kq) ends
 // with tile 2(kq&1) + (kq>>1) of its group: the MFMA of tiles 0/1 leaves
@@ -815,28 +822,22 @@ __device__ __forceinline__ void unit_scores(float (&val)[UT / 4], const UnitLoad
 // wave), spread over the chip; the scores go to A[pair, candidate] for
 // k_topk_tokens.
 // The scores of one wave's unit (UT*16 candidates from c0): val[j] belongs to
-// candidate cand[j]. FOLD: the folded form (G <= 8, r = 8 or 16, bs = 64).
+// candidate cand[j]; qa holds the A fragments of pack_q. FOLD: the folded
+// form (G <= 8, r = 8 or 16, bs = 64).
 template <int MT, int RB, int UT, bool FOLD>
 __device__ __forceinline__ void score_unit(float (&val)[UT / 4], int (&cand)[UT / 4], const int32_t* bidx,
-                                           const int32_t* lab, const uint16_t* qp, const uint8_t* cbase,
-                                           const float* sbase, int c0, int kb, int64_t N, int64_t Ns, int G, int D,
-                                           int bs, int bsh, int r) {
-  const int lane = threadIdx.x & 63, kq = lane >> 4;
+                                           const u32x4 (&qa)[MT], const uint8_t* cbase, const float* sbase, int c0,
+                                           int kb, int64_t N, int64_t Ns, int G, int bs, int bsh, int r) {
+  const int lane = threadIdx.x & 63;
   const int rb = r / 2, ncand = kb * bs;
   if constexpr (FOLD) {
     static_assert(MT == 1 && (RB == 4 || RB == 8), "folded scores: G <= 8, r = 8 or 16");
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(cbase, (int)(Ns * RB));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase, (int)(Ns * 4));
-    const u32x4 qa = fold_q<RB>(lab, qp, G, D, r);
-    fold_unit<RB, UT / 4>(val, cand, bidx, cr, sr, c0, kb, N, qa);
+    fold_unit<RB, UT / 4>(val, cand, bidx, cr, sr, c0, kb, N, qa[0]);
   } else {
-    int ch[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ch[e] = lab[min(8 * kq + e, r - 1)];
     UnitLoads<UT> L;
     unit_loads<RB, UT>(L, bidx, cbase, sbase, c0, ncand, N, bs, bsh, rb);
-    u32x4 qa[MT];
-    label_q<MT>(qa, ch, qp, G, D, r);
     unit_scores<MT, RB, UT>(val, L, qa, G, rb);
 #pragma unroll
     for (int j = 0; j < UT / 4; ++j) cand[j] = c0 + 64 * j + lane;
@@ -856,11 +857,14 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
   const int wave = threadIdx.x >> 6;
   const int ncand = kb * bs, rb = r / 2;
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  uint32_t hv[MT][8];
+  gather_q<MT, FOLD>(hv, label_ch + (int64_t)h * r, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
+  u32x4 qa[MT];
+  pack_q<MT, FOLD>(qa, hv, r);
   float val[UT / 4];
   int cand[UT / 4];
-  score_unit<MT, RB, UT, FOLD>(val, cand, block_idx + (int64_t)p * kb, label_ch + (int64_t)h * r,
-                               q + ((int64_t)b * Hq + (int64_t)h * G) * D, codes + (int64_t)p * Ns * rb,
-                               scale + (int64_t)p * Ns, c0, kb, N, Ns, G, D, bs, bsh, r);
+  score_unit<MT, RB, UT, FOLD>(val, cand, block_idx + (int64_t)p * kb, qa, codes + (int64_t)p * Ns * rb,
+                               scale + (int64_t)p * Ns, c0, kb, N, Ns, G, bs, bsh, r);
   // bounded buffer stores: the hardware drops candidates >= ncand
   const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
@@ -892,10 +896,15 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   const int b = p / Hkv, h = p % Hkv;
   const int wave = tid >> 6;
   const int ncand = kb * bs, rb = r / 2;
+  // the q gathers (label channels, then q on them) go out with the block-score
+  // row and land while the blocks are selected: the selection's barriers
+  // order LDS only and do not wait for them
+  uint32_t hv[MT][8];
   {
     const int per = (NB + 255) / 256;
     float v[PERB];
     load_row_f32<PERB>(S + (int64_t)p * NB, NB, tid * per, v);
+    gather_q<MT, FOLD>(hv, label_ch + (int64_t)h * r, q + ((int64_t)b * Hq + (int64_t)h * G) * D, G, D, r);
     uint32_t key[PERB];
     int32_t id[PERB];
 #pragma unroll
@@ -906,14 +915,16 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
     }
     block_topk<PERB, 256>(key, id, (uint32_t)kb, sblk, kb, sh);
   }
-  __syncthreads();
+  lds_sync();
   if (blockIdx.x == 0)
     for (int i = tid; i < kb; i += 256) block_idx[(int64_t)p * kb + i] = sblk[i];
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  u32x4 qa[MT];
+  pack_q<MT, FOLD>(qa, hv, r);
   float val[UT / 4];
   int cand[UT / 4];
-  score_unit<MT, RB, UT, FOLD>(val, cand, sblk, label_ch + (int64_t)h * r, q + ((int64_t)b * Hq + (int64_t)h * G) * D,
-                               codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, kb, N, Ns, G, D, bs, bsh, r);
+  score_unit<MT, RB, UT, FOLD>(val, cand, sblk, qa, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, kb, N,
+                               Ns, G, bs, bsh, r);
   const __amdgpu_buffer_rsrc_t arow = make_rsrc(A + (int64_t)p * ncand, ncand * 4);
 #pragma unroll
   for (int j = 0; j < UT / 4; ++j)
