@@ -660,41 +660,20 @@ __device__ __forceinline__ void unit_loads(UnitLoads<UT>& L, const int32_t* bidx
 }
 
 // A fragments of q on the label channels, in two steps so that the gathers
-// can be issued long before the fragments are needed (rows past G repeat head
-// G-1, so the maximum over all rows is the heads' maximum).
-//
-// Folded form (G <= 8, one tile): gather_q loads the raw bf16 values of the
-// lane's own fragment, pack_q zeroes the padding and pairs them. Lane (n, kq)
-// holds head n&7 of half n>>3 on k = 8kq .. 8kq+7; half 0 takes channels 0-15
-// on k 0-15 and half 1 the same channels on k 16-31, the other quarter of
-// each row is zero.
-__device__ __forceinline__ void gather_q(uint32_t (&hv)[8], const int32_t* lab, const uint16_t* qp, int G, int D,
-                                         int r) {
-  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
-  const uint16_t* qr = qp + (int64_t)min(n & 7, G - 1) * D;
-  const int cb = 8 * (kq & 1);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hv[e] = qr[lab[min(cb + e, r - 1)]];
-}
-
-__device__ __forceinline__ void pack_q(u32x4 (&qa)[1], const uint32_t (&hv)[8], int r) {
-  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
-  uint32_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = ((kq >> 1) != (n >> 3) || 8 * (kq & 1) + e >= r) ? 0u : hv[e];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qa[0][e] = h[2 * e] | (h[2 * e + 1] << 16);
-}
-
-// Plain form (MT head tiles x 32 label channels, padding zero): the
-// workgroup of 256 threads gathers the matrix once and shares it through LDS.
-// Every wave needs all of it, and a wave gathering it alone makes MT*8 two-byte
+// can be issued long before the fragments are needed. The workgroup of 256
+// threads gathers the matrix of q on the label channels once (MT*16 rows x 32
+// channel slots; rows past G repeat head G-1, so the maximum over all rows is
+// the heads' maximum; slots past r are zero) and shares it through LDS: every
+// wave needs all of it, and a wave gathering it alone makes MT*8 two-byte
 // loads per lane at 64 scattered addresses each (for 128 heads the gathers
-// alone kept a wave busy for about 6 us). Thread t gathers channel slot t%32
-// of rows t/32 + 8k (label_q_issue, into registers); label_q_finish writes
-// them to LDS and reads the fragments back: head m*16 + n, channels 8kq ..
-// 8kq+7, one 16-byte read per tile from rows of 80 bytes (16 rows at distinct
-// bank offsets).
+// alone kept a wave busy for about 6 us). Thread t gathers slot t%32 of rows
+// t/32 + 8k (label_q_issue, into registers); label_q_finish writes them to
+// LDS and reads the fragments back with one 16-byte read per tile from rows
+// of 80 bytes (16 rows at distinct bank offsets).
+// Plain form: lane (n, kq) of tile m holds head m*16 + n on channels 8kq ..
+// 8kq+7. Folded form (G <= 8, one tile): lane (n, kq) holds head n&7 of half
+// n>>3 on k = 8kq .. 8kq+7; half 0 takes channels 0-15 on k 0-15 and half 1
+// the same channels on k 16-31, the other quarter of each row is zero.
 constexpr int kLabRow = 40;  // uint16 per LDS row: 32 channels and 16 bytes of padding
 
 template <int MT>
@@ -706,15 +685,22 @@ __device__ __forceinline__ void label_q_issue(uint32_t (&hl)[2 * MT], const int3
   for (int k = 0; k < 2 * MT; ++k) hl[k] = qp[(int64_t)min((t >> 5) + 8 * k, G - 1) * D + li];
 }
 
-template <int MT>
+template <int MT, bool FOLD>
 __device__ __forceinline__ void label_q_finish(u32x4 (&qa)[MT], const uint32_t (&hl)[2 * MT], uint16_t* sq, int r) {
   const int t = threadIdx.x, i = t & 31;
   const int lane = t & 63, n = lane & 15, kq = lane >> 4;
 #pragma unroll
   for (int k = 0; k < 2 * MT; ++k) sq[((t >> 5) + 8 * k) * kLabRow + i] = i < r ? (uint16_t)hl[k] : (uint16_t)0;
   lds_sync();
+  if constexpr (FOLD) {
+    static_assert(MT == 1, "folded scores: one head tile");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&sq[(n & 7) * kLabRow + 8 * (kq & 1)]);
+    const bool mine = (kq >> 1) == (n >> 3);
+    qa[0] = mine ? v : u32x4{0u, 0u, 0u, 0u};
+  } else {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) qa[m] = *reinterpret_cast<const u32x4*>(&sq[(m * 16 + n) * kLabRow + 8 * kq]);
+    for (int m = 0; m < MT; ++m) qa[m] = *reinterpret_cast<const u32x4*>(&sq[(m * 16 + n) * kLabRow + 8 * kq]);
+  }
 }
 
 // Eight INT4 codes (one byte per channel pair, low nibble first) widened to
@@ -832,7 +818,7 @@ __device__ __forceinline__ void unit_scores(float (&val)[UT / 4], const UnitLoad
 // wave), spread over the chip; the scores go to A[pair, candidate] for
 // k_topk_tokens.
 // The scores of one wave's unit (UT*16 candidates from c0): val[j] belongs to
-// candidate cand[j]; qa holds the A fragments (pack_q or label_q_finish).
+// candidate cand[j]; qa holds the A fragments (label_q_finish).
 // FOLD: the folded form (G <= 8, r = 8 or 16, bs = 64).
 template <int MT, int RB, int UT, bool FOLD>
 __device__ __forceinline__ void score_unit(float (&val)[UT / 4], int (&cand)[UT / 4], const int32_t* bidx,
@@ -869,17 +855,11 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
   const int32_t* lab = label_ch + (int64_t)h * r;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
+  __shared__ __align__(16) uint16_t sq[MT * 16 * kLabRow];
   u32x4 qa[MT];
-  if constexpr (FOLD) {
-    uint32_t hv[8];
-    gather_q(hv, lab, qp, G, D, r);
-    pack_q(qa, hv, r);
-  } else {
-    __shared__ __align__(16) uint16_t sq[MT * 16 * kLabRow];
-    uint32_t hl[2 * MT];
-    label_q_issue<MT>(hl, lab, qp, G, D, r);
-    label_q_finish<MT>(qa, hl, sq, r);
-  }
+  uint32_t hl[2 * MT];
+  label_q_issue<MT>(hl, lab, qp, G, D, r);
+  label_q_finish<MT, FOLD>(qa, hl, sq, r);
   float val[UT / 4];
   int cand[UT / 4];
   score_unit<MT, RB, UT, FOLD>(val, cand, block_idx + (int64_t)p * kb, qa, codes + (int64_t)p * Ns * rb,
@@ -918,18 +898,15 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   // the q gathers (label channels, then q on them) go out with the block-score
   // row and land while the blocks are selected: the selection's barriers
   // order LDS only and do not wait for them
-  __shared__ __align__(16) uint16_t sq[FOLD ? 8 : MT * 16 * kLabRow];
-  uint32_t hv[8], hl[2 * MT];
+  __shared__ __align__(16) uint16_t sq[MT * 16 * kLabRow];
+  uint32_t hl[2 * MT];
   {
     const int per = (NB + 255) / 256;
     float v[PERB];
     load_row_f32<PERB>(S + (int64_t)p * NB, NB, tid * per, v);
     const int32_t* lab = label_ch + (int64_t)h * r;
     const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-    if constexpr (FOLD)
-      gather_q(hv, lab, qp, G, D, r);
-    else
-      label_q_issue<MT>(hl, lab, qp, G, D, r);
+    label_q_issue<MT>(hl, lab, qp, G, D, r);
     uint32_t key[PERB];
     int32_t id[PERB];
 #pragma unroll
@@ -945,10 +922,7 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
     for (int i = tid; i < kb; i += 256) block_idx[(int64_t)p * kb + i] = sblk[i];
   const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
   u32x4 qa[MT];
-  if constexpr (FOLD)
-    pack_q(qa, hv, r);
-  else
-    label_q_finish<MT>(qa, hl, sq, r);
+  label_q_finish<MT, FOLD>(qa, hl, sq, r);
   float val[UT / 4];
   int cand[UT / 4];
   score_unit<MT, RB, UT, FOLD>(val, cand, sblk, qa, codes + (int64_t)p * Ns * rb, scale + (int64_t)p * Ns, c0, kb, N,
