@@ -340,9 +340,8 @@ static void go_blocks(const BlockScoreArgs& a, hipStream_t st) {
   }
 }
 
-// One 16-block tile per wave for a single head tile: twice the workgroups of
-// two tiles per wave, and the shorter waves keep more of the stream in flight
-// across the chip (128k: 12.6 us per launch against 13.1).
+// One 16-block tile per wave for a single head tile (twice the workgroups of
+// two tiles per wave; 128k: 12.6 us per launch against 13.1).
 hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st) {
   const int mt = (a.G + 15) / 16;
   switch (mt) {
