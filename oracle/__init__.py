@@ -198,12 +198,13 @@ def staggered(s, qs, kv, label_ch, built):
     kb = min(s.Kb, s.NB)
     M = np.empty((steps, np_, kb), dtype=np.int32); T = np.full((steps, np_, kb), -1, dtype=np.int32)
     nT = np.empty((steps, np_), dtype=np.int32); ne = np.empty((steps, np_), dtype=np.int32)
+    ev = np.full((steps, np_, 2 * kb), -1, dtype=np.int32)
     out = np.empty((steps, np_, s.G, s.DV)); lse = np.empty((steps, np_, s.G))
     sh = _shape(s)
     rc = lib().orc_staggered(C.byref(sh), C.c_int(steps), _p(qs), _p(kv), _p(label_ch),
                              _p(_c(built.kmax, np.float64)), _p(_c(built.kmin, np.float64)),
                              _p(_c(built.codes, np.int8)), _p(_c(built.scale, np.float32)),
-                             _p(M), _p(T), _p(nT), _p(ne), _p(out), _p(lse))
+                             _p(M), _p(T), _p(nT), _p(ne), _p(ev), _p(out), _p(lse))
     if rc != 0:
         raise RuntimeError(f"oracle staggered schedule failed ({rc})")
-    return Step(M=M, T=T, nT=nT, nevict=ne, out=out, lse=lse)
+    return Step(M=M, T=T, nT=nT, nevict=ne, evicted=ev, out=out, lse=lse)

@@ -34,8 +34,10 @@
  * Parity pins (tests/test_oracle_pins.py): dense attention when Kb and Kt
  * cover everything, the upper-bound property of block scores, brute-force
  * selection on tiny inputs with forced ties, block size 1, the Quest-only and
- * DS-only special cases, quantizer bounds and exact round trips, log-sum-exp
- * against a library routine, and a zero-drift staggered run.
+ * DS-only special cases, quantizer bounds, exact round trips and exact
+ * half-way ties, log-sum-exp against a library routine, a zero-drift
+ * staggered run, and drifting runs whose evictions are replayed by an
+ * independent LRU.
  */
 #include <math.h>
 #include <stdint.h>
@@ -354,12 +356,14 @@ int orc_decode(const orc_shape_t *s, const uint16_t *q, const uint16_t *kv, cons
  * pairs in order (np = B*Hkv).
  * Outputs per step t and pair p:
  *   M [steps, np, Kb'] ; T [steps, np, Kb'] (first nT entries, ascending);
- *   nT [steps, np]; nevict [steps, np]; out [steps, np, G, DV]; lse [steps, np, G].
+ *   nT [steps, np]; nevict [steps, np]; evicted [steps, np, 2*Kb'] (may be
+ *   NULL: the first nevict entries, in eviction order); out [steps, np, G, DV];
+ *   lse [steps, np, G].
  * Returns 0, or a negative value if the schedule was violated.              */
 int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uint16_t *kv,
                   const int32_t *label_ch, const double *kmax, const double *kmin,
                   const int8_t *codes, const float *scale, int32_t *M, int32_t *T, int32_t *nT,
-                  int32_t *nevict, double *out, double *lse) {
+                  int32_t *nevict, int32_t *evicted, double *out, double *lse) {
   int G = s->Hq / s->Hkv;
   int np = s->B * s->Hkv;
   int64_t NB = nblocks(s);
@@ -423,6 +427,7 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
         if (nc < need) perr = -4;
         for (int j = 0; j < need && j < nc; ++j) {
           resident[ev[j].i] = 0;
+          if (evicted) evicted[o * cap + ne] = ev[j].i;
           ++ne;
         }
         n_res -= ne;

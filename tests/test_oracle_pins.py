@@ -205,6 +205,33 @@ def test_quantizer_zero_token_and_packing():
     assert packed[1].tolist() == [0x19, 0x30]
 
 
+def test_quantizer_exact_ties_round_half_to_even():
+    """Quotients k / scale that fall exactly half-way between two codes round to the
+    even code (the reading taken for the INT4 label cache): with the label absmax at
+    7 * 2^e the scale is exactly 2^e, so a key (m + 1/2) * 2^e is an exact tie.
+    Half-away-from-zero would give 3 for 2.5 and -3 for -2.5; half-up would give 3 for
+    2.5; truncation 2 for 2.5 but 3 for 3.5 -- each differs from the table below."""
+    half_even = {0.5: 0, 1.5: 2, 2.5: 2, 3.5: 4, 4.5: 4, 5.5: 6, 6.5: 6,
+                 -0.5: 0, -1.5: -2, -2.5: -2, -3.5: -4, -4.5: -4, -5.5: -6, -6.5: -6}
+    s = W.small_shape(B=1, Hq=2, Hkv=1, N=2 * 3, bs=4, D=16, DV=16, r=8)
+    lab = np.array([0, 2, 3, 5, 8, 11, 12, 15], dtype=np.int32)
+    ties = list(half_even)
+    rows, expect, scales = [], [], []
+    for e in (0, -2, 3):                       # scale exactly 1, 1/4, 8
+        for part in (ties[:7], ties[7:]):      # seven ties plus the +-7 channel per token
+            absmax = 7.0 if part[0] > 0 else -7.0
+            vals = [absmax] + part
+            rows.append([v * 2.0 ** e for v in vals])
+            expect.append([7 if absmax > 0 else -7] + [half_even[v] for v in part])
+            scales.append(2.0 ** e)
+    kv = np.zeros((len(rows), s.row), dtype=np.uint16)
+    kv[:, lab] = bits(np.array(rows))
+    s = s.with_(N=len(rows))
+    codes, scale = oracle.quantize_pair(s, kv, lab)
+    assert scale.tolist() == scales
+    assert codes.tolist() == expect
+
+
 # ------------------------------------------------------------ token stage --
 
 def test_token_stage_is_exact_topk_when_codes_are_exact():
@@ -351,6 +378,57 @@ def test_staggered_invariants_with_drift():
             prev = st.M[t, p].tolist()
             moved += len(Tt)
     assert moved > 0
+
+
+def _drift(q0, steps, sigma, rng):
+    """q_t = q_{t-1} + sigma * N(0, 1), rounded to bf16 (large sigma: many evictions)."""
+    qs = np.empty((steps,) + q0.shape, dtype=np.uint16)
+    qs[0] = q0
+    for t in range(1, steps):
+        qs[t] = W.f32_to_bf16_bits((f64(qs[t - 1]) + sigma * rng.standard_normal(q0.shape)).astype(np.float32))
+    return qs
+
+
+@pytest.mark.parametrize("sigma,Kb,steps", [(0.5, 4, 30), (3.0, 4, 16), (0.25, 6, 40)])
+def test_staggered_lru_eviction_order(sigma, Kb, steps):
+    """Schedules that evict: at every step the oracle's evicted blocks equal an LRU
+    replayed here from the selection history alone -- only as many as the 2*Kb slots
+    require, none of M_{t-1} or M_t, least recently selected first (the prologue
+    selection counts as step -1), lower block first on equal steps."""
+    s = W.small_shape(B=2, Hq=8, Hkv=2, N=2048, bs=64, Kb=Kb, Kt=64, steps=steps)
+    rng = np.random.default_rng(int(sigma * 100) + Kb)
+    q, kv = make_inputs(s, rng)
+    lab = lab_all(s)
+    qs = _drift(q, steps, sigma, rng)
+    built = oracle.decode(s, qs[0], kv, lab)
+    st = oracle.staggered(s, qs, kv, lab, built)
+    assert st.nevict.sum() > 0
+    order_matters = tie_cut = 0
+    for p in range(s.pairs):
+        resident = set(built.block_idx[p].tolist())
+        last = {j: -1 for j in resident}
+        prev = set(resident)
+        for t in range(steps):
+            Mt = set(st.M[t, p].tolist())
+            Tt = sorted(Mt - resident)
+            assert st.T[t, p, : st.nT[t, p]].tolist() == Tt
+            need = max(0, len(resident) + len(Tt) - 2 * Kb)
+            cands = sorted((last[j], j) for j in resident - prev - Mt)
+            assert len(cands) >= need
+            expect = [j for _, j in cands[:need]]
+            assert st.nevict[t, p] == need
+            assert st.evicted[t, p, :need].tolist() == expect, (p, t)
+            if 0 < need < len(cands):
+                order_matters += 1
+                tie_cut += cands[need - 1][0] == cands[need][0]
+            resident = (resident - set(expect)) | set(Tt)
+            assert len(resident) <= 2 * Kb and Mt <= resident
+            for j in Mt:
+                last[j] = t
+            prev = Mt
+    assert order_matters > 0   # steps where a different eviction rule would pick other blocks
+    if sigma >= 3.0:
+        assert tie_cut > 0     # the lower-block rule decides among blocks last selected together
 
 
 def _sub(built, p):
