@@ -190,8 +190,12 @@ def decode(s, q, kv, label_ch, pairs=None, built=None, force_blocks=None, force_
                 token_idx=ti, ntok=nt, out=out, lse=lse)
 
 
-def staggered(s, qs, kv, label_ch, built):
-    """Staggered offloaded schedule (O10) over all pairs; `built` = decode(...) over all pairs."""
+def staggered(s, qs, kv, label_ch, built, force_prologue=None, force_M=None):
+    """Staggered offloaded schedule (O10) over all pairs; `built` = decode(...) over all pairs.
+
+    force_prologue [np, Kb'] / force_M [steps, np, Kb'] replace the schedule's own
+    block selections (the prologue's and each step's), so that a run whose sets
+    differ only inside the score band can be followed step by step."""
     steps = qs.shape[0]
     qs = _c(qs, np.uint16); kv = _c(kv, np.uint16); label_ch = _c(label_ch, np.int32)
     np_ = s.pairs
@@ -204,6 +208,8 @@ def staggered(s, qs, kv, label_ch, built):
     rc = lib().orc_staggered(C.byref(sh), C.c_int(steps), _p(qs), _p(kv), _p(label_ch),
                              _p(_c(built.kmax, np.float64)), _p(_c(built.kmin, np.float64)),
                              _p(_c(built.codes, np.int8)), _p(_c(built.scale, np.float32)),
+                             _p(None if force_prologue is None else _c(force_prologue, np.int32)),
+                             _p(None if force_M is None else _c(force_M, np.int32)),
                              _p(M), _p(T), _p(nT), _p(ne), _p(ev), _p(out), _p(lse))
     if rc != 0:
         raise RuntimeError(f"oracle staggered schedule failed ({rc})")

@@ -340,6 +340,16 @@ int orc_decode(const orc_shape_t *s, const uint16_t *q, const uint16_t *kv, cons
   return err;
 }
 
+/* Copies a given block set (ascending, distinct, in [0, NB)) into dst; -1 if
+ * it is not one. */
+static int orc_force_set(int32_t *dst, const int32_t *src, int kb, int64_t NB) {
+  for (int j = 0; j < kb; ++j) {
+    if (src[j] < 0 || src[j] >= NB || (j > 0 && src[j] <= src[j - 1])) return -1;
+    dst[j] = src[j];
+  }
+  return 0;
+}
+
 /* ------------------------------------------- O10: staggered offloaded run --
  * Section 2B: block selections are stable across consecutive steps
  * (M_t ~ M_{t-1}); at step t the token stage runs inside M_{t-1} while M_t is
@@ -354,6 +364,10 @@ int orc_decode(const orc_shape_t *s, const uint16_t *q, const uint16_t *kv, cons
  *             block index on equal steps);  C_{t+1} = (C_t - evicted) u T_t.
  * qs [steps, B, Hq, D]; kmax/kmin/codes/scale as built by orc_decode for ALL
  * pairs in order (np = B*Hkv).
+ * force_prologue [np, Kb'] and force_M [steps, np, Kb'] (each may be NULL):
+ *   block sets, ascending, used in place of the prologue's and step t's own
+ *   stage 1 -- so that a run whose selections differ from these only among
+ *   blocks of (nearly) equal score can be followed step by step.
  * Outputs per step t and pair p:
  *   M [steps, np, Kb'] ; T [steps, np, Kb'] (first nT entries, ascending);
  *   nT [steps, np]; nevict [steps, np]; evicted [steps, np, 2*Kb'] (may be
@@ -362,8 +376,9 @@ int orc_decode(const orc_shape_t *s, const uint16_t *q, const uint16_t *kv, cons
  * Returns 0, or a negative value if the schedule was violated.              */
 int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uint16_t *kv,
                   const int32_t *label_ch, const double *kmax, const double *kmin,
-                  const int8_t *codes, const float *scale, int32_t *M, int32_t *T, int32_t *nT,
-                  int32_t *nevict, int32_t *evicted, double *out, double *lse) {
+                  const int8_t *codes, const float *scale, const int32_t *force_prologue,
+                  const int32_t *force_M, int32_t *M, int32_t *T, int32_t *nT, int32_t *nevict,
+                  int32_t *evicted, double *out, double *lse) {
   int G = s->Hq / s->Hkv;
   int np = s->B * s->Hkv;
   int64_t NB = nblocks(s);
@@ -391,6 +406,7 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
     int n_res = 0, perr = 0;
     const uint16_t *q0 = qs + ((int64_t)b * s->Hq + (int64_t)h * G) * s->D;
     if (orc_select_blocks_pair(s, q0, mx, mn, NULL, Sbuf, prev) < 0) perr = -2;
+    if (force_prologue && orc_force_set(prev, force_prologue + (int64_t)p * kb, kb, NB) != 0) perr = -5;
     for (int j = 0; j < kb; ++j) {
       resident[prev[j]] = 1;
       last[prev[j]] = -1;
@@ -404,6 +420,7 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
       int64_t o = (int64_t)t * np + p;
       orc_attend_pair(s, qt, kvp, tok, nt, out + o * G * s->DV, lse + o * G);
       if (orc_select_blocks_pair(s, qt, mx, mn, NULL, Sbuf, cur) < 0) perr = -2;
+      if (force_M && orc_force_set(cur, force_M + o * kb, kb, NB) != 0) perr = -5;
       memset(in_prev, 0, (size_t)NB);
       memset(in_cur, 0, (size_t)NB);
       for (int j = 0; j < kb; ++j) {

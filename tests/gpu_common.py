@@ -162,13 +162,24 @@ def check_all(s, q, kv, lab, pairs=None, expect_exact=False):
     assert chain_err <= OUT_TOL, chain_err
     stats["chain_err"] = chain_err
 
-    # both stages in one call (tls_select): the same sets as the two calls
+    # both stages in one call (tls_select, the path the benchmark times): the
+    # same sets as the two calls, and each checked against the oracle on its
+    # own -- blocks by the band rule on the oracle's block scores, tokens by the
+    # band rule on the oracle's candidate scores over the call's own block set
     bi_sep = to_np(run.dec.block_idx).copy()
     run.dec.block_idx.fill_(-7)
     run.dec.token_idx.fill_(-7)
     run.dec.select(run.qd, run.cache)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(to_np(run.dec.block_idx), bi_sep)
-    np.testing.assert_array_equal(to_np(run.dec.token_idx).reshape(s.pairs, -1), gt2)
+    bi_sel = to_np(run.dec.block_idx).reshape(s.pairs, -1)
+    ti_sel = to_np(run.dec.token_idx).reshape(s.pairs, -1)
+    np.testing.assert_array_equal(bi_sel.reshape(bi_sep.shape), bi_sep)
+    np.testing.assert_array_equal(ti_sel, gt2)
+    for i, p in enumerate(pairs):
+        b, h = divmod(int(p), s.Hkv)
+        band_check(bi_sel[p], np.arange(s.NB), ref.S[i], kb)
+        _, cand, cs = oracle.select_tokens_pair(s, q[b, h * s.G:(h + 1) * s.G], lab[h], ref.codes[i],
+                                                ref.scale[i], bi_sel[p])
+        band_check(ti_sel[p], cand, cs, s.Kt)
     stats["kt"] = kt
     return stats

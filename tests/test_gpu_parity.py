@@ -189,6 +189,34 @@ def test_integer_ties_are_broken_by_lower_index(seed):
     log(f"[gpu] integer ties seed {seed}: {st}")
 
 
+def test_build_exact_ties_round_half_to_even():
+    """The label cache built on the GPU for keys whose quotients k / scale are exact
+    half-way cases (label absmax 7 * 2^e, so the scale is 2^e): codes round half to
+    even (hand-written table), bit-exact with the oracle."""
+    import two_level_sparse_amd as T
+    from two_level_sparse_amd.runtime import Cache
+    half_even = {0.5: 0, 1.5: 2, 2.5: 2, 3.5: 4, 4.5: 4, 5.5: 6, 6.5: 6,
+                 -0.5: 0, -1.5: -2, -2.5: -2, -3.5: -4, -4.5: -4, -5.5: -6, -6.5: -6}
+    ties = list(half_even)
+    lab = np.array([[0, 2, 3, 5, 8, 11, 12, 15]], dtype=np.int32)
+    rows, expect = [], []
+    for e in (0, -2, 3):
+        for part in (ties[:7], ties[7:]):
+            a = 7.0 if part[0] > 0 else -7.0
+            rows.append([a * 2.0 ** e] + [v * 2.0 ** e for v in part])
+            expect.append([7 if a > 0 else -7] + [half_even[v] for v in part])
+    s = W.small_shape(B=1, Hq=2, Hkv=1, D=64, DV=64, N=len(rows), bs=4, r=8, Kb=1, Kt=1, n_outlier=0)
+    kv = np.zeros((1, 1, s.N, s.row), dtype=np.uint16)
+    kv[0, 0][:, lab[0]] = W.f32_to_bf16_bits(np.array(rows, dtype=np.float32))
+    cache = Cache(s, kv, lab).build()
+    torch.cuda.synchronize()
+    codes = to_np(cache.codes).reshape(s.N, s.r // 2)
+    ref_codes, ref_scale = oracle.quantize_pair(s, kv[0, 0], lab[0])
+    assert ref_codes.tolist() == expect
+    np.testing.assert_array_equal(codes, oracle.pack_codes(np.array(expect, dtype=np.int8)))
+    np.testing.assert_array_equal(to_np(cache.scale).reshape(-1).view(np.uint32), ref_scale.view(np.uint32))
+
+
 def test_deterministic():
     s = SMALL["gqa4"]
     q, kv, lab = inputs(s, seed=9)
@@ -251,9 +279,9 @@ def full_inputs(s):
 
 @pytest.mark.parametrize("name,pairs", [
     ("c1_8k_gqa8", None),
-    ("c2_32k_gqa", [0, 7, 13, 31]),
-    ("c3_128k_gqa", [0, 21, 42, 63]),
-    ("c4_64k_mla", [0, 9, 15]),
+    ("c2_32k_gqa", list(range(0, 32, 2))),
+    ("c3_128k_gqa", list(range(0, 64, 4))),
+    ("c4_64k_mla", None),
 ])
 def test_full_workloads_sampled(name, pairs):
     """The benchmark's full-size workloads in the launch configuration it uses;

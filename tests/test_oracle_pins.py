@@ -429,6 +429,17 @@ def test_staggered_lru_eviction_order(sigma, Kb, steps):
     assert order_matters > 0   # steps where a different eviction rule would pick other blocks
     if sigma >= 3.0:
         assert tie_cut > 0     # the lower-block rule decides among blocks last selected together
+    # made to follow its own selections, the schedule is unchanged; made to follow
+    # other (valid) selections, it applies the same rules to them
+    same = oracle.staggered(s, qs, kv, lab, built, force_prologue=built.block_idx, force_M=st.M)
+    for key in ("M", "T", "nT", "nevict", "evicted", "out"):
+        np.testing.assert_array_equal(getattr(same, key), getattr(st, key))
+    alt_M = st.M.copy()
+    alt_M[1] = st.M[0]                    # step 1 repeats step 0's selection: nothing to move
+    alt = oracle.staggered(s, qs, kv, lab, built, force_prologue=built.block_idx, force_M=alt_M)
+    np.testing.assert_array_equal(alt.M, alt_M)
+    assert np.all(alt.nT[1] == 0) and np.all(alt.nevict[1] == 0)
+    np.testing.assert_array_equal(alt.out[:2], st.out[:2])   # steps 0 and 1 use M_{-1} and M_0
 
 
 def _sub(built, p):
