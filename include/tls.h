@@ -73,7 +73,7 @@ enum {
   TLS_ERR_STATE = -5        /* offload context used out of order                */
 };
 
-enum { TLS_WS_BLOCKS = 0, TLS_WS_TOKENS = 1, TLS_WS_DECODE = 2, TLS_WS_SELECT = 3 };
+enum { TLS_WS_BLOCKS = 0, TLS_WS_TOKENS = 1, TLS_WS_DECODE = 2, TLS_WS_SELECT = 3, TLS_WS_STEP = 4 };
 
 typedef struct tls_shape {
   int32_t batch;         /* B                                                    */
@@ -166,6 +166,35 @@ int tls_select(const tls_shape_t *shape, const void *q, const void *summ, const 
 int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_cache, const int32_t *slot_map,
                       int32_t slots_per_pair, const int32_t *token_idx, float *out, float *lse_opt, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* One whole decode step (section 2A: both selection stages, then attention
+ * over the kept tokens) in ONE launch: the results of tls_select followed by
+ * tls_sparse_decode on the full cache (kv [B,Hkv,N,row], no slot map) --
+ * block_idx [B,Hkv,Kb'] and token_idx [B,Hkv,Kt'] ascending, out [B,Hq,DV],
+ * lse_opt [B,Hq] or NULL. The pairs' steps are interleaved on the device: one
+ * pair's selection runs while others stream their block summaries or gather
+ * their rows.
+ * Covers D = DV = 128 with a separate V, G <= 8, block size 64, 8 or 16 label
+ * channels, NB <= 4096 and Kb' <= 128; other shapes return
+ * TLS_ERR_UNSUPPORTED (use the two calls).
+ * ws: tls_workspace_size(shape, TLS_WS_STEP) bytes, 256-byte aligned. Unlike
+ * the other workspaces, its contents matter: it must be zero-filled before its
+ * first use by this call (e.g. one hipMemset), and every call that completes
+ * leaves it in that state, so later calls need no clearing. A workspace
+ * written by anything else in between must be cleared again. Calls sharing a
+ * workspace must not overlap in time. Errors as tls_select and
+ * tls_sparse_decode; a failure inside the launch (which no valid input
+ * causes) is reported by tls_decode_step_status. */
+int tls_decode_step(const tls_shape_t *shape, const void *q, const void *summ, const int32_t *label_ch,
+                    const uint8_t *codes, const float *scale, const void *kv, int32_t *block_idx,
+                    int32_t *token_idx, float *out, float *lse_opt, void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronises `stream` and reads the error word tls_decode_step keeps in its
+ * workspace: TLS_OK, or TLS_ERR_STATE if a launch abandoned work (an item it
+ * waited for was not published within its time limit, or an XCD's queue was
+ * left undrained); the outputs of such a launch are not valid and the
+ * workspace must be zero-filled again. */
+int tls_decode_step_status(void *ws, void *stream);
 
 /* ----------------------------------------------------------------------
  * Staggered offload (section 2B). The full cache stays in pinned host memory;

@@ -182,4 +182,34 @@ def check_all(s, q, kv, lab, pairs=None, expect_exact=False):
                                                 ref.scale[i], bi_sel[p])
         band_check(ti_sel[p], cand, cs, s.Kt)
     stats["kt"] = kt
+
+    # the whole step in one launch (tls_decode_step, where it covers the shape):
+    # the same sets as tls_select (the same arithmetic), outputs within 2e-3 of
+    # the oracle's attention over its own token sets; twice in a row, since
+    # the launch must leave its workspace ready for the next one
+    if run.dec.one_launch:
+        out_sep = to_np(run.dec.out).copy()
+        for rep in range(2):
+            run.dec.block_idx.fill_(-7)
+            run.dec.token_idx.fill_(-7)
+            run.dec.out.fill_(float("nan"))
+            run.dec.step_one_launch(run.qd, run.cache)
+            run.dec.step_status()
+            bi1 = to_np(run.dec.block_idx).reshape(s.pairs, -1)
+            ti1 = to_np(run.dec.token_idx).reshape(s.pairs, -1)
+            np.testing.assert_array_equal(bi1, bi_sel)
+            np.testing.assert_array_equal(ti1, ti_sel)
+            o1 = to_np(run.dec.out).reshape(s.pairs, s.G, s.DV)
+            l1 = to_np(run.dec.lse).reshape(s.pairs, s.G)
+            step_err = 0.0
+            for i, p in enumerate(pairs):
+                b, h = divmod(int(p), s.Hkv)
+                tk = ti1[p][ti1[p] >= 0]
+                o_ref, l_ref = oracle.attend_pair(s, q[b, h * s.G:(h + 1) * s.G], kv[b, h], tk)
+                step_err = max(step_err, float(np.max(np.abs(o1[p] - o_ref))), float(np.max(np.abs(l1[p] - l_ref))))
+            assert step_err <= OUT_TOL, step_err
+            # every pair, checked or not, agrees with the separate calls' attention
+            sep = out_sep.reshape(s.pairs, s.G, s.DV)
+            assert float(np.max(np.abs(o1 - sep))) <= 1e-4
+        stats["one_launch_err"] = step_err
     return stats

@@ -46,6 +46,26 @@ def test_workspace_sizes(lib, name):
     dec = T.tls_workspace_size(sh, T.TLS_WS_DECODE)
     assert dec >= s.Hq * s.B * (s.DV + 2) * 4
     assert T.tls_workspace_size(sh, 7) == 0
+    step = T.tls_workspace_size(sh, T.TLS_WS_STEP)
+    if s.D == 128 and not s.v_is_k_prefix and s.G <= 8:
+        # the one-launch step: state words, block scores and the partials
+        assert step >= s.pairs * s.NB * 4 + s.pairs * ((s.Kt + 255) // 256) * 8 * 132 * 4
+    else:
+        assert step == 0   # shapes it does not cover (the 64k latent-attention workload)
+
+
+def test_one_launch_step_rejects_what_it_does_not_cover(lib):
+    s = W.CONFIGS["c4_64k_mla"]
+    rc = lib.tls_decode_step(C.byref(T.shape_of(s)), 16, 16, 16, 16, 16, 16, 16, 16, 16, None, 256, 1 << 30, None)
+    assert rc == T.TLS_ERR_UNSUPPORTED
+    s = W.CONFIGS["c3_128k_gqa"]
+    sh = T.shape_of(s)
+    rc = lib.tls_decode_step(C.byref(sh), 16, 16, 16, 16, 16, 16, 16, 16, 16, None, 256, 16, None)
+    assert rc == T.TLS_ERR_WORKSPACE
+    rc = lib.tls_decode_step(C.byref(sh), 16, 16, 16, 16, 16, None, 16, 16, 16, None, 256, 1 << 30, None)
+    assert rc == T.TLS_ERR_INVALID_ARG
+    for bad in (dict(Hq=128), dict(bs=32), dict(r=32), dict(Kb=200)):
+        assert T.tls_workspace_size(T.shape_of(s.with_(**bad)), T.TLS_WS_STEP) == 0, bad
 
 
 def test_invalid_shapes_give_zero_workspace(lib):

@@ -26,13 +26,13 @@ TLS_ERR_UNSUPPORTED = -2
 TLS_ERR_WORKSPACE = -3
 TLS_ERR_HIP = -4
 TLS_ERR_STATE = -5
-TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE, TLS_WS_SELECT = 0, 1, 2, 3
+TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE, TLS_WS_SELECT, TLS_WS_STEP = 0, 1, 2, 3, 4
 
 TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE, TLS_COPY_FULL = 0, 1, 2, 3
 TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens", "tls_select",
-            "tls_sparse_decode", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
+            "tls_sparse_decode", "tls_decode_step", "tls_decode_step_status", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
             "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
             "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
             "tls_last_error", "tls_version"]
@@ -75,6 +75,8 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_select_tokens": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_select": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_sparse_decode": (C.c_int, [sh, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "tls_decode_step": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "tls_decode_step_status": (C.c_int, [vp, vp]),
         "tls_offload_create": (C.c_int, [sh, vp, vp, vp, vp, vp, C.POINTER(vp)]),
         "tls_offload_slot_map": (vp, [vp, i32]),
         "tls_prefetch_delta": (C.c_int, [vp, i32, vp, vp, vp, C.POINTER(i64)]),
@@ -161,6 +163,19 @@ def tls_sparse_decode(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, o
     _check(load_library().tls_sparse_decode(C.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(slot_map),
                                             int(slots_per_pair), _ptr(token_idx), _ptr(out), _ptr(lse), _ptr(ws),
                                             ws_bytes, _stream(stream)))
+
+
+def tls_decode_step(shape, q, summ, label_ch, codes, scale, kv, block_idx, token_idx, out, lse=None, ws=None,
+                    ws_bytes=0, stream=None):
+    """Both selection stages and the attention in one launch; ws must be
+    zero-filled before its first use (every call leaves it so)."""
+    _check(load_library().tls_decode_step(C.byref(shape), _ptr(q), _ptr(summ), _ptr(label_ch), _ptr(codes),
+                                          _ptr(scale), _ptr(kv), _ptr(block_idx), _ptr(token_idx), _ptr(out),
+                                          _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tls_decode_step_status(ws, stream=None):
+    _check(load_library().tls_decode_step_status(_ptr(ws), _stream(stream)))
 
 
 def tls_offload_create(shape, host_kv, dev_cache, slot_map0, slot_map1, initial_blocks):

@@ -11,7 +11,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libtls.so"
 BUILD = PKG / "_build"
-SOURCES = ["k_build.hip", "k_select.hip", "k_decode.hip", "k_copy.hip", "tls_api.cpp", "offload.cpp"]
+SOURCES = ["k_build.hip", "k_select.hip", "k_decode.hip", "k_step.hip", "k_copy.hip", "tls_api.cpp", "offload.cpp"]
 ARCH = os.environ.get("TLS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops are kept out of the device code (-packed-fp32-ops).

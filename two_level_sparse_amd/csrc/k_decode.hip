@@ -23,14 +23,12 @@
 // on this part writes back the XCD's whole L2; a second launch is cheaper.)
 #include <type_traits>
 
+#include "tls_attn_dev.h"
 #include "tls_dev.h"
 #include "tls_launch.h"
 
 namespace tls {
 
-// A split's partial per head: m, l, two unused floats, then o[DV] (16-byte
-// aligned for the merge's vector loads).
-constexpr int kPartHdr = 4;
 
 template <int D, int DV, int HT, bool PRE, bool SMAP>
 __global__ __launch_bounds__(256) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -502,245 +500,26 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
   }
 }
 
-// k_attend_pv: 128-channel K and V in one 512-byte row (the GQA shape), with
-// both products on MFMA. Workgroup = 4 wavefronts = one (pair, head tile of
-// up to 16 heads, token split); every wave streams its own 16-token tiles
-// (tiles w, w+4, ...) and keeps its own (m, l, o); the four meet in LDS.
-//   - The split's token rows are resolved once into LDS. A tile's 16 whole
-//     rows go to wave-private LDS with direct global->LDS 16-byte loads (two
-//     512-byte rows per load), double-buffered. Row r keeps global 16-byte
-//     piece c at position c ^ swz(r), which spreads both read patterns below
-//     over the banks. A masked token loads the split's first valid row
-//     (finite data) and is masked in softmax.
-//   - S^T = K q^T on MFMA (16x16x32): A = the 16 key rows, B = the heads'
-//     query fragments kept in registers. The lane of head n then holds tokens
-//     4kq+i, which is exactly its A-operand row of P for a 16x16x16 product.
-//   - Online softmax per head in the exp2 domain; the running max is made
-//     common across the lanes of a head with cross-row swaps.
-//   - O += P V on MFMA (16x16x16, 8 tiles of 16 channels), P as two bf16 terms
-//     (hi + lo, together within about 2^-17 of the fp32 value); V fragments (4
-//     tokens of one channel per lane) come from the staged rows with the LDS
-//     transpose read (ds_read_b64_tr_b16).
-// Against k_attend_gqa (P.V on the vector ALU, about 500 VALU instructions
-// per 16-token tile) this leaves a tile 4 + 16 MFMAs and a few dozen VALU
-// instructions, so the waves spend their time waiting on the gather instead.
-constexpr int kPvTile = 16;
-constexpr int kPvMaxTps = 2048;
-constexpr int kPvRowBytes = 512;
-
-__device__ __forceinline__ int pv_swz(int r) { return 2 * (r & 7) | ((r >> 3) & 1); }
-
+// k_attend_pv: attend_pv_range over split blockIdx.x (tps tokens) of head tile
+// blockIdx.y of pair blockIdx.z.
 template <int HT, bool SMAP>
 __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                       const int32_t* __restrict__ slot_map,
                                                       const int32_t* __restrict__ token_idx, float* __restrict__ part,
                                                       int Hq, int Hkv, int G, int64_t N, int64_t Ns, int bs, int64_t NB,
                                                       int slots, int kt, int tps, int nsplit, int nht, float qk_scale) {
-  constexpr int D = 128, DV = 128, KS = D / 32, ROW = D + DV;  // elements per row
-  constexpr int TB = kPvTile * kPvRowBytes;                     // bytes per tile buffer
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  // the two buffers of every wave in two LDS objects, so that the compiler
-  // sees that reading one does not wait for the loads into the other
-  __shared__ __attribute__((aligned(1024))) uint8_t tA[4][TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t tB[4][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tA[4][kPvTile * kPvRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t tB[4][kPvTile * kPvRowBytes];
   __shared__ int32_t rows[4][kPvMaxTps / 4];  // wave w: its tiles' rows, tile m at [16m, 16m+16)
   __shared__ float c_lds[4][16];
   __shared__ float ml_lds[4][16][2];
-
   const int split = blockIdx.x, ht = blockIdx.y, p = blockIdx.z;
-  const int b = p / Hkv, h = p % Hkv;
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int n = lane & 15, kq = lane >> 4;
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
-  const int ntok = max(t_end - t_begin, 0);
-  const uint16_t* kvp = kv + (SMAP ? (int64_t)p * slots * bs : (int64_t)p * Ns) * ROW;
-
-  // query fragments (B of S^T): head ht*HT + n, rows past G repeat head G-1
-  u32x4 qf[KS];
-  {
-    const int g = min(ht * HT + n, G - 1);
-    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)h * G + g) * D + 8 * kq;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = ld16(qr + 32 * k);
-  }
-  // Wave w takes tiles w, w+4, .. of the split (its m-th tile: tokens
-  // 16(w+4m) ..). Each wave resolves the rows of its own tiles (-1: masked),
-  // lane L those of tiles m = L/16 (mod 4), so that it starts loading without
-  // waiting for the others; a masked token loads the wave's smallest valid
-  // row. The rows stay in the wave's part of LDS.
-  const int ntile_all = (ntok + kPvTile - 1) / kPvTile;
-  const int mt_w = ntile_all > wave ? (ntile_all - wave + 3) / 4 : 0;  // this wave's tiles
-  int32_t* rw = rows[wave];
-  uint32_t vmin = 0xFFFFFFFFu;
-  {
-    const int32_t* tix = token_idx + (int64_t)p * kt + t_begin;
-    const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
-    for (int m = lane >> 4; m < mt_w; m += 4) {
-      const int k = (wave + 4 * m) * kPvTile + (lane & 15);
-      const int tok = k < ntok ? tix[k] : -1;
-      int r = -1;
-      if (tok >= 0 && tok < N) {
-        if constexpr (SMAP) {
-          const int slot = smap[tok / bs];
-          if (slot >= 0 && slot < slots) r = slot * bs + tok % bs;
-        } else {
-          r = tok;
-        }
-      }
-      rw[m * kPvTile + (lane & 15)] = r;
-      if (r >= 0) vmin = min(vmin, (uint32_t)r);
-    }
-  }
-  const uint32_t fbu = wave_umin(vmin);
-  const int fb = fbu == 0xFFFFFFFFu ? -1 : (int)fbu;
-  const int ntw = fb < 0 ? 0 : mt_w;  // a wave without a valid row has nothing to add
-  wait_vmcnt<0>();  // q and the token lists are in: the loop's only vector loads are the direct ones
-  wave_lds_sync();
-
-  // the wave's tile m into buffer `dst`: load i fills rows 2i, 2i+1 (lanes
-  // 0-31, 32-63), lane L bringing global piece (L&31) ^ swz(row) to position L&31
-  auto issue = [&](uint8_t* dst, int m) {
-#pragma unroll
-    for (int i = 0; i < kPvTile / 2; ++i) {
-      const int r = 2 * i + (lane >> 5);
-      const int row = rw[m * kPvTile + r];
-      const int piece = (lane & 31) ^ pv_swz(r);
-      const uint16_t* src = kvp + (int64_t)(row >= 0 ? row : fb) * ROW + piece * 8;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
-    }
-  };
-
-  float m_run = -INFINITY, l_part = 0.0f;  // head n (m common over kq)
-  f32x4 o[DV / 16];
-#pragma unroll
-  for (int t = 0; t < DV / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const uint8_t* tb, int j) {
-    // ---- S^T: lane (head n, kq) gets tokens 4kq+i ----
-    u32x4 kf[KS];
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-      kf[k] = *reinterpret_cast<const u32x4*>(tb + n * kPvRowBytes + (((4 * k + kq) ^ pv_swz(n)) * 16));
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) sc = mfma16x16x32(kf[k], qf[k], sc);
-    float z[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = rw[j * kPvTile + 4 * kq + i] >= 0 ? sc[i] * qk_scale : -INFINITY;
-    const float tmax = max_rows(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-    const float m_new = fmaxf(m_run, tmax);
-    const float ref = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = exp2f(m_run - ref);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2f(z[i] - ref);
-    l_part = l_part * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-    // P as hi + lo bf16: A of the 16x16x16 product, k = token 4kq+i
-    u32x2 phi, plo;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const uint32_t h0 = f32_to_bf16_rn(pr[2 * e]), h1 = f32_to_bf16_rn(pr[2 * e + 1]);
-      const uint32_t l0 = f32_to_bf16_rn(pr[2 * e] - bf2f(h0)), l1 = f32_to_bf16_rn(pr[2 * e + 1] - bf2f(h1));
-      phi[e] = h0 | (h1 << 16);
-      plo[e] = l0 | (l1 << 16);
-    }
-    // rescale o (rows = heads 4kq+i) when a running max moved
-    if (__ballot(corr != 1.0f)) {
-      if (kq == 0) c_lds[wave][n] = corr;
-      wave_lds_sync();
-      const f32x4 cr = *reinterpret_cast<const f32x4*>(&c_lds[wave][4 * kq]);
-#pragma unroll
-      for (int t = 0; t < DV / 16; ++t) o[t] *= cr;
-      wave_lds_sync();
-    }
-    // ---- O += P V: lane a of a 16-lane group addresses row 4kq + a/4,
-    // channels 16t + 4(a%4) .. +3 (piece 16 + 2t + (a%4)/2, byte 8*(a&1)) ----
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    const int vr = 4 * kq + (n >> 2);
-    const uint8_t* vrow = tb + vr * kPvRowBytes + 8 * (n & 1);
-    const int vsw = pv_swz(vr), vp = 16 + ((n >> 1) & 1);
-    const s16x4 pa = __builtin_bit_cast(s16x4, phi), pb = __builtin_bit_cast(s16x4, plo);
-#pragma unroll
-    for (int t = 0; t < DV / 16; ++t) {
-      const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + ((vp + 2 * t) ^ vsw) * 16));
-      const s16x4 vb = __builtin_bit_cast(s16x4, v);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, o[t], 0, 0, 0);
-    }
-  };
-
-  // wave-private double buffer: the wave's even tiles in tA, odd ones in tB.
-  // The next tile's loads go out before a tile is computed and are waited
-  // for after it (with the builtin wait, which the compiler accounts for, so
-  // that reading one buffer does not also wait for the loads into the other).
-  if (ntw > 0) issue(tA[wave], 0);
-  wait_vmcnt<0>();
-  for (int m = 0; m < ntw; m += 2) {
-    if (m + 1 < ntw) issue(tB[wave], m + 1);
-    compute(tA[wave], m);
-    wait_vmcnt<0>();
-    if (m + 1 >= ntw) break;
-    if (m + 2 < ntw) issue(tA[wave], m + 2);
-    compute(tB[wave], m + 1);
-    wait_vmcnt<0>();
-  }
-  // ---- the workgroup partial: per head (m, l, -, -, o[DV]) ----
-  const float l_tot = sum_rows(l_part);
-  if (kq == 0) {
-    ml_lds[wave][n][0] = m_run;
-    ml_lds[wave][n][1] = l_tot;
-  }
-  __syncthreads();
-  // this wave's o scaled to the common max, into its own (now idle) buffer
-  // as [channel][16 heads]: one 16-byte write per lane and channel tile
-  {
-    float f[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * kq + i;
-      float ms = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][hh][0]);
-      const float mw = ml_lds[wave][hh][0];
-      f[i] = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
-    }
-    f32x4* ow = reinterpret_cast<f32x4*>(tA[wave]);
-#pragma unroll
-    for (int t = 0; t < DV / 16; ++t)
-      ow[(16 * t + n) * 4 + kq] = f32x4{f[0] * o[t][0], f[1] * o[t][1], f[2] * o[t][2], f[3] * o[t][3]};
-  }
-  __syncthreads();
-  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (DV + kPartHdr);
-  if (tid < HT) {
-    float ms = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) ms = fmaxf(ms, ml_lds[w][tid][0]);
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = ml_lds[w][tid][0];
-      l += mw == -INFINITY ? 0.0f : ml_lds[w][tid][1] * exp2f(mw - ms);
-    }
-    *reinterpret_cast<f32x4*>(dst + tid * (DV + kPartHdr)) = f32x4{ms, l, 0.0f, 0.0f};
-  }
-  // thread (channel c, heads 8*(tid/128) ..): the sum over the four waves
-  {
-    const int c = tid & (DV - 1);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int g4 = 2 * (tid >> 7) + gg;  // heads 4*g4 .. 4*g4+3
-      if (4 * g4 >= HT) continue;
-      f32x4 acc = reinterpret_cast<const f32x4*>(tA[0])[c * 4 + g4];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) acc += reinterpret_cast<const f32x4*>(tA[w])[c * 4 + g4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g4 + i < HT) dst[(4 * g4 + i) * (DV + kPartHdr) + kPartHdr + c] = acc[i];
-    }
-  }
+  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (128 + kPartHdr);
+  attend_pv_range<HT, SMAP, kPvMaxTps / 4>(q, kv, slot_map, token_idx + (int64_t)p * kt + t_begin,
+                                           max(t_end - t_begin, 0), dst, Hq, Hkv, G, N, Ns, bs, NB, slots, p, ht,
+                                           qk_scale, tA, tB, rows, c_lds, ml_lds);
 }
 
 // k_attend_mla: the latent-attention shape (K rows of 576, V = their first

@@ -27,19 +27,11 @@
 
 #include "tls_dev.h"
 #include "tls_launch.h"
+#include "tls_select_dev.h"
 
 namespace tls {
 
 // ----------------------------------------------------------- block scores --
-// q+ and q- of one A fragment: per 16-bit half, sign set -> negative part.
-__device__ __forceinline__ void split_sign(u32x4 raw, u32x4& pos, u32x4& neg) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t mask = ((raw[e] >> 15) & 0x00010001u) * 0xFFFFu;
-    neg[e] = raw[e] & mask;
-    pos[e] = raw[e] & ~mask;
-  }
-}
 
 // Streaming scorer for small head groups (G <= 48): every summary byte is used
 // by at most three 16-row MFMA tiles, so the kernel is a plain HBM stream.
@@ -358,220 +350,6 @@ hipError_t launch_score_blocks(const BlockScoreArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ top-k --
-// Exact top-k of one row per workgroup of NT threads (256, 512 or 1024);
-// keys in registers, thread t owning elements [t*PER, t*PER+PER). Invalid
-// elements carry key 0, below every valid key.
-constexpr int kTopkThreads = 1024;  // the largest workgroup: 16 keys per thread up to 16384
-constexpr int kTopkChunk = 16384;   // the most keys one workgroup selects from
-
-template <int NT>
-struct alignas(16) TopkLds {
-  uint32_t hist[3][256];  // pass i counts into hist[i % 3]
-  uint32_t red[3][NT / 64];
-  uint32_t scan[NT / 64];
-};
-
-// Block-wide exclusive scan of one uint32 per thread; returns the prefix.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh /* one per wave */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
-  if (lane == 63) sh[wave] = x;
-  lds_sync();
-  uint32_t before = 0u;
-  for (int w = 0; w < wave; ++w) before += sh[w];
-  return before + x - v;
-}
-
-// The bin of a 256-bin histogram that holds the krem-th largest key: every
-// wave reads the whole histogram and finds it on its own (wave-uniform
-// results, no LDS round trip). Lane l holds bins 255-4l .. 252-4l, so an
-// exclusive prefix scan over lanes counts the keys in the bins above.
-struct BinPick {
-  uint32_t bin, above, count;
-};
-__device__ __forceinline__ BinPick pick_bin(const uint32_t* hist, uint32_t krem) {
-  const int lane = threadIdx.x & 63;
-  const int b0 = 252 - 4 * lane;
-  const u32x4 hb = *reinterpret_cast<const u32x4*>(&hist[b0]);
-  const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
-  const uint32_t above = wave_incl_scan(mine) - mine;
-  const uint64_t hit = __ballot(above < krem && krem <= above + mine);
-  const int L = __builtin_ctzll(hit);  // the lane whose 4 bins hold it (one exists: krem <= keys in range)
-  uint32_t bin = 0u, ab = 0u, cnt = 0u, run = above;
-#pragma unroll
-  for (int i = 3; i >= 0; --i) {
-    if (run < krem && krem <= run + hb[i]) {  // true for exactly one bin of lane L
-      bin = (uint32_t)(b0 + i);
-      ab = run;
-      cnt = hb[i];
-    }
-    run += hb[i];
-  }
-  return BinPick{readlane(bin, L), readlane(ab, L), readlane(cnt, L)};
-}
-
-// Selects the K largest keys (ties: lower element index first) and writes
-// their ids ascending to out[0..min(K, valid)), then -1 up to out_len.
-// Radix select. The first pass bins the keys' float values linearly between
-// the smallest and the largest (a monotone map, so a bin holds one interval
-// of keys; binning the raw keys instead would put every float of one binade
-// into a single bin). The later passes histogram (key - lo) >> shift, the next
-// 8 bits below the top set bit of (hi - lo), over the keys left in [lo, hi].
-// The search stops as soon as the chosen bin is taken whole, with the
-// threshold at the bin's lower edge and every key equal to it kept. One
-// barrier per pass: the histograms rotate over three buffers (a buffer is
-// cleared two passes after its last read), and every wave picks the bin.
-template <int PER, int NT>
-__device__ void block_topk(const uint32_t (&key)[PER], const int32_t (&id)[PER], uint32_t K, int32_t* out,
-                           int out_len, TopkLds<NT>& sh, uint32_t* out_key = nullptr) {
-  constexpr int kWaves = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nval = 0u;
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (key[e] != 0u) {
-      kmin = min(kmin, key[e]);
-      kmax = max(kmax, key[e]);
-      ++nval;
-    }
-  kmin = wave_umin(kmin);
-  kmax = wave_umax(kmax);
-  nval = wave_usum(nval);
-  if (lane == 0) {
-    sh.red[0][wave] = kmin;
-    sh.red[1][wave] = kmax;
-    sh.red[2][wave] = nval;
-  }
-  for (int i = tid; i < 512; i += NT) sh.hist[i >> 8][i & 255] = 0u;  // buffers 0 and 1
-  lds_sync();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u, total = 0u;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    lo = min(lo, sh.red[0][w]);
-    hi = max(hi, sh.red[1][w]);
-    total += sh.red[2][w];
-  }
-  const uint32_t kk = K < total ? K : total;
-  uint32_t thr = 0u, krem = 0u;  // kk == total: keep every valid element
-  if (kk < total) {
-    krem = kk;
-    bool done = false;
-    int pass = 0;  // histogram buffer = pass % 3; pass p clears buffer (p + 1) % 3
-    const float vlo = key_float(lo), vhi = key_float(hi);
-    const float sc = 256.0f / (vhi - vlo);
-    if (hi > lo && sc > 0.0f && sc < INFINITY) {
-      uint32_t bin[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float x = key[e] != 0u ? (key_float(key[e]) - vlo) * sc : 0.0f;  // in [0, 256]
-        bin[e] = min((uint32_t)x, 255u);
-        if (key[e] != 0u) atomicAdd(&sh.hist[0][bin[e]], 1u);
-      }
-      if (tid < 256) sh.hist[2][tid] = 0u;  // (buffer 1 was cleared at the start)
-      lds_sync();
-      const BinPick pk = pick_bin(sh.hist[0], krem);
-      pass = 1;
-      const uint32_t d = pk.bin;
-      krem -= pk.above;
-      // keys of bin d: one interval [lo, hi] (a block reduction; its barrier
-      // also orders this pass's histogram reads before buffer 0 is cleared)
-      kmin = 0xFFFFFFFFu;
-      kmax = 0u;
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        if (key[e] != 0u && bin[e] == d) {
-          kmin = min(kmin, key[e]);
-          kmax = max(kmax, key[e]);
-        }
-      kmin = wave_umin(kmin);
-      kmax = wave_umax(kmax);
-      if (lane == 0) {
-        sh.red[0][wave] = kmin;
-        sh.red[1][wave] = kmax;
-      }
-      lds_sync();
-      lo = 0xFFFFFFFFu;
-      hi = 0u;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        lo = min(lo, sh.red[0][w]);
-        hi = max(hi, sh.red[1][w]);
-      }
-      if (krem == pk.count) {
-        // the whole bin is taken: the threshold is its smallest key
-        thr = lo;
-        krem = 0xFFFFFFFFu;
-        done = true;
-      }
-    }
-    while (!done && hi > lo) {
-      const uint32_t diff = hi - lo;
-      const int nbits = 32 - __clz(diff);
-      const int shift = nbits > 8 ? nbits - 8 : 0;
-      uint32_t* hcur = sh.hist[pass % 3];
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        if (key[e] >= lo && key[e] <= hi) atomicAdd(&hcur[(key[e] - lo) >> shift], 1u);
-      if (tid < 256) sh.hist[(pass + 1) % 3][tid] = 0u;  // last read two barriers ago
-      lds_sync();
-      const BinPick pk = pick_bin(hcur, krem);
-      ++pass;
-      const uint32_t d = pk.bin;
-      krem -= pk.above;
-      const uint32_t nlo = lo + (d << shift);
-      if (krem == pk.count) {
-        // the whole bin is taken: every key in it is >= nlo and every key
-        // of a lower bin is < nlo
-        thr = nlo;
-        krem = 0xFFFFFFFFu;
-        done = true;
-        break;
-      }
-      const uint32_t span = shift == 0 ? 0u : ((1u << shift) - 1u);
-      hi = (hi - nlo) > span ? nlo + span : hi;
-      lo = nlo;
-    }
-    if (!done) thr = lo;
-  }
-// Elements above the threshold, plus the first krem equal to it (index
-// order), placed by one block-wide scan into an LDS row that goes out in
-// coalesced stores (placing straight into global memory would scatter every
-// store instruction over the wave's whole output range).
-  __shared__ uint32_t stage[NT * PER];
-  uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    gt += (key[e] > thr) ? 1u : 0u;
-    eq += (key[e] == thr && key[e] != 0u) ? 1u : 0u;
-  }
-  const uint32_t pre = block_exclusive_scan(gt | (eq << 16), sh.scan);
-  auto place = [&](bool ids) {
-    uint32_t eq_before = pre >> 16;
-    uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      bool take = key[e] > thr;
-      if (key[e] == thr && key[e] != 0u) {
-        take = eq_before < krem;
-        ++eq_before;
-      }
-      if (take) {
-        if (pos < kk) stage[pos] = ids ? (uint32_t)id[e] : key[e];  // never more than kk entries
-        ++pos;
-      }
-    }
-  };
-  place(true);
-  lds_sync();
-  for (int i = tid; i < out_len; i += NT) out[i] = i < (int)kk ? (int32_t)stage[i] : -1;
-  if (out_key) {
-    lds_sync();
-    place(false);
-    lds_sync();
-    for (int i = tid; i < out_len; i += NT) out_key[i] = i < (int)kk ? stage[i] : 0u;  // key 0: no element
-  }
-}
 
 // Top-Kb of the block scores of one pair per workgroup.
 template <int PER, int NT>
@@ -589,7 +367,8 @@ __global__ __launch_bounds__(NT) void k_topk_blocks(const float* __restrict__ S,
     id[e] = c;
     key[e] = c < n ? order_key(v[e]) : 0u;
   }
-  block_topk<PER, NT>(key, id, (uint32_t)K, out + (int64_t)row * K, K, sh);
+  __shared__ uint32_t stage[NT * PER];
+  block_topk<PER, NT>(key, id, (uint32_t)K, out + (int64_t)row * K, K, sh, stage);
 }
 
 // ----------------------------------------------------------- token stage --
@@ -661,114 +440,6 @@ __device__ __forceinline__ void unit_loads(UnitLoads<UT>& L, const int32_t* bidx
   }
 }
 
-// A fragments of q on the label channels, in two steps so that the gathers
-// can be issued long before the fragments are needed. The workgroup of 256
-// threads gathers the matrix of q on the label channels once (MT*16 rows x 32
-// channel slots; rows past G repeat head G-1, so the maximum over all rows is
-// the heads' maximum; slots past r are zero) and shares it through LDS: every
-// wave needs all of it, and a wave gathering it alone makes MT*8 two-byte
-// loads per lane at 64 scattered addresses each (for 128 heads the gathers
-// alone kept a wave busy for about 6 us). Thread t gathers slot t%32 of rows
-// t/32 + 8k (label_q_issue, into registers); label_q_finish writes them to
-// LDS and reads the fragments back with one 16-byte read per tile from rows
-// of 80 bytes (16 rows at distinct bank offsets).
-// Plain form: lane (n, kq) of tile m holds head m*16 + n on channels 8kq ..
-// 8kq+7. Folded form (G <= 8, one tile): lane (n, kq) holds head n&7 of half
-// n>>3 on k = 8kq .. 8kq+7; half 0 takes channels 0-15 on k 0-15 and half 1
-// the same channels on k 16-31, the other quarter of each row is zero.
-constexpr int kLabRow = 40;  // uint16 per LDS row: 32 channels and 16 bytes of padding
-
-template <int MT>
-__device__ __forceinline__ void label_q_issue(uint32_t (&hl)[2 * MT], const int32_t* lab, const uint16_t* qp, int G,
-                                              int D, int r) {
-  const int t = threadIdx.x, i = t & 31;
-  const int li = lab[min(i, r - 1)];
-#pragma unroll
-  for (int k = 0; k < 2 * MT; ++k) hl[k] = qp[(int64_t)min((t >> 5) + 8 * k, G - 1) * D + li];
-}
-
-template <int MT, bool FOLD>
-__device__ __forceinline__ void label_q_finish(u32x4 (&qa)[MT], const uint32_t (&hl)[2 * MT], uint16_t* sq, int r) {
-  const int t = threadIdx.x, i = t & 31;
-  const int lane = t & 63, n = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int k = 0; k < 2 * MT; ++k) sq[((t >> 5) + 8 * k) * kLabRow + i] = i < r ? (uint16_t)hl[k] : (uint16_t)0;
-  lds_sync();
-  if constexpr (FOLD) {
-    static_assert(MT == 1, "folded scores: one head tile");
-    const u32x4 v = *reinterpret_cast<const u32x4*>(&sq[(n & 7) * kLabRow + 8 * (kq & 1)]);
-    const bool mine = (kq >> 1) == (n >> 3);
-    qa[0] = mine ? v : u32x4{0u, 0u, 0u, 0u};
-  } else {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) qa[m] = *reinterpret_cast<const u32x4*>(&sq[(m * 16 + n) * kLabRow + 8 * kq]);
-  }
-}
-
-// Eight INT4 codes (one byte per channel pair, low nibble first) widened to
-// bf16, exact: the B fragment of one lane.
-__device__ __forceinline__ u32x4 codes_to_bf16(uint32_t w) {
-  u32x4 bop;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int lo4 = (int)(w << (28 - 8 * e)) >> 28;  // channel 2e of the word
-    const int hi4 = (int)(w << (24 - 8 * e)) >> 28;  // channel 2e + 1
-    bop[e] = (__float_as_uint((float)lo4) >> 16) | (__float_as_uint((float)hi4) & 0xFFFF0000u);
-  }
-  return bop;
-}
-
-// ---- folded scores: up to 8 heads on 8 or 16 label channels, blocks of 64 ----
-// One 16x16x32 MFMA carries two tiles of 16 candidates: rows 0-7 are the
-// heads on k 0-15 (tile X's channels), rows 8-15 the same heads on k 16-31
-// (tile Y's); B holds tile X's codes on k 0-15 and tile Y's on k 16-31.
-// With G <= 8 and r <= 16 none of the product is padding, so every lane
-// unpacks codes that count (a plain tile leaves half of k and half of the
-// rows empty, and its lanes unpack zeros). A group of 64 candidates is one
-// whole block: its codes and scales sit at a block-uniform offset (scalar)
-// plus a per-lane constant, so the loads need no per-candidate address
-// arithmetic. Rows past G repeat head G-1, which leaves every maximum as it is.
-// NG groups of 64 candidates from candidate c0 (a multiple of 64): val[g] is
-// the score of candidate cand[g] (0 if it does not exist). Lane (n, kq) ends
-// with tile 2(kq&1) + (kq>>1) of its group: the MFMA of tiles 0/1 leaves
-// tile 0 on rows 0-1 and tile 1 on rows 2-3, the one of tiles 2/3 likewise,
-// and one 16-lane swap of the two (odd rows of the first with even rows of the
-// second) pairs each tile's two row halves. `bidx` is the pair's block list.
-template <int RB, int NG>
-__device__ __forceinline__ void fold_unit(float (&val)[NG], int (&cand)[NG], const int32_t* bidx,
-                                          __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int c0, int kb,
-                                          int64_t N, u32x4 qa) {
-  const int lane = threadIdx.x & 63, n = lane & 15, kq = lane >> 4;
-  const int tile = 2 * (kq & 1) + (kq >> 1);
-  const int voff = (n + 16 * (kq >> 1)) * RB + 4 * (kq & 1);  // tiles 0/1; +32 rows for tiles 2/3
-  uint32_t cwa[NG], cwb[NG];
-  float tsc[NG];
-  int tok0[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int blk = c0 / 64 + g;
-    tok0[g] = __builtin_amdgcn_readfirstlane(blk < kb ? bidx[blk] : 0) * 64;
-  }
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    cwa[g] = __builtin_amdgcn_raw_buffer_load_b32(cr, voff, tok0[g] * RB, 0);
-    cwb[g] = __builtin_amdgcn_raw_buffer_load_b32(cr, voff + 32 * RB, tok0[g] * RB, 0);
-    tsc[g] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (16 * tile + n) * 4, tok0[g] * 4, 0));
-  }
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const f32x4 a = mfma16x16x32(qa, codes_to_bf16(cwa[g]), f32x4{0.f, 0.f, 0.f, 0.f});
-    const f32x4 c = mfma16x16x32(qa, codes_to_bf16(cwb[g]), f32x4{0.f, 0.f, 0.f, 0.f});
-    const float xa = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-    const float xc = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
-    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xa), __float_as_uint(xc), false, false);
-    const float best = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    const int within = 16 * tile + n;
-    const bool ok = c0 / 64 + g < kb && (int64_t)tok0[g] + within < N;
-    val[g] = ok ? tsc[g] * best : 0.0f;
-    cand[g] = c0 + 64 * g + within;
-  }
-}
 
 // Scores of the unit: val[j] for candidate c0 + 64j + lane (0 if it does not
 // exist).
@@ -892,6 +563,7 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
                                                           int Hq, int Hkv, int G, int D, int64_t N, int64_t Ns, int bs,
                                                           int bsh, int r, int kb) {
   __shared__ TopkLds<256> sh;
+  __shared__ uint32_t stage[256 * PERB];
   __shared__ int32_t sblk[kSelMaxBlocks];
   const int p = blockIdx.y, tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
@@ -917,7 +589,7 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
       id[e] = c;
       key[e] = (e < per && c < NB) ? order_key(v[e]) : 0u;
     }
-    block_topk<PERB, 256>(key, id, (uint32_t)kb, sblk, kb, sh);
+    block_topk<PERB, 256>(key, id, (uint32_t)kb, sblk, kb, sh, stage);
   }
   lds_sync();
   if (blockIdx.x == 0)
@@ -966,7 +638,8 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(const float* __restrict__ A,
     key[e] = ok ? order_key(v[e]) : 0u;
     id[e] = ok ? (int32_t)t : -1;
   }
-  block_topk<PER, NT>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh);
+  __shared__ uint32_t stage[NT * PER];
+  block_topk<PER, NT>(key, id, (uint32_t)kt, token_idx + (int64_t)p * kt, kt, sh, stage);
 }
 
 // More candidates than one workgroup holds (16384): an exact top-k in passes.
@@ -1007,7 +680,8 @@ __global__ __launch_bounds__(NT) void k_topk_tokens_chunk(const float* __restric
     id[e] = ok ? (int32_t)t : -1;
   }
   const int64_t o = (int64_t)p * ostride + (int64_t)ch * kt;
-  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, okey + o);
+  __shared__ uint32_t stage[NT * PER];
+  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, stage, okey + o);
 }
 
 // A later pass: chunk blockIdx.x of the (key, id) list of pair blockIdx.y.
@@ -1031,7 +705,8 @@ __global__ __launch_bounds__(NT) void k_topk_lists(const uint32_t* __restrict__ 
     id[e] = ok ? iid[j] : -1;
   }
   const int64_t o = (int64_t)p * ostride + (int64_t)ch * kt;
-  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, okey ? okey + o : nullptr);
+  __shared__ uint32_t stage[NT * PER];
+  block_topk<PER, NT>(key, id, (uint32_t)kt, oid + o, kt, sh, stage, okey ? okey + o : nullptr);
 }
 
 static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((unsigned)bs) : -1; }

@@ -108,8 +108,34 @@ size_t ws_bytes(const Derived& d, int which) {
       plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
       return round_up(pl.part_bytes);
     }
+    case TLS_WS_STEP: {
+      if (!step_supported(d.G, d.D, d.DV, d.v_off == 0, d.bs, d.r, d.NB, d.kb, d.kt)) return 0;
+      StepPlan pl;
+      plan_step(d.pairs, kMaxXcd, d.NB, d.kb, &pl);  // (the sizes do not depend on the XCD count)
+      return round_up(pl.state_words * 4) + round_up((size_t)d.pairs * d.NB * 4) +
+             round_up((size_t)d.pairs * pl.kstride * 4) + round_up((size_t)d.pairs * 4 * 4) +
+             round_up((size_t)d.pairs * pl.nC * 2 * 4) + round_up(pl.part_floats * 4);
+    }
     default: return 0;
   }
+}
+
+// XCDs (L2 domains) and compute units of the current device, queried once
+// per device.
+static void device_layout(int* nx, int* ncu) {
+  static std::atomic<int> cache_nx[64], cache_cu[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int x = cache_nx[dev].load(std::memory_order_relaxed), c = cache_cu[dev].load(std::memory_order_relaxed);
+  if (x == 0 || c == 0) {
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x < 1) x = 1;
+    if (x > kMaxXcd) x = kMaxXcd;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 1;
+    cache_nx[dev].store(x, std::memory_order_relaxed);
+    cache_cu[dev].store(c, std::memory_order_relaxed);
+  }
+  *nx = x;
+  *ncu = c;
 }
 
 }  // namespace tls
@@ -263,6 +289,90 @@ int tls_select(const tls_shape_t* shape, const void* q, const void* summ, const 
   if (e != hipSuccess) return hip_error(e, "topk(blocks) launch");
   e = launch_select_tokens(a, A, st);
   return e == hipSuccess ? TLS_OK : hip_error(e, "select_tokens launch");
+}
+
+int tls_decode_step(const tls_shape_t* shape, const void* q, const void* summ, const int32_t* label_ch,
+                    const uint8_t* codes, const float* scale, const void* kv, int32_t* block_idx, int32_t* token_idx,
+                    float* out, float* lse_opt, void* ws, size_t ws_len, void* stream) {
+  clear_error();
+  Derived d;
+  int rc = derive(shape, &d);
+  if (rc) return rc;
+  if (!q || !summ || !label_ch || !codes || !scale || !kv || !block_idx || !token_idx || !out)
+    return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(q, 16) || !aligned(summ, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(scale, 4) ||
+      !aligned(codes, 4))
+    return set_error(TLS_ERR_INVALID_ARG, "q, summ, kv and out must be 16-byte aligned, codes and scale 4-byte");
+  if (!step_supported(d.G, d.D, d.DV, d.v_off == 0, d.bs, d.r, d.NB, d.kb, d.kt))
+    return set_error(TLS_ERR_UNSUPPORTED,
+                     "tls_decode_step covers D = DV = 128 with separate V, G <= 8, block size 64, 8 or 16 label "
+                     "channels, NB <= 4096 and Kb' <= 128 (use tls_select and tls_sparse_decode)");
+  if ((int64_t)d.Ns * (d.r / 2) > 0x7FFFFFFF)
+    return set_error(TLS_ERR_UNSUPPORTED, "label cache of a sequence above 2 GiB");
+  const size_t need = ws_bytes(d, TLS_WS_STEP);
+  if (!ws || ws_len < need) return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return set_error(TLS_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  int nx = 1, ncu = 1;
+  device_layout(&nx, &ncu);
+  StepPlan pl;
+  plan_step(d.pairs, nx, d.NB, d.kb, &pl);
+  char* w = (char*)ws;
+  StepArgs a;
+  a.q = (const uint16_t*)q;
+  a.summ = (const uint16_t*)summ;
+  a.label_ch = label_ch;
+  a.codes = codes;
+  a.scale = scale;
+  a.kv = (const uint16_t*)kv;
+  a.block_idx = block_idx;
+  a.token_idx = token_idx;
+  a.out = out;
+  a.lse = lse_opt;
+  a.state = (int*)w;
+  a.ring = a.state + pl.ring_off;
+  a.hist = (uint32_t*)(a.state + pl.hist_off);
+  w += round_up(pl.state_words * 4);
+  a.S = (float*)w;
+  w += round_up((size_t)d.pairs * d.NB * 4);
+  a.K = (uint32_t*)w;
+  w += round_up((size_t)d.pairs * pl.kstride * 4);
+  a.cut_info = (int*)w;
+  w += round_up((size_t)d.pairs * 4 * 4);
+  a.chunk_info = (int*)w;
+  w += round_up((size_t)d.pairs * pl.nC * 2 * 4);
+  a.part = (float*)w;
+  a.pairs = d.pairs;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.r = d.r;
+  a.kb = d.kb;
+  a.kt = d.kt;
+  a.N = d.N;
+  a.Ns = d.Ns;
+  a.NB = d.NB;
+  a.NBs = d.NBs;
+  a.qk_scale = d.sm * 1.4426950408889634f;
+  a.nx = pl.nx;
+  a.nA = pl.nA;
+  a.nT = pl.nT;
+  a.nsplit = pl.nC;
+  a.ring_cap = pl.ring_cap;
+  a.kstride = pl.kstride;
+  hipError_t e = launch_step(a, 2 * ncu, (hipStream_t)stream);
+  return e == hipSuccess ? TLS_OK : hip_error(e, "decode_step launch");
+}
+
+int tls_decode_step_status(void* ws, void* stream) {
+  clear_error();
+  if (!ws) return set_error(TLS_ERR_INVALID_ARG, "NULL workspace");
+  int err = 0;
+  hipError_t e = hipMemcpyAsync(&err, ws, sizeof err, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_error(e, "decode_step status read");
+  if (err & 1) return set_error(TLS_ERR_STATE, "an attention item was not published in time (error word %d)", err);
+  if (err) return set_error(TLS_ERR_STATE, "a queue was left undrained (error word %d)", err);
+  return TLS_OK;
 }
 
 int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,

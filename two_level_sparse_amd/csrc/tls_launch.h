@@ -121,4 +121,43 @@ hipError_t launch_gather_blocks(const uint16_t* host_kv_dev, uint16_t* dev_cache
                                 hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t st);
 
+// One whole decode step in one launch (k_step.hip): 128-channel GQA rows,
+// G <= 8, blocks of 64, 8 or 16 label channels, NB <= 4096, Kb' <= 128.
+constexpr int kMaxXcd = 16;       // XCDs the state area has queues for
+constexpr int kStepChunk = 512;   // candidates per attention item
+struct StepArgs {
+  const uint16_t* q;
+  const uint16_t* summ;
+  const int32_t* label_ch;
+  const uint8_t* codes;
+  const float* scale;
+  const uint16_t* kv;
+  int32_t* block_idx;  // [pairs, kb]
+  int32_t* token_idx;  // [pairs, kt]
+  float* out;
+  float* lse;          // may be NULL
+  float* S;            // [pairs, NB] block scores
+  uint32_t* K;         // [pairs, kstride] candidate order keys
+  uint32_t* hist;      // [pairs, 4096] histograms of the keys' top bits, inside the state area
+  int* cut_info;       // [pairs, 4] threshold key, threshold-equal keys kept, kept count
+  int* chunk_info;     // [pairs, nsplit, 2] kept and threshold-equal keys before each chunk
+  float* part;         // [pairs, nsplit, 8, 132] partials
+  int* state;          // zero at rest
+  int* ring;           // [nx, ring_cap], inside the state area
+  int pairs, Hq, Hkv, G, r, kb, kt;
+  int64_t N, Ns, NB, NBs;
+  float qk_scale;
+  int nx, nA, nT, nsplit, ring_cap, kstride;
+};
+struct StepPlan {
+  int nx, nA, nT, nC, pert, kstride, ring_cap;
+  size_t ring_off;     // int32 words before the rings in the state area
+  size_t hist_off;     // int32 words before the key histograms in the state area
+  size_t state_words;  // int32 words of the state area (rings included; the same for any nx)
+  size_t part_floats;
+};
+bool step_supported(int G, int D, int DV, bool v_is_k_prefix, int bs, int r, int64_t NB, int kb, int kt);
+void plan_step(int pairs, int nx, int64_t NB, int kb, StepPlan* plan);
+hipError_t launch_step(const StepArgs& a, int grid, hipStream_t st);
+
 }  // namespace tls
