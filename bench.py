@@ -14,9 +14,13 @@ Cache left there by the previous step (R * touched bytes >= 1 GiB). Each timed
 step replays a HIP graph captured from the step's library calls (no host
 launch cost in the timed region; --no-graph launches them one by one).
 
-Prints one JSON line: queries/sec (= batch / step time), the HBM roofline of
-the dominant kernel (attention; the library records HIP events around each
-of its launches on the stream it runs on) and the fp64 oracle timed on host cores over a bounded
+Prints one JSON line: queries/sec (= batch / step time); the HBM roofline of
+the whole step (algorithmic bytes per step / step time), with the dominant
+kernel (attention; the library records HIP events around each of its launches
+on the stream it runs on) as a labelled sub-field, against HBM for the GQA
+kernels and against the bf16 MFMA peak for the latent-attention kernel; the
+index build (summaries and INT4 label cache, once per cache, outside the step)
+timed on its own; and the fp64 oracle timed on host cores over a bounded
 sample of pairs as the CPU baseline.
 """
 from __future__ import annotations
@@ -65,21 +69,39 @@ def attention_kernel(s):
     return "k_attend_gqa" if s.D <= 128 else "k_attend"
 
 
-def measured_traffic(config):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when the attention kernel source changed since the counters were taken."""
+def kernel_source_sha():
+    """Digest of every kernel source (the .hip files and their device headers):
+    a counter summary is valid only for the sources it was taken with."""
     import hashlib
+    h = hashlib.sha256()
+    csrc = ROOT / "two_level_sparse_amd" / "csrc"
+    for f in sorted(list(csrc.glob("*.hip")) + list(csrc.glob("*_dev.h")) + [csrc / "tls_dev.h"]):
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, key):
+    """HBM bytes (counters FETCH_SIZE + WRITE_SIZE, calibrated) per step
+    (key "step_traffic_bytes") or per attention launch ("attention_traffic_bytes")
+    from the committed counter summary, or None when a kernel source changed
+    since the counters were taken."""
     prof = ROOT / "profiles" / f"traffic_{config}.txt"
-    src = ROOT / "two_level_sparse_amd" / "csrc" / "k_decode.hip"
     if not prof.exists():
         return None
-    sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    sha = kernel_source_sha()
     for line in prof.read_text().splitlines():
-        if line.startswith("attention_traffic_bytes="):
+        if line.startswith(key + "="):
             kv = dict(tok.split("=") for tok in line.split())
             if kv.get("source_sha256_prefix") == sha:
-                return int(kv["attention_traffic_bytes"])
+                return int(kv[key])
     return None
+
+
+def attention_flops(s):
+    """Multiply-adds x 2 of the attention over the kept tokens: q.K (D) and P.V (DV) per head and token."""
+    kt = min(s.Kt, min(s.Kb, s.NB) * s.bs)
+    return 2.0 * s.pairs * s.G * kt * (s.D + s.DV)
 
 
 class TimingEvent:
@@ -142,6 +164,27 @@ def block_scorer_mfma(s, dec, qs, caches, stream, reps=20):
                      "mfma_util": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                      "GBps": round(summ_bytes / us / 1e3, 1)}
     return out
+
+
+def build_time(s, cache, reps=5):
+    """The index build (tls_build_summaries: key max/min per block and the INT4
+    label cache, once per cache, outside the decode step) timed on its own with
+    events: bytes = every key row read once + summaries, codes and scales written."""
+    import torch
+    kb = s.pairs * s.N * s.D * 2  # the K half of every row (the label pass reads only label channels of it)
+    written = s.pairs * (s.NB * 2 * s.D * 2 + s.N * (s.r // 2) + s.N * 4)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cache.build()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        cache.build()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    return {"kernel": "k_build", "us": round(us, 1), "bytes": kb + written,
+            "GBps": round((kb + written) / us / 1e3, 1), "frac": round((kb + written) / us / 1e3 / HBM_PEAK_GBS, 4),
+            "note": "once per cache, excluded from the per-step rate"}
 
 
 class DenseDecoder:
@@ -209,7 +252,6 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = enough for 1 GiB)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps one call at a time instead of replaying a captured HIP graph per step")
-    ap.add_argument("--chunks", type=int, default=1, help="batch chunks pipelined on separate streams")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 256 MiB device copy before timing (counter calibration for profiles)")
@@ -232,7 +274,7 @@ def main():
     import torch
 
     import two_level_sparse_amd as T
-    from two_level_sparse_amd.runtime import Cache, Decoder, PipelinedDecoder, bf16
+    from two_level_sparse_amd.runtime import Cache, Decoder, bf16
 
     T.load_library()
     s = W.CONFIGS[args.config]
@@ -266,7 +308,7 @@ def main():
     if args.mode == "dense":
         dec = DenseDecoder(s)
     else:
-        dec = PipelinedDecoder(s, args.chunks) if args.chunks > 1 else Decoder(s)
+        dec = Decoder(s)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -285,15 +327,10 @@ def main():
         stream.wait_stream(side)
         torch.cuda.synchronize()
 
-    pipelined = args.chunks > 1
-
     def one_step(i, ev=None, eager=False):
         r = i % R
         if graphs is not None and not eager:
             graphs[r].replay()
-            return
-        if pipelined:
-            dec.step(qs[r], caches[r])
             return
         if args.mode != "dense":
             dec.select(qs[r], caches[r])
@@ -339,28 +376,44 @@ def main():
     # around it on its stream, over further steps launched one call at a time
     # on the same rotating caches. A spin kernel first lets the host queue all
     # of them, so the GPU runs them back to back as in the timed replays.
-    dec_ms, scorer, how = None, None, None
-    if not pipelined:
-        P = max(20, 2 * R) if args.mode != "dense" else 5
-        evs = [(TimingEvent(), TimingEvent()) for _ in range(P)]
-        torch.cuda._sleep(int(2e7))
-        for i in range(P):
-            one_step(i, evs[i], eager=True)
-        torch.cuda.synchronize()
-        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        how = "timing-only HIP events (no system-scope fence) recorded by the library around each attention launch, steps queued behind a spin kernel"
-        if args.mode != "dense":
-            scorer = block_scorer_mfma(s, dec, qs, caches, stream)
+    scorer = None
+    P = max(20, 2 * R) if args.mode != "dense" else 5
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(P)]
+    torch.cuda._sleep(int(2e7))
+    for i in range(P):
+        one_step(i, evs[i], eager=True)
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    how = ("timing-only HIP events (no system-scope fence) recorded by the library around each attention "
+           "launch, steps queued behind a spin kernel")
+    if args.mode != "dense":
+        scorer = block_scorer_mfma(s, dec, qs, caches, stream)
 
-    roof = None
-    if dec_ms:
-        ach = ab["attention"] / (dec_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": f"{attention_kernel(s)} (attention of tls_sparse_decode)",
-                "achieved": round(ach, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(s.name) if args.mode == "tls" else None,
-                "launch_us": round(dec_ms * 1e3, 2), "bytes_per_launch": ab["attention"],
-                "timing": how}
+    # the whole step against HBM: algorithmic bytes per step / step time
+    ach_step = ab["total"] / step_s / 1e9
+    roof = {"bound": "hbm", "kernel": "whole step (every kernel of one step, replayed as one graph)",
+            "achieved": round(ach_step, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach_step / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(s.name, "step_traffic_bytes") if args.mode == "tls" else None,
+            "bytes_per_step": ab["total"], "step_us": round(step_s * 1e6, 2),
+            "timing": "events around the timed graph replays (inter-kernel gaps included)"}
+    if dec_ms:  # the dominant kernel, attention
+        kname = attention_kernel(s)
+        dk = {"kernel": f"{kname} (attention of tls_sparse_decode)", "launch_us": round(dec_ms * 1e3, 2),
+              "bytes_per_launch": ab["attention"], "timing": how}
+        gbs = ab["attention"] / (dec_ms / 1e3) / 1e9
+        if kname == "k_attend_mla":
+            # both products on MFMA, 128 heads on one latent row: bound by the matrix cores
+            tfl = attention_flops(s) / (dec_ms / 1e3) / 1e12
+            dk.update({"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "flops_per_launch": attention_flops(s),
+                       "hbm": {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+        else:
+            dk.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        dk["traffic"] = measured_traffic(s.name, "attention_traffic_bytes") if args.mode == "tls" else None
+        roof["dominant_kernel"] = dk
 
     res = {
         "metric": METRIC,
@@ -377,7 +430,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{s.name}: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim {s.D}/{s.DV}, "
                                f"context {s.N}, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, {s.r} INT4 label channels",
-                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs), "chunks": args.chunks,
+                   "batch": s.B, "ctx_len": s.N, "rotation": R, "graph": bool(graphs),
                    "mode": args.mode},
         "hbm": {"algorithmic_bytes_per_step": ab["total"],
                 "achieved_GBps": round(ab["total"] / step_s / 1e9, 1),
@@ -385,6 +438,7 @@ def main():
         "roofline": roof,
         "ms_per_step_median_of_5_windows": round(ms_median, 5),
         "block_scorer": scorer,
+        "index_build": build_time(s_data, base) if args.mode != "dense" else None,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu and args.mode == "tls":

@@ -192,6 +192,46 @@ def test_device_planning_rejects_an_invalid_selection():
     sd.close()
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_host_planning_rejects_an_invalid_selection_before_changing_state(mode):
+    """Host-planned modes: M_t valid for pair 0 but not for pair 1 -- the call
+    fails and changes nothing, so retrying the step with a valid M_t gives what
+    a fresh context gives for it (transfers, slot maps, blocks moved)."""
+    import two_level_sparse_amd as T
+    s, q0, sd_a = small_context()
+    _, _, sd_b = small_context()
+    pro = to_np(sd_a.selection(-1)).reshape(s.pairs, -1)
+    good = pro.copy()
+    for p in range(s.pairs):  # one block of each pair's set replaced by one outside it
+        outside = np.setdiff1d(np.arange(s.NB), pro[p])
+        good[p, -1] = outside[-1]
+        good[p] = np.sort(good[p])
+    bad = good.copy()
+    bad[1, 0] = -5
+    for sd in (sd_a, sd_b):
+        T.tls_offload_set_copy_mode(sd.ctx, mode)
+    ev = torch.cuda.Event()
+    ev.record()  # creates the HIP event
+    dgood = torch.from_numpy(good.astype(np.int32)).cuda()
+    dbad = torch.from_numpy(bad.astype(np.int32)).cuda()
+    torch.cuda.synchronize()
+    with pytest.raises(T.TlsError) as ei:
+        T.tls_prefetch_delta(sd_a.ctx, 0, dbad, sd_a.side, ev)
+    assert ei.value.code == T.TLS_ERR_STATE
+    assert sd_a.total_copied() == 0
+    n_a = T.tls_prefetch_delta(sd_a.ctx, 0, dgood, sd_a.side, ev)
+    n_b = T.tls_prefetch_delta(sd_b.ctx, 0, dgood, sd_b.side, ev)
+    torch.cuda.synchronize()
+    assert n_a == n_b == s.pairs
+    ca, ba = sd_a.last_delta()
+    cb, bb = sd_b.last_delta()
+    np.testing.assert_array_equal(ca, cb)
+    np.testing.assert_array_equal(ba, bb)
+    assert torch.equal(sd_a.maps[1], sd_b.maps[1])
+    sd_a.close()
+    sd_b.close()
+
+
 def test_staggered_graph_replay_matches_the_oracle():
     """The same staggered steps captured into one HIP graph (device planning)
     and replayed: every step's output, the last selection and delta, and the

@@ -66,7 +66,10 @@ struct tls_offload {
   tls::MapItem* map_items = nullptr;       // pinned slot-map changes (host view)
   const tls::CopyItem* items_dev = nullptr;     // device views of the two lists
   const tls::MapItem* map_items_dev = nullptr;
-  std::vector<tls::MapItem> prev_changes, cur_changes;
+  std::vector<tls::MapItem> prev_changes, cur_changes;  // reserved for 2*pairs*kb each
+  std::vector<tls::MapItem> both;          // reserved for 4*pairs*kb: prev_changes + cur_changes
+  std::vector<std::pair<int64_t, int32_t>> evict;  // reserved for cap: (last step selected, block)
+  std::vector<int32_t> free_slots;         // reserved for cap
   std::vector<int32_t> last_pos;           // [pairs*NB] dedupe scratch, -1 when unused
   int64_t total_copied = 0;                // host-planned blocks moved since creation
   // device planning state (TLS_COPY_DEVICE), one allocation
@@ -186,6 +189,13 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   c->mark.assign((size_t)d.NB, 0u);
   c->last_counts.assign(d.pairs, 0);
   c->last_blocks.assign((size_t)d.pairs * d.kb, -1);
+  // the host-planned steps only clear and refill these, so they never allocate:
+  // a step changes at most kb evictions + kb copies per pair
+  c->prev_changes.reserve((size_t)2 * d.pairs * d.kb);
+  c->cur_changes.reserve((size_t)2 * d.pairs * d.kb);
+  c->both.reserve((size_t)4 * d.pairs * d.kb);
+  c->evict.reserve((size_t)c->cap);
+  c->free_slots.reserve((size_t)c->cap);
   hipError_t e = hipHostMalloc((void**)&c->host_M, (size_t)d.pairs * d.kb * sizeof(int32_t), hipHostMallocDefault);
   for (int i = 0; i < 2 && e == hipSuccess; ++i)
     e = hipHostMalloc((void**)&c->host_map[i], (size_t)d.pairs * d.NB * sizeof(int32_t), hipHostMallocDefault);
@@ -288,11 +298,20 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_error(e, "copy of M_t to host");
 
+  // every pair's M_t is checked before any state changes, so a rejected call
+  // leaves the context as it was (and the same step can be retried)
+  for (int p = 0; p < d.pairs; ++p) {
+    const int32_t* cur = c->host_M + (size_t)p * d.kb;
+    for (int i = 0; i < d.kb; ++i)
+      if (cur[i] < 0 || cur[i] >= d.NB || (i > 0 && cur[i] <= cur[i - 1]))
+        return set_error(TLS_ERR_STATE, "M_t of pair %d is not ascending block numbers in [0, NB)", p);
+  }
+
   int64_t total = 0;
   int nitems = 0;
   c->cur_changes.clear();
-  std::vector<std::pair<int64_t, int32_t>> evict;
-  std::vector<int32_t> free_slots;
+  std::vector<std::pair<int64_t, int32_t>>& evict = c->evict;
+  std::vector<int32_t>& free_slots = c->free_slots;
   for (int p = 0; p < d.pairs; ++p) {
     const int32_t* cur = c->host_M + (size_t)p * d.kb;
     int32_t* prv = c->prev.data() + (size_t)p * d.kb;
@@ -306,7 +325,6 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
     }
     const uint32_t s = c->stamp;
     for (int i = 0; i < d.kb; ++i) {
-      if (cur[i] < 0 || cur[i] >= d.NB) return set_error(TLS_ERR_STATE, "M_t holds an invalid block number");
       c->mark[prv[i]] = s;
       c->mark[cur[i]] = s;
     }
@@ -329,6 +347,7 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
         const int32_t blk = owner[sl];
         if (blk >= 0 && c->mark[blk] != s) evict.emplace_back(last[blk], blk);
       }
+      // (cannot fail: cap = 2 kb slots hold M_{t-1} u M_t with room to spare)
       if ((int)evict.size() < need) return set_error(TLS_ERR_STATE, "not enough evictable slots");
       std::partial_sort(evict.begin(), evict.begin() + need, evict.end());
       for (int k = 0; k < need; ++k) {
@@ -366,7 +385,8 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
     // map (step+1)&1 holds the state of two prefetches ago: apply the changes
     // of the previous and of this prefetch (one entry per index, last wins).
     int nmap = 0;
-    std::vector<tls::MapItem> both(c->prev_changes);
+    std::vector<tls::MapItem>& both = c->both;
+    both.assign(c->prev_changes.begin(), c->prev_changes.end());
     both.insert(both.end(), c->cur_changes.begin(), c->cur_changes.end());
     for (size_t k = 0; k < both.size(); ++k) c->last_pos[both[k].index] = (int32_t)k;
     for (size_t k = 0; k < both.size(); ++k)

@@ -178,20 +178,26 @@ __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, 
   };
 
   // wave-private double buffer: the wave's even tiles in tA, odd ones in tB.
-  // The next tile's loads go out before a tile is computed and are waited
-  // for after it (with the builtin wait, which the compiler accounts for, so
-  // that reading one buffer does not also wait for the loads into the other).
+  // Two tiles are in flight whenever the wave waits: a buffer is refilled
+  // (tile m+2) as soon as tile m has been computed from it, and the wave then
+  // waits only for tile m+1 (vmcnt <= 8: the 8 loads of tile m+2 are the
+  // younger ones). The waits are the builtin's, which the compiler accounts
+  // for, and the buffers are separate LDS objects, so reading one buffer does
+  // not also wait for the loads into the other. Tile m's LDS reads have all
+  // returned before its last MFMAs issue, so the refill cannot overtake them.
+  static_assert(kPvTile / 2 == 8, "the waits below count 8 loads per tile");
   if (ntw > 0) issue(tA[wave], 0);
-  wait_vmcnt<0>();
+  if (ntw > 1) issue(tB[wave], 1);
   for (int m = 0; m < ntw; m += 2) {
-    if (m + 1 < ntw) issue(tB[wave], m + 1);
+    if (m + 1 < ntw) wait_vmcnt<8>(); else wait_vmcnt<0>();
     compute(tA[wave], m);
-    wait_vmcnt<0>();
-    if (m + 1 >= ntw) break;
     if (m + 2 < ntw) issue(tA[wave], m + 2);
+    if (m + 1 >= ntw) break;
+    if (m + 2 < ntw) wait_vmcnt<8>(); else wait_vmcnt<0>();
     compute(tB[wave], m + 1);
-    wait_vmcnt<0>();
+    if (m + 3 < ntw) issue(tB[wave], m + 3);
   }
+  wait_vmcnt<0>();
   // ---- the workgroup partial: per head (m, l, -, -, o[DV]) ----
   const float l_tot = sum_rows(l_part);
   if (kq == 0) {
