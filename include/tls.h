@@ -167,6 +167,26 @@ int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_ca
                       int32_t slots_per_pair, const int32_t *token_idx, float *out, float *lse_opt, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* tls_sparse_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same kernels, same results (bit for bit) as tls_sparse_decode,
+ * but the split partials go to a device array of the library's own
+ * (TLS_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead of
+ * a caller workspace; the caller passes only inputs and outputs. A shape whose
+ * partials need more (tls_workspace_size(shape, TLS_WS_DECODE) above
+ * TLS_NOALLOC_SCRATCH_BYTES) returns TLS_ERR_WORKSPACE before anything is
+ * launched. Nothing in the array needs clearing between calls (every partial
+ * is written before it is read). Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other threads)
+ * race on it, and the caller must order them. The first call on each device
+ * looks the array's device address up (hipGetSymbolAddress, which may load
+ * the library's device code), so make it before a graph capture begins. No
+ * call allocates. Other errors as tls_sparse_decode. */
+#define TLS_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int tls_sparse_decode_noalloc(const tls_shape_t *shape, const void *q, const void *kv_cache,
+                              const int32_t *slot_map, int32_t slots_per_pair, const int32_t *token_idx,
+                              float *out, float *lse_opt, void *stream);
+
 /* One whole decode step (section 2A: both selection stages, then attention
  * over the kept tokens) in ONE launch: the results of tls_select followed by
  * tls_sparse_decode on the full cache (kv [B,Hkv,N,row], no slot map) --

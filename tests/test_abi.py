@@ -107,6 +107,20 @@ def test_argument_errors_before_any_device_work(lib):
     assert lib.tls_profile_events(T.TLS_PROFILE_BLOCK_SCORES, None, None) == T.TLS_OK
 
 
+def test_noalloc_decode_checks_before_any_device_work(lib):
+    """tls_sparse_decode_noalloc: NULL buffers, and shapes whose split partials
+    exceed its device array, are refused before the array is looked up; every
+    workload here fits the array."""
+    sh = T.shape_of(W.CONFIGS["c1_8k_gqa8"])
+    assert lib.tls_sparse_decode_noalloc(C.byref(sh), None, 16, None, 0, 16, 16, None, None) == T.TLS_ERR_INVALID_ARG
+    for name, s in W.CONFIGS.items():
+        assert 0 < T.tls_workspace_size(T.shape_of(s), T.TLS_WS_DECODE) <= T.TLS_NOALLOC_SCRATCH_BYTES, name
+    big = W.CONFIGS["c4_64k_mla"].with_(B=64)
+    assert T.tls_workspace_size(T.shape_of(big), T.TLS_WS_DECODE) > T.TLS_NOALLOC_SCRATCH_BYTES
+    rc = lib.tls_sparse_decode_noalloc(C.byref(T.shape_of(big)), 16, 16, None, 0, 16, 16, None, None)
+    assert rc == T.TLS_ERR_WORKSPACE and b"scratch array" in lib.tls_last_error()
+
+
 def test_select_both_stages_arguments_and_workspace(lib):
     """tls_select (both selection stages in one call): its workspace holds the
     block scores and the token stage's workspace; it rejects what either

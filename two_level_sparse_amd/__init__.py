@@ -30,9 +30,10 @@ TLS_WS_BLOCKS, TLS_WS_TOKENS, TLS_WS_DECODE, TLS_WS_SELECT, TLS_WS_STEP = 0, 1, 
 
 TLS_COPY_GATHER, TLS_COPY_MEMCPY, TLS_COPY_DEVICE, TLS_COPY_FULL = 0, 1, 2, 3
 TLS_PROFILE_BLOCK_SCORES, TLS_PROFILE_ATTENTION, TLS_PROFILE_HOST_COPY = 0, 1, 2
+TLS_NOALLOC_SCRATCH_BYTES = 40 << 20  # the device array of tls_sparse_decode_noalloc
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens", "tls_select",
-            "tls_sparse_decode", "tls_decode_step", "tls_decode_step_status", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
+            "tls_sparse_decode", "tls_sparse_decode_noalloc", "tls_decode_step", "tls_decode_step_status", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
             "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
             "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
             "tls_last_error", "tls_version"]
@@ -75,6 +76,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_select_tokens": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_select": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_sparse_decode": (C.c_int, [sh, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "tls_sparse_decode_noalloc": (C.c_int, [sh, vp, vp, vp, i32, vp, vp, vp, vp]),
         "tls_decode_step": (C.c_int, [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tls_decode_step_status": (C.c_int, [vp, vp]),
         "tls_offload_create": (C.c_int, [sh, vp, vp, vp, vp, vp, C.POINTER(vp)]),
@@ -163,6 +165,14 @@ def tls_sparse_decode(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, o
     _check(load_library().tls_sparse_decode(C.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(slot_map),
                                             int(slots_per_pair), _ptr(token_idx), _ptr(out), _ptr(lse), _ptr(ws),
                                             ws_bytes, _stream(stream)))
+
+
+def tls_sparse_decode_noalloc(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, out, lse=None, stream=None):
+    """tls_sparse_decode with the split partials in the library's own device
+    array (no workspace; calls on one GPU must not overlap)."""
+    _check(load_library().tls_sparse_decode_noalloc(C.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(slot_map),
+                                                    int(slots_per_pair), _ptr(token_idx), _ptr(out), _ptr(lse),
+                                                    _stream(stream)))
 
 
 def tls_decode_step(shape, q, summ, label_ch, codes, scale, kv, block_idx, token_idx, out, lse=None, ws=None,

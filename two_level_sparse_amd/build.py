@@ -29,7 +29,7 @@ def _compile(src: str) -> Path:
     obj = BUILD / (src + ".o")
     cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
     if src.endswith(".cpp"):
-        cmd = [hipcc(), *COMMON, "-x", "hip", "-c", str(CSRC / src), "-o", str(obj)]
+        cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", str(CSRC / src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/tls.h"
 #include "tls_api_internal.h"
@@ -375,10 +376,52 @@ int tls_decode_step_status(void* ws, void* stream) {
   return TLS_OK;
 }
 
-int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,
-                      int32_t slots_per_pair, const int32_t* token_idx, float* out, float* lse_opt, void* ws,
-                      size_t ws_len, void* stream) {
-  clear_error();
+}  // extern "C"
+
+// ---- scratch of tls_sparse_decode_noalloc
+// The library's own device array for the split partials of the attention, for
+// callers that cannot allocate. Each GPU the library runs on holds its own
+// copy (at its own address) until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept; only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[TLS_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mutex;
+
+// The current device's address of `scratch`; nullptr (error message set) if
+// the lookup fails.
+static void* scratch_address() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_error(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error(TLS_ERR_UNSUPPORTED, "device %d: the scratch array is tracked for devices 0..%d", dev, kMaxDevices - 1);
+    return nullptr;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+// The attention (tls_sparse_decode) with its split partials in `part`.
+static int sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,
+                         int32_t slots_per_pair, const int32_t* token_idx, float* out, float* lse_opt, void* part,
+                         size_t part_len, bool own_scratch, void* stream) {
   Derived d;
   int rc = derive(shape, &d);
   if (rc) return rc;
@@ -392,15 +435,43 @@ int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_ca
     return set_error(TLS_ERR_UNSUPPORTED, "attention is compiled for (D,DV) in {(64,64),(128,128),(256,256),(576,512)}");
   DecodePlan pl;
   plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
-  if (!ws || ws_len < ws_bytes(d, TLS_WS_DECODE))
-    return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", ws_bytes(d, TLS_WS_DECODE));
-  DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, ws, out, lse_opt,
+  const size_t need = ws_bytes(d, TLS_WS_DECODE);
+  if (own_scratch) {
+    if (need > TLS_NOALLOC_SCRATCH_BYTES)
+      return set_error(TLS_ERR_WORKSPACE,
+                       "the split partials of this shape need %zu bytes, above the %zu-byte scratch array of "
+                       "tls_sparse_decode_noalloc (use tls_sparse_decode with a workspace)",
+                       need, (size_t)TLS_NOALLOC_SCRATCH_BYTES);
+    part = scratch_address();
+    if (!part) return TLS_ERR_HIP;  // (message set by scratch_address)
+  } else if (!part || part_len < need) {
+    return set_error(TLS_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  }
+  DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, part, out, lse_opt,
                d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
                slot_map ? slots_per_pair : 0, d.N, d.NB, d.Ns, d.sm,
                g_prof_start[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed),
                g_prof_end[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed)};
   hipError_t e = launch_decode(a, pl, (hipStream_t)stream);
   return e == hipSuccess ? TLS_OK : hip_error(e, "sparse_decode launch");
+}
+
+extern "C" {
+
+int tls_sparse_decode(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,
+                      int32_t slots_per_pair, const int32_t* token_idx, float* out, float* lse_opt, void* ws,
+                      size_t ws_len, void* stream) {
+  clear_error();
+  return sparse_decode(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, out, lse_opt, ws, ws_len, false,
+                       stream);
+}
+
+int tls_sparse_decode_noalloc(const tls_shape_t* shape, const void* q, const void* kv_cache, const int32_t* slot_map,
+                              int32_t slots_per_pair, const int32_t* token_idx, float* out, float* lse_opt,
+                              void* stream) {
+  clear_error();
+  return sparse_decode(shape, q, kv_cache, slot_map, slots_per_pair, token_idx, out, lse_opt, nullptr, 0, true,
+                       stream);
 }
 
 }  // extern "C"
