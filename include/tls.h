@@ -41,7 +41,16 @@
  *   kv         [B, Hkv, N, row]      bf16; row = D + DV (K then V) or, when
  *                                    v_is_k_prefix, row = D and V[t] = K[t, 0:DV]
  *   label_ch   [Hkv, r]              int32, ascending channel numbers
- *   summ       [B, Hkv, NB, 2, D]    bf16; [.., 0, :] = Kmax, [.., 1, :] = Kmin
+ *   summ       [B, Hkv, NT, D/32, 2, 4, 16, 8]  bf16, NT = ceil(NBs / 16) with
+ *                                    NBs = ceil(ctx_capacity / bs) (NB when the
+ *                                    capacity is the length): the
+ *                                    block summaries in tile-fragment order --
+ *                                    element [b, h, T, c, m, kq, n, e] is channel
+ *                                    32c + 8kq + e of block 16T + n, m = 0 its
+ *                                    Kmax, m = 1 its Kmin (so every 16-block,
+ *                                    32-channel MFMA operand is 1 KB contiguous);
+ *                                    the entries of blocks 16T + n >= NB in the
+ *                                    last tile are not used
  *   codes      [B, Hkv, N, r/2]      uint8; channel i in byte i/2, low nibble for
  *                                    even i, two's-complement 4-bit code in [-7, 7]
  *   scale      [B, Hkv, N]           float; dequantised key = code * scale
@@ -105,7 +114,8 @@ size_t tls_workspace_size(const tls_shape_t *shape, int which);
 
 /* Block summaries and the INT4 label cache (section 2A: the block-level index
  * and the token-level index; run once per cache, not per step).
- *   kv [B,Hkv,N,row] -> summ [B,Hkv,NB,2,D], codes [B,Hkv,N,r/2], scale [B,Hkv,N].
+ *   kv [B,Hkv,N,row] -> summ (tile-fragment order, above), codes [B,Hkv,N,r/2],
+ *   scale [B,Hkv,N].
  * Kmax/Kmin are exact per-channel extremes over the valid tokens of a block.
  * Label cache per token: a = max |K[t, c_i]| over the label channels; a == 0
  * gives scale 0 and codes 0, otherwise scale = float(a/7) and

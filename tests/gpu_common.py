@@ -29,6 +29,15 @@ def bf16_bits(t):
     return to_np(t.view(torch.int16)).view(np.uint16)
 
 
+def unpack_summaries(summ, s, NB=None):
+    """The GPU's block summaries (tile-fragment order, see include/tls.h) as
+    bf16 bits [pairs, NB, 2, D]: [.., 0, :] Kmax, [.., 1, :] Kmin."""
+    bits = bf16_bits(summ).reshape(s.pairs, -1)
+    nt = bits.shape[1] // (32 * s.D)
+    a = bits.reshape(s.pairs, nt, s.D // 32, 2, 4, 16, 8).transpose(0, 1, 5, 3, 2, 4, 6)
+    return a.reshape(s.pairs, nt * 16, 2, s.D)[:, : (s.NB if NB is None else NB)]
+
+
 def band_check(got, ids, scores, K):
     """Checks a GPU selection `got` (ascending, -1 padded) against oracle scores of
     the candidate ids. Returns (n_band, exact) where exact = same set as the oracle."""
@@ -98,7 +107,7 @@ def check_all(s, q, kv, lab, pairs=None, expect_exact=False):
     stats = dict(block_band=0, token_band=0, block_exact=True, token_exact=True)
 
     # build: summaries, codes and scales bit-exact
-    summ = bf16_bits(run.cache.summ).reshape(s.pairs, s.NB, 2, s.D)
+    summ = unpack_summaries(run.cache.summ, s)
     codes = to_np(run.cache.codes).reshape(s.pairs, s.N, s.r // 2)
     scale = to_np(run.cache.scale).reshape(s.pairs, s.N)
     for i, p in enumerate(pairs):

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workload as W
-from gpu_common import band_check, bf16_bits, to_np
+from gpu_common import band_check, bf16_bits, to_np, unpack_summaries
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ CASES = {
 def check_indices(s, gc, kv, lab, n):
     """summaries, codes and scales of the first n tokens against the oracle's build of length n"""
     sn = s.with_(N=n)
-    summ = bf16_bits(gc.summ).reshape(s.pairs, -1, 2, s.D)[:, : sn.NB]
+    summ = unpack_summaries(gc.summ, s, sn.NB)
     codes = to_np(gc.codes).reshape(s.pairs, -1, s.r // 2)[:, :n]
     scale = to_np(gc.scale).reshape(s.pairs, -1)[:, :n]
     rows = bf16_bits(gc.kv).reshape(s.pairs, -1, s.row)[:, :n]

@@ -29,9 +29,10 @@ __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, 
   const int64_t t0 = j * bs;
   const int64_t t1 = t0 + bs < N ? t0 + bs : N;
 
-  // Per-channel max / min over the valid tokens of block j.
-  uint16_t* smax = summ + ((int64_t)p * NBs + j) * 2 * D;
-  uint16_t* smin = smax + D;
+  // Per-channel max / min over the valid tokens of block j, written in
+  // tile-fragment order (channels c, c+1 stay adjacent: one 4-byte store each).
+  uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
+  const int KC = D / 32;
   for (int c = 2 * lane; c < D; c += 128) {
     float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
     for (int64_t t = t0; t < t1; ++t) {
@@ -43,8 +44,10 @@ __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, 
       mn1 = fminf(mn1, b);
     }
     // Extremes of bf16 values are bf16 values: keep the upper 16 bits.
-    *reinterpret_cast<uint32_t*>(smax + c) = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xFFFF0000u);
-    *reinterpret_cast<uint32_t*>(smin + c) = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xFFFF0000u);
+    *reinterpret_cast<uint32_t*>(sp + summ_elem(j, c, 0, KC)) =
+        (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xFFFF0000u);
+    *reinterpret_cast<uint32_t*>(sp + summ_elem(j, c, 1, KC)) =
+        (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xFFFF0000u);
   }
 
   // INT4 label cache: symmetric absmax per token over the label channels.

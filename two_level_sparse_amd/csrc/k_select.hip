@@ -50,13 +50,16 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
   const int64_t jbase = ((int64_t)blockIdx.x * 4 + wave) * (16 * NSUB);
   if (jbase >= NB) return;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-  const uint16_t* sp = summ + (int64_t)p * NBs * 2 * D;
+  const int kc = KC > 0 ? KC : D / 32;
+  const uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
 
+  // the wave's tiles in tile-fragment order (a tile past the last is the last
+  // again; its scores are not stored): lane L reads elements 8L .. 8L+7 of a unit
   const uint16_t* brow[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    const int64_t j = jbase + s * 16 + n;
-    brow[s] = sp + (j < NB ? j : NB - 1) * 2 * D;
+    const int64_t T = min(jbase / 16 + s, summ_tiles(NB) - 1);
+    brow[s] = sp + summ_unit(T, 0, 0, kc) + 8 * lane;
   }
   const uint16_t* qrow[MT];
 #pragma unroll
@@ -67,16 +70,15 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) acc[m][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunk = KC > 0 ? KC : D / 32;
-  for (int cb = 0; cb < nchunk; cb += UNR) {
+  for (int cb = 0; cb < kc; cb += UNR) {
     u32x4 kmx[UNR][NSUB], kmn[UNR][NSUB], qr[UNR][MT];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int off = (cb + u) * 32 + 8 * kq;
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        kmx[u][s] = ld16(brow[s] + off);
-        kmn[u][s] = ld16(brow[s] + D + off);
+        kmx[u][s] = ld16(brow[s] + summ_unit(0, cb + u, 0, kc));
+        kmn[u][s] = ld16(brow[s] + summ_unit(0, cb + u, 1, kc));
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) qr[u][m] = ld16(qrow[m] + off);
@@ -114,14 +116,28 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
 // one latent kv head): a GEMM with M = G heads, N = blocks, K = 2*D. A
 // workgroup of 8 waves scores kLdsTiles tiles of 16 consecutive blocks of one
 // pair. Wave w takes head tiles 2*(w&3), 2*(w&3)+1 and one half of the
-// channel chunks (w>>2), whose q fragments it keeps in registers; the two
-// halves' sums meet in LDS. The summaries of all the workgroup's tiles go to
-// LDS with direct global->LDS 16-byte loads, laid out as B fragments (piece
-// (chunk, max|min) = 64 lanes x 16 bytes, read back conflict-free), and are
-// read by the 4 waves that share a channel half. q is loaded once per
-// workgroup for kLdsTiles tiles of summaries.
+// channel chunks (w>>2); the two halves' sums meet in LDS at the end.
+//
+// The contraction streams over the chunks of a half: step g multiplies chunk
+// g of the first half (waves 0-3) and chunk KH+g of the second (waves 4-7).
+// Everything a step needs -- the wave's own q fragments of its chunk and the
+// summary pieces (tile, half, max|min) of both chunks -- goes to one of
+// kLdsSlots LDS slots with direct global->LDS 16-byte loads, kLdsSlots-1
+// steps ahead of the products, laid out as MFMA fragments (64 lanes x 16
+// bytes per piece, read back conflict-free). Only direct loads are in
+// flight, so a wave waits with vmcnt for exactly the step it multiplies next
+// (plain loads of q beside them would make the compiler wait for all), and
+// one barrier per step both publishes the step's pieces and frees the slot
+// of the step before for the next issue. Each slot is its own LDS object, so
+// reading one slot does not also wait for the loads into the others.
 constexpr int kLdsTiles = 4;
 constexpr int kLdsWaves = 8;
+constexpr int kLdsSlots = 4;
+
+struct LdsScoreSlot {
+  u32x4 q[kLdsWaves][2][64];             // wave, head tile of the wave, lane
+  u32x4 b[kLdsTiles][2][2][64];          // tile, half, max|min, lane
+};
 
 template <int MT, int KC>
 __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint16_t* __restrict__ q,
@@ -129,23 +145,18 @@ __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint1
                                                                      float* __restrict__ S, int Hq, int Hkv, int G,
                                                                      int64_t NB, int64_t NBs) {
   constexpr int D = KC * 32;
-  constexpr int MW = 2;                 // head tiles per wave
-  constexpr int KH = KC / 2;            // channel chunks per wave
-  constexpr int PIECES = 2 * KC;        // per tile
-  constexpr int PPW = (PIECES + kLdsWaves - 1) / kLdsWaves;
-  constexpr int CG = KH % 3 == 0 ? 3 : KH % 2 == 0 ? 2 : 1;  // chunks per group of LDS reads
-  static_assert(MT <= 8 && KC % 2 == 0 && kLdsTiles == 4, "tile layout");
-  // tiles 0-1 and 2-3 in two LDS objects, so that reading tiles 0-1 does not
-  // wait for the loads of tiles 2-3
-  __shared__ u32x4 btA[2][PIECES][64], btB[2][PIECES][64];
+  constexpr int MW = 2;       // head tiles per wave
+  constexpr int KH = KC / 2;  // steps (chunks per half)
+  constexpr int BPW = kLdsTiles * 2 * 2 / kLdsWaves;  // summary pieces per wave and step
+  constexpr int LPS = MW + BPW;                       // direct loads per wave and step
+  static_assert(MT == 8 && KC % 2 == 0 && kLdsTiles == 4 && BPW == 2, "tile layout");
+  // (a slot no step uses is never referenced, and takes no LDS)
+  __shared__ LdsScoreSlot s0, s1, s2, s3;
   __shared__ float part[kLdsTiles][4][16];
-  // after the products: the second channel half's sums, [tile][head-tile pair][MW][lane],
-  // in btA when it is large enough
-  constexpr int HALF = kLdsTiles * 4 * MW * 64;
-  constexpr bool kAlias = 2 * PIECES * 64 >= HALF;
-  __shared__ f32x4 half_own[kAlias ? 1 : HALF];
-  f32x4* half1 = kAlias ? reinterpret_cast<f32x4*>(&btA[0][0][0]) : half_own;
-  auto bt = [&](int t) -> u32x4(*)[64] { return t < 2 ? btA[t] : btB[t - 2]; };
+  // after the products: the second channel half's sums, [tile][head-tile pair][MW][lane]
+  static_assert(sizeof(LdsScoreSlot) >= kLdsTiles * 4 * MW * 64 * sizeof(f32x4), "half sums fit a slot");
+  f32x4* half1 = reinterpret_cast<f32x4*>(&s0);
+
   // Workgroup -> (pair, tile group). Workgroups are dealt to the 8 XCDs in
   // turn (linear id mod 8); when the pair count allows, every workgroup of a
   // pair lands on one XCD, whose L2 then serves the pair's q to all of them.
@@ -165,100 +176,123 @@ __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint1
   const int n = lane & 15, kq = lane >> 4;
   const int hp = wave & 3, kh = wave >> 2;  // head-tile pair, channel half
   // A workgroup always loads kLdsTiles tiles; rows past NB repeat row NB-1
-  // and are not stored.
+  // and are not stored. q rows past G repeat row G-1; their products are
+  // left out of the maxima.
   const int64_t t0 = (int64_t)tg * kLdsTiles;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-  const uint16_t* sp = summ + (int64_t)p * NBs * 2 * D;
-
-  // Direct loads of tiles [ta, tb): wave w issues pieces w, w+8, ...
-  auto issue = [&](int ta, int tb) {
+  const uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
+  const uint16_t* qr[MW];
 #pragma unroll
-    for (int t = ta; t < tb; ++t) {
-      const int64_t j = min((t0 + t) * 16 + n, NB - 1);
-      const uint16_t* src = sp + j * 2 * D + 8 * kq;
+  for (int i = 0; i < MW; ++i) qr[i] = qp + (int64_t)min((2 * hp + i) * 16 + n, G - 1) * D + 8 * kq + kh * KH * 32;
+  // this wave's summary pieces x = wave + 8k: (tile x>>2, half (x>>1)&1,
+  // max|min x&1), each one 1 KB unit of the tile-fragment order (a tile past
+  // the last is the last again; its scores are not stored)
+  const uint16_t* br[BPW];
 #pragma unroll
-      for (int k = 0; k < PPW; ++k) {
-        const int pc = wave + kLdsWaves * k;
-        if (pc < PIECES)
-          __builtin_amdgcn_global_load_lds(
-              (__attribute__((address_space(1))) void*)(src + (pc & 1) * D + (pc >> 1) * 32),
-              (__attribute__((address_space(3))) void*)&bt(t)[pc][0], 16, 0, 0);
-      }
-    }
-  };
-  // Tiles 0 and 1 first, then the q fragments (rows past G repeat row G-1;
-  // their products are left out of the maxima), split once into q+ / q-.
-  // Waiting for q also waits for those two tiles; tiles 2 and 3 are issued
-  // after it and land while tiles 0 and 1 are multiplied.
-  issue(0, 2);
-  u32x4 qpos[MW][KH], qneg[MW][KH];
-  {
-    u32x4 raw[MW][KH];
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      const uint16_t* qr = qp + (int64_t)min((2 * hp + i) * 16 + n, G - 1) * D + 8 * kq + kh * KH * 32;
-#pragma unroll
-      for (int c = 0; c < KH; ++c) raw[i][c] = ld16(qr + c * 32);
-    }
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int i = 0; i < MW; ++i)
-#pragma unroll
-      for (int c = 0; c < KH; ++c) split_sign(raw[i][c], qpos[i][c], qneg[i][c]);
+  for (int k = 0; k < BPW; ++k) {
+    const int x = wave + kLdsWaves * k;
+    const int64_t T = min(t0 + (x >> 2), summ_tiles(NB) - 1);
+    br[k] = sp + summ_unit(T, ((x >> 1) & 1) * KH, x & 1, KC) + 8 * lane;
   }
-  __builtin_amdgcn_sched_barrier(0);
-  issue(2, kLdsTiles);
-  // tiles 0 and 1 are in LDS for every wave: a barrier without a memory fence
-  // (a fence would wait for tiles 2 and 3 as well)
-  __asm__ volatile("s_barrier" ::: "memory");
-
-  f32x4 tot[kLdsTiles][MW];
-  auto product = [&](int t) {
-    // four independent accumulation chains per head tile (q+ / q- terms of
-    // even / odd chunks), so that consecutive MFMAs do not wait on each other
-    f32x4 acc[MW][4];
+  auto slot_of = [&](auto gc) -> LdsScoreSlot& {
+    constexpr int sl = decltype(gc)::value % kLdsSlots;
+    if constexpr (sl == 0) return s0;
+    else if constexpr (sl == 1) return s1;
+    else if constexpr (sl == 2) return s2;
+    else return s3;
+  };
+  auto issue = [&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    if constexpr (g < KH) {
+      LdsScoreSlot& sl = slot_of(gc);
 #pragma unroll
-    for (int i = 0; i < MW; ++i)
+      for (int i = 0; i < MW; ++i)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(qr[i] + g * 32),
+                                         (__attribute__((address_space(3))) void*)&sl.q[wave][i][0], 16, 0, 0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cg = 0; cg < KH; cg += CG) {
-      u32x4 bmx[CG], bmn[CG];
-#pragma unroll
-      for (int u = 0; u < CG; ++u) {
-        const int c = kh * KH + cg + u;
-        bmx[u] = bt(t)[2 * c][lane];
-        bmn[u] = bt(t)[2 * c + 1][lane];
-      }
-#pragma unroll
-      for (int u = 0; u < CG; ++u) {
-#pragma unroll
-        for (int i = 0; i < MW; ++i) {
-          {
-            const int a = 2 * (u & 1);
-            acc[i][a] = mfma16x16x32(qpos[i][cg + u], bmx[u], acc[i][a]);
-            acc[i][a + 1] = mfma16x16x32(qneg[i][cg + u], bmn[u], acc[i][a + 1]);
-          }
-        }
+      for (int k = 0; k < BPW; ++k) {
+        const int x = wave + kLdsWaves * k;
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(br[k] + summ_unit(0, g, 0, KC)),
+                                         (__attribute__((address_space(3))) void*)&sl.b[x >> 2][(x >> 1) & 1][x & 1][0],
+                                         16, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < MW; ++i) tot[t][i] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
   };
-  product(0);
-  product(1);
-  wait_vmcnt<0>();
-  __asm__ volatile("s_barrier" ::: "memory");
+
+  // accumulators: one chain per (tile, head tile); a chunk's q+ products go
+  // to the eight chains first, then its q- products
+  f32x4 acc[kLdsTiles][MW];
 #pragma unroll
-  for (int t = 2; t < kLdsTiles; ++t) product(t);
-  // the second channel half hands its sums to the first (through the tile
-  // buffer, once every wave is done reading it)
+  for (int t = 0; t < kLdsTiles; ++t)
+#pragma unroll
+    for (int i = 0; i < MW; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto product = [&](const LdsScoreSlot& sl) {
+    // all ten LDS reads first, then one wait (interleaved with the MFMAs the
+    // compiler waits for each pair of reads in turn)
+    u32x4 qraw[MW], bmx[kLdsTiles], bmn[kLdsTiles];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) qraw[i] = sl.q[wave][i][lane];
+#pragma unroll
+    for (int t = 0; t < kLdsTiles; ++t) {
+      bmx[t] = sl.b[t][kh][0][lane];
+      bmn[t] = sl.b[t][kh][1][lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 qpos[MW], qneg[MW];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) split_sign(qraw[i], qpos[i], qneg[i]);
+#pragma unroll
+    for (int t = 0; t < kLdsTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < MW; ++i) acc[t][i] = mfma16x16x32(qpos[i], bmx[t], acc[t][i]);
+#pragma unroll
+    for (int t = 0; t < kLdsTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < MW; ++i) acc[t][i] = mfma16x16x32(qneg[i], bmn[t], acc[t][i]);
+  };
+  // step g: wait for this wave's loads of step g (the ones issued after it
+  // may stay in flight), then a barrier (no fence: it would wait for those
+  // too) after which every wave's pieces of step g are in LDS and every wave
+  // is done with step g-1, whose slot then takes step g-1+kLdsSlots
+  auto step = [&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    if constexpr (g < KH) {
+      // (the products of step g-1, and with them every read of its slot, stay
+      // ahead of this wait and barrier: the slot is refilled right after)
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int last_issued = g == 0 ? kLdsSlots - 1 : g + kLdsSlots - 2;
+      constexpr int ahead = (last_issued < KH - 1 ? last_issued : KH - 1) - g;
+      wait_vmcnt<LPS * ahead>();
+      __asm__ volatile("s_barrier" ::: "memory");
+      if constexpr (g > 0) issue(std::integral_constant<int, g - 1 + kLdsSlots>{});
+      product(slot_of(gc));
+    }
+  };
+  issue(std::integral_constant<int, 0>{});
+  issue(std::integral_constant<int, 1>{});
+  issue(std::integral_constant<int, 2>{});
+  issue(std::integral_constant<int, 3>{});
+  static_assert(kLdsSlots == 4 && KH <= 12, "steps unrolled below");
+  step(std::integral_constant<int, 0>{});
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  step(std::integral_constant<int, 3>{});
+  step(std::integral_constant<int, 4>{});
+  step(std::integral_constant<int, 5>{});
+  step(std::integral_constant<int, 6>{});
+  step(std::integral_constant<int, 7>{});
+  step(std::integral_constant<int, 8>{});
+  step(std::integral_constant<int, 9>{});
+  step(std::integral_constant<int, 10>{});
+  step(std::integral_constant<int, 11>{});
+  // the second channel half hands its sums to the first (through slot 0,
+  // once every wave is done reading the slots)
   __syncthreads();
   if (kh == 1) {
 #pragma unroll
     for (int t = 0; t < kLdsTiles; ++t)
 #pragma unroll
-      for (int i = 0; i < MW; ++i) half1[((t * 4 + hp) * MW + i) * 64 + lane] = tot[t][i];
+      for (int i = 0; i < MW; ++i) half1[((t * 4 + hp) * MW + i) * 64 + lane] = acc[t][i];
   }
   __syncthreads();
   if (kh == 0) {
@@ -267,7 +301,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void k_score_blocks_lds(const uint1
       float best = -INFINITY;
 #pragma unroll
       for (int i = 0; i < MW; ++i) {
-        const f32x4 sum = tot[t][i] + half1[((t * 4 + hp) * MW + i) * 64 + lane];
+        const f32x4 sum = acc[t][i] + half1[((t * 4 + hp) * MW + i) * 64 + lane];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if ((2 * hp + i) * 16 + 4 * kq + r < G) best = fmaxf(best, sum[r]);

@@ -132,14 +132,13 @@ __device__ __attribute__((noinline)) void item_scores(ArgsP a0, int p, int64_t j
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, kq = lane >> 4;
   const uint16_t* qp = a->q + ((int64_t)b * a->Hq + (int64_t)h * G) * 128;
-  const uint16_t* sp = a->summ + (int64_t)p * a->NBs * 256;
-  const uint16_t* brow[2];
+  const uint16_t* sp = a->summ + (int64_t)p * summ_pair_elems(a->NBs, 128);
+  const uint16_t* brow[2];  // the two tiles in tile-fragment order (one past the last: the last again)
   int64_t jt[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     jt[s] = j0 + 16 * (wave + 4 * s);
-    const int64_t j = jt[s] + n;
-    brow[s] = sp + (j < NB ? j : NB - 1) * 256;
+    brow[s] = sp + summ_unit(min(jt[s] / 16, summ_tiles(NB) - 1), 0, 0, 4) + 8 * lane;
   }
   const uint16_t* qrow = qp + (int64_t)min(n, G - 1) * 128;
   u32x4 kmx[4][2], kmn[4][2], qr[4];
@@ -148,8 +147,8 @@ __device__ __attribute__((noinline)) void item_scores(ArgsP a0, int p, int64_t j
     const int off = c * 32 + 8 * kq;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      kmx[c][s] = ld16(brow[s] + off);
-      kmn[c][s] = ld16(brow[s] + 128 + off);
+      kmx[c][s] = ld16(brow[s] + summ_unit(0, c, 0, 4));
+      kmn[c][s] = ld16(brow[s] + summ_unit(0, c, 1, 4));
     }
     qr[c] = ld16(qrow + off);
   }

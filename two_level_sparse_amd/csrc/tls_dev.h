@@ -22,6 +22,24 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // 16-byte global load (8 bf16 / 4 words); pointer must be 16-byte aligned.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Block summaries in tile-fragment order: per (batch, kv head) pair, tiles of
+// 16 blocks; in tile T, 32-channel chunk c and m (0: Kmax, 1: Kmin) form one
+// 512-element unit whose element (kq*16 + n)*8 + e holds channel 32c + 8kq + e
+// of block 16T + n -- exactly the B fragment of a 16x16x32 MFMA with the tile's
+// blocks as columns, so lane L of a fragment load reads elements 8L .. 8L+7
+// and every load is 1 KB contiguous.
+__host__ __device__ constexpr int64_t summ_tiles(int64_t nblocks) { return (nblocks + 15) / 16; }
+// elements per pair for NBs blocks of capacity
+__host__ __device__ constexpr int64_t summ_pair_elems(int64_t NBs, int D) { return summ_tiles(NBs) * 32 * D; }
+// element offset, within a pair, of unit (tile T, chunk c, m); KC = D / 32
+__host__ __device__ constexpr int64_t summ_unit(int64_t T, int c, int m, int KC) {
+  return ((T * KC + c) * 2 + m) * 512;
+}
+// element offset, within a pair, of channel ch of block j's summary m
+__host__ __device__ constexpr int64_t summ_elem(int64_t j, int ch, int m, int KC) {
+  return summ_unit(j / 16, ch / 32, m, KC) + (((ch % 32) / 8) * 16 + j % 16) * 8 + ch % 8;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // One 16x16x32 bf16 MFMA: acc[m][n] += sum_k a[m][k] * b[k][n].

@@ -38,13 +38,19 @@ class Cache:
         self.kv = kv if isinstance(kv, torch.Tensor) else bf16(kv, device)
         assert tuple(self.kv.shape) == (s.B, s.Hkv, s.N, s.row) and self.kv.dtype == torch.bfloat16
         self.label_ch = torch.as_tensor(np.ascontiguousarray(label_ch, dtype=np.int32)).to(device)
-        self.summ = torch.empty((s.B, s.Hkv, s.NB, 2, s.D), dtype=torch.bfloat16, device=device)
+        self.summ = torch.empty((s.B, s.Hkv, summ_pair_elems(s.NB, s.D)), dtype=torch.bfloat16, device=device)
         self.codes = torch.empty((s.B, s.Hkv, s.N, s.r // 2), dtype=torch.uint8, device=device)
         self.scale = torch.empty((s.B, s.Hkv, s.N), dtype=torch.float32, device=device)
 
     def build(self, stream=None):
         tls_build_summaries(self.shape, self.kv, self.label_ch, self.summ, self.codes, self.scale, stream)
         return self
+
+
+def summ_pair_elems(nblocks, D):
+    """bf16 elements of one pair's block summaries (tile-fragment order: whole
+    tiles of 16 blocks, each block's Kmax and Kmin rows of D channels)."""
+    return (nblocks + 15) // 16 * 16 * 2 * D
 
 
 class GrowingCache:
@@ -61,7 +67,7 @@ class GrowingCache:
         self.kv = torch.zeros((s.B, s.Hkv, self.capacity, s.row), dtype=torch.bfloat16, device=device)
         self.kv[:, :, : s.N] = kv if isinstance(kv, torch.Tensor) else bf16(kv, device)
         self.label_ch = torch.as_tensor(np.ascontiguousarray(label_ch, dtype=np.int32)).to(device)
-        self.summ = torch.zeros((s.B, s.Hkv, nb_cap, 2, s.D), dtype=torch.bfloat16, device=device)
+        self.summ = torch.zeros((s.B, s.Hkv, summ_pair_elems(nb_cap, s.D)), dtype=torch.bfloat16, device=device)
         self.codes = torch.zeros((s.B, s.Hkv, self.capacity, s.r // 2), dtype=torch.uint8, device=device)
         self.scale = torch.zeros((s.B, s.Hkv, self.capacity), dtype=torch.float32, device=device)
 
