@@ -190,12 +190,16 @@ def decode(s, q, kv, label_ch, pairs=None, built=None, force_blocks=None, force_
                 token_idx=ti, ntok=nt, out=out, lse=lse)
 
 
-def staggered(s, qs, kv, label_ch, built, force_prologue=None, force_M=None):
+def staggered(s, qs, kv, label_ch, built, force_prologue=None, force_M=None, lens=None):
     """Staggered offloaded schedule (O10) over all pairs; `built` = decode(...) over all pairs.
 
     force_prologue [np, Kb'] / force_M [steps, np, Kb'] replace the schedule's own
     block selections (the prologue's and each step's), so that a run whose sets
-    differ only inside the score band can be followed step by step."""
+    differ only inside the score band can be followed step by step.
+    lens [steps + 1]: a cache that grows between steps (s.N = the allocated
+    length, kv holding all of it): the prologue sees lens[0] tokens, step t
+    lens[t + 1]; built's codes and scales (of all s.N tokens) are used, its
+    summaries are not (the schedule builds them from each prefix)."""
     steps = qs.shape[0]
     qs = _c(qs, np.uint16); kv = _c(kv, np.uint16); label_ch = _c(label_ch, np.int32)
     np_ = s.pairs
@@ -210,6 +214,7 @@ def staggered(s, qs, kv, label_ch, built, force_prologue=None, force_M=None):
                              _p(_c(built.codes, np.int8)), _p(_c(built.scale, np.float32)),
                              _p(None if force_prologue is None else _c(force_prologue, np.int32)),
                              _p(None if force_M is None else _c(force_M, np.int32)),
+                             _p(None if lens is None else _c(lens, np.int64)),
                              _p(M), _p(T), _p(nT), _p(ne), _p(ev), _p(out), _p(lse))
     if rc != 0:
         raise RuntimeError(f"oracle staggered schedule failed ({rc})")

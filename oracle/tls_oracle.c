@@ -368,21 +368,39 @@ static int orc_force_set(int32_t *dst, const int32_t *src, int kb, int64_t NB) {
  *   block sets, ascending, used in place of the prologue's and step t's own
  *   stage 1 -- so that a run whose selections differ from these only among
  *   blocks of (nearly) equal score can be followed step by step.
+ * lens [steps + 1] (may be NULL: every length is s->N): a cache that grows
+ *   at decode time (pages, section 1: the cache grows with every generated
+ *   token). s->N is then the allocated length (the stride of kv, codes and
+ *   scale, which are given for all of it); the prologue sees the first
+ *   lens[0] tokens and step t the first lens[t+1] (non-decreasing, each with
+ *   at least Kb blocks): its token stage, attention and selection M_t all use
+ *   that prefix, with block summaries built from it (the INT4 codes of a
+ *   token depend on its own row only, so those of the whole length serve).
+ *   Blocks that do not exist yet are never selected and never resident.
  * Outputs per step t and pair p:
  *   M [steps, np, Kb'] ; T [steps, np, Kb'] (first nT entries, ascending);
  *   nT [steps, np]; nevict [steps, np]; evicted [steps, np, 2*Kb'] (may be
  *   NULL: the first nevict entries, in eviction order); out [steps, np, G, DV];
  *   lse [steps, np, G].
- * Returns 0, or a negative value if the schedule was violated.              */
+ * Returns 0, or a negative value if the schedule was violated (-6: lens
+ * invalid).                                                                 */
 int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uint16_t *kv,
                   const int32_t *label_ch, const double *kmax, const double *kmin,
                   const int8_t *codes, const float *scale, const int32_t *force_prologue,
-                  const int32_t *force_M, int32_t *M, int32_t *T, int32_t *nT, int32_t *nevict,
-                  int32_t *evicted, double *out, double *lse) {
+                  const int32_t *force_M, const int64_t *lens, int32_t *M, int32_t *T, int32_t *nT,
+                  int32_t *nevict, int32_t *evicted, double *out, double *lse) {
   int G = s->Hq / s->Hkv;
   int np = s->B * s->Hkv;
-  int64_t NB = nblocks(s);
+  int64_t NB = nblocks(s); /* blocks of the whole (capacity) length */
   int kb = (int)(s->Kb < NB ? s->Kb : NB);
+  /* A growing cache: every length must keep Kb' and Kt' unchanged, i.e. hold
+   * at least Kb blocks from the first selection on, and never shrink. */
+  if (lens) {
+    for (int t = 0; t <= steps; ++t) {
+      if (lens[t] < 1 || lens[t] > s->N || (t > 0 && lens[t] < lens[t - 1])) return -6;
+      if ((lens[t] + s->bs - 1) / s->bs < s->Kb) return -6;
+    }
+  }
   int64_t ktc = (int64_t)kb * s->bs;
   int kt = (int)(s->Kt < ktc ? s->Kt : ktc);
   int cap = 2 * kb;
@@ -404,9 +422,22 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
     int64_t *last = (int64_t *)malloc((size_t)NB * sizeof(int64_t));
     orc_item *ev = (orc_item *)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(orc_item));
     int n_res = 0, perr = 0;
+    /* the cache as it is when a selection or step runs: lens[0] tokens for
+     * the prologue, lens[t+1] for step t (its token stage, its attention and
+     * its own selection); the summaries of that prefix are built afresh */
+    orc_shape_t cs = *s;
+    double *gmx = NULL, *gmn = NULL;
+    if (lens) {
+      gmx = (double *)malloc((size_t)NB * s->D * sizeof(double));
+      gmn = (double *)malloc((size_t)NB * s->D * sizeof(double));
+      cs.N = lens[0];
+      orc_summaries_pair(&cs, kvp, gmx, gmn);
+      mx = gmx;
+      mn = gmn;
+    }
     const uint16_t *q0 = qs + ((int64_t)b * s->Hq + (int64_t)h * G) * s->D;
-    if (orc_select_blocks_pair(s, q0, mx, mn, NULL, Sbuf, prev) < 0) perr = -2;
-    if (force_prologue && orc_force_set(prev, force_prologue + (int64_t)p * kb, kb, NB) != 0) perr = -5;
+    if (orc_select_blocks_pair(&cs, q0, mx, mn, NULL, Sbuf, prev) < 0) perr = -2;
+    if (force_prologue && orc_force_set(prev, force_prologue + (int64_t)p * kb, kb, nblocks(&cs)) != 0) perr = -5;
     for (int j = 0; j < kb; ++j) {
       resident[prev[j]] = 1;
       last[prev[j]] = -1;
@@ -414,13 +445,17 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
     n_res = kb;
     for (int t = 0; t < steps && perr == 0; ++t) {
       const uint16_t *qt = qs + (((int64_t)t * s->B + b) * s->Hq + (int64_t)h * G) * s->D;
+      if (lens && lens[t + 1] != cs.N) { /* rows appended before step t */
+        cs.N = lens[t + 1];
+        orc_summaries_pair(&cs, kvp, gmx, gmn);
+      }
       for (int j = 0; j < kb; ++j)
         if (!resident[prev[j]]) perr = -3; /* a block in use must be resident */
-      int nt = orc_select_tokens_pair(s, qt, lab, cd, sc, prev, kb, tok, NULL, NULL, NULL);
+      int nt = orc_select_tokens_pair(&cs, qt, lab, cd, sc, prev, kb, tok, NULL, NULL, NULL);
       int64_t o = (int64_t)t * np + p;
-      orc_attend_pair(s, qt, kvp, tok, nt, out + o * G * s->DV, lse + o * G);
-      if (orc_select_blocks_pair(s, qt, mx, mn, NULL, Sbuf, cur) < 0) perr = -2;
-      if (force_M && orc_force_set(cur, force_M + o * kb, kb, NB) != 0) perr = -5;
+      orc_attend_pair(&cs, qt, kvp, tok, nt, out + o * G * s->DV, lse + o * G);
+      if (orc_select_blocks_pair(&cs, qt, mx, mn, NULL, Sbuf, cur) < 0) perr = -2;
+      if (force_M && orc_force_set(cur, force_M + o * kb, kb, nblocks(&cs)) != 0) perr = -5;
       memset(in_prev, 0, (size_t)NB);
       memset(in_cur, 0, (size_t)NB);
       for (int j = 0; j < kb; ++j) {
@@ -460,6 +495,8 @@ int orc_staggered(const orc_shape_t *s, int steps, const uint16_t *qs, const uin
       cur = sw;
     }
     if (perr < err) err = perr;
+    free(gmx);
+    free(gmn);
     free(Sbuf);
     free(prev);
     free(cur);

@@ -482,3 +482,66 @@ def test_c1_regression_record():
     np.testing.assert_array_equal(st.block_idx, rec["block_idx"])
     np.testing.assert_array_equal(st.token_idx, rec["token_idx"])
     np.testing.assert_array_equal(st.out, rec["out"])
+
+
+def test_staggered_growing_cache_equals_one_step_decodes_of_each_prefix():
+    """A cache that grows between steps (lens; pages, section 1: the KV cache
+    grows with every generated token). At every step t the schedule must equal a
+    fresh one-step decode of the first lens[t+1] tokens alone -- summaries and
+    label cache built from that prefix: its selection M_t is that decode's stage
+    1, its output is that decode's attention forced to M_{t-1}; the prologue is
+    stage 1 of the first lens[0] tokens. Transfers and evictions are the LRU
+    replayed from the selection history, new blocks enter as the cache reaches
+    them, and constant lengths give the fixed-length schedule."""
+    steps = 24
+    s = W.small_shape(B=1, Hq=8, Hkv=2, N=3072, bs=64, Kb=4, Kt=64, steps=steps)  # N: the allocated length
+    rng = np.random.default_rng(31)
+    q, kv = make_inputs(s, rng)
+    lab = lab_all(s)
+    qs = _drift(q, steps, 1.0, rng)
+    lens = np.cumsum(np.r_[1500, rng.integers(1, 60, steps)]).astype(np.int64)
+    assert lens[-1] <= s.N
+    built = oracle.decode(s, qs[0], kv, lab)  # codes and scales of all N tokens
+    st = oracle.staggered(s, qs, kv, lab, built, lens=lens)
+
+    fixed = oracle.staggered(s, qs, kv, lab, built)
+    const = oracle.staggered(s, qs, kv, lab, built, lens=np.full(steps + 1, s.N, dtype=np.int64))
+    for f in ("M", "T", "nT", "nevict", "out", "lse"):
+        np.testing.assert_array_equal(getattr(const, f), getattr(fixed, f))
+
+    def prefix(n):
+        return s.with_(N=int(n)), np.ascontiguousarray(kv[:, :, :n])
+
+    sp, kvp = prefix(lens[0])
+    prev = oracle.decode(sp, qs[0], kvp, lab).block_idx  # the prologue's M_{-1}
+    history = [prev]
+    for t in range(steps):
+        sp, kvp = prefix(lens[t + 1])
+        one = oracle.decode(sp, qs[t], kvp, lab)
+        np.testing.assert_array_equal(st.M[t], one.block_idx)
+        forced = oracle.decode(sp, qs[t], kvp, lab, built=one, force_blocks=prev)
+        np.testing.assert_array_equal(st.out[t], forced.out)
+        np.testing.assert_array_equal(st.lse[t], forced.lse)
+        prev = one.block_idx
+        history.append(prev)
+    nb0 = (lens[0] + s.bs - 1) // s.bs
+    assert (st.M >= nb0).any()  # blocks that did not exist at the prologue get selected
+
+    # transfers and evictions: the LRU replayed from the selection history
+    assert st.nevict.sum() > 0
+    for p in range(s.pairs):
+        resident = set(history[0][p].tolist())
+        last = {j: -1 for j in resident}
+        prevset = set(resident)
+        for t in range(steps):
+            Mt = set(history[t + 1][p].tolist())
+            Tt = sorted(Mt - resident)
+            assert st.T[t, p, : st.nT[t, p]].tolist() == Tt
+            need = max(0, len(resident) + len(Tt) - 2 * s.Kb)
+            cands = sorted((last[j], j) for j in resident - prevset - Mt)
+            expect = [j for _, j in cands[:need]]
+            assert st.evicted[t, p, :need].tolist() == expect, (p, t)
+            resident = (resident - set(expect)) | set(Tt)
+            for j in Mt:
+                last[j] = t
+            prevset = Mt
