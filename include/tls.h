@@ -170,7 +170,8 @@ int tls_select(const tls_shape_t *shape, const void *q, const void *summ, const 
  *   out[b, g] = sum_t softmax_t(sm_scale * q_g . K[t]) V[t] over t in token_idx
  * kv_cache: with slot_map == NULL, the full cache [B,Hkv,N,row]. Otherwise a
  *   resident cache [B,Hkv,slots_per_pair,bs,row] addressed through
- *   slot_map [B,Hkv,NB] (int32 slot of each block, -1 = not resident); every
+ *   slot_map [B,Hkv,NBs] (int32 slot of each block, -1 = not resident; NBs =
+ *   blocks of ctx_capacity, NB when the capacity is the length); every
  *   block holding a kept token must be resident.
  * Entries -1 in token_idx are skipped. lse_opt: NULL or [B,Hq] float. */
 int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_cache, const int32_t *slot_map,
@@ -238,10 +239,14 @@ int tls_decode_step_status(void *ws, void *stream);
 typedef struct tls_offload tls_offload_t;
 
 /* Create an offload context.
- *   host_kv      [B,Hkv,N,row] bf16 in pinned host memory (hipHostMalloc),
- *                borrowed until tls_offload_destroy; N must be a multiple of bs.
+ *   host_kv      [B,Hkv,Ns,row] bf16 in pinned host memory (hipHostMalloc),
+ *                Ns = ctx_capacity (ctx_len when 0), a multiple of bs, its
+ *                first ctx_len tokens filled; borrowed until
+ *                tls_offload_destroy. A capacity above ctx_len lets the cache
+ *                grow (tls_offload_append) and needs at least Kb blocks now.
  *   dev_cache    [B,Hkv,2*Kb',bs,row] bf16 device memory, borrowed.
- *   dev_slot_map two device buffers of [B,Hkv,NB] int32 each, borrowed
+ *   dev_slot_map two device buffers of [B,Hkv,NBs] int32 each (NBs = blocks
+ *                of Ns), borrowed
  *                (dev_slot_map[0] and dev_slot_map[1]); step t reads buffer t%2
  *                and the prefetch of step t writes buffer (t+1)%2.
  *   initial_blocks [B,Hkv,Kb'] int32 host array: M_{-1}, ascending. These
@@ -294,6 +299,28 @@ int tls_prefetch_delta(tls_offload_t *ctx, int32_t step, const int32_t *dev_bloc
  * may change at any step). */
 enum { TLS_COPY_GATHER = 0, TLS_COPY_MEMCPY = 1, TLS_COPY_DEVICE = 2, TLS_COPY_FULL = 3 };
 int tls_offload_set_copy_mode(tls_offload_t *ctx, int mode);
+
+/* Decode-time append to an offloaded cache (section 1: the cache grows with
+ * every generated token; section 2B: it lives in host memory).
+ *   new_kv [B,Hkv,n_new,row] bf16 device, 16-byte aligned: the rows of the
+ *   next n_new tokens. summ/codes/scale: the device index the steps read
+ *   (capacity strides), label_ch as for tls_build_summaries.
+ * Three launches on `stream`: the rows are written to host_kv after the
+ * current length (through its device mapping); the summaries of the blocks
+ * they fall in are updated from the new rows and the previous summaries (the
+ * max / min of a block is exact either way), and their codes and scales
+ * computed, so the index equals tls_build_summaries of the longer cache; and
+ * where such a block is resident in the slot map that the next step's
+ * attention reads, the rows are written into its slot too (a block that is
+ * not resident is read from host_kv when it is next transferred). The steps
+ * after it take a shape whose ctx_len includes the new tokens.
+ * Ordering: `stream` must run after the copies of the last tls_prefetch_delta
+ * (its copies_done event) and before the next step's calls. Errors:
+ * TLS_ERR_INVALID_ARG (length beyond ctx_capacity, n_new < 1, NULL or
+ * misaligned buffers), TLS_ERR_UNSUPPORTED (host_kv without a device
+ * mapping), TLS_ERR_HIP. */
+int tls_offload_append(tls_offload_t *ctx, const void *new_kv, int32_t n_new, const int32_t *label_ch, void *summ,
+                       uint8_t *codes, float *scale, void *stream);
 /* The current mode, or a negative error code for a NULL context. */
 int tls_offload_get_copy_mode(const tls_offload_t *ctx);
 

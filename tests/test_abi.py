@@ -175,7 +175,8 @@ def test_token_selection_over_the_whole_cache_takes_passes(lib):
 
 def test_append_checks_the_capacity_before_any_device_work(lib):
     """tls_append_kv: the grown length must fit the allocated capacity, which
-    must itself hold the current length; offload contexts take no spare capacity."""
+    must itself hold the current length; an offload context takes a capacity
+    of whole blocks, with at least Kb blocks present when it is to grow."""
     s = W.small_shape(N=1000)
     sh = T.shape_of(s, capacity=1064)
     rc = lib.tls_append_kv(C.byref(sh), None, 1, 16, 16, 16, 16, 16, None)
@@ -192,7 +193,13 @@ def test_append_checks_the_capacity_before_any_device_work(lib):
     assert rc == T.TLS_ERR_INVALID_ARG and b"ctx_capacity" in lib.tls_last_error()
     # a capacity beyond the length is a valid shape for every call
     assert lib.tls_workspace_size(C.byref(sh), T.TLS_WS_DECODE) > 0
+    # offloaded caches: whole blocks of capacity, and a growing one needs Kb blocks from the start
     h = C.c_void_p()
-    off = T.shape_of(s.with_(N=1024), capacity=1088)
+    off = T.shape_of(s.with_(N=1024), capacity=1090)
     rc = lib.tls_offload_create(C.byref(off), 16, 16, 16, 16, 16, C.byref(h))
-    assert rc == T.TLS_ERR_UNSUPPORTED and h.value is None
+    assert rc == T.TLS_ERR_UNSUPPORTED and h.value is None and b"multiple" in lib.tls_last_error()
+    few = T.shape_of(s.with_(N=64 * (s.Kb - 1), Kb=s.Kb), capacity=64 * (s.Kb + 4))
+    rc = lib.tls_offload_create(C.byref(few), 16, 16, 16, 16, 16, C.byref(h))
+    assert rc == T.TLS_ERR_UNSUPPORTED and h.value is None and b"top_kb" in lib.tls_last_error()
+    rc = lib.tls_offload_append(None, 16, 1, 16, 16, 16, 16, None)
+    assert rc == T.TLS_ERR_INVALID_ARG

@@ -95,6 +95,96 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None, qs=None):
     return stats
 
 
+@pytest.mark.parametrize("mode", [2, 0, 1])
+def test_staggered_growing_cache(mode):
+    """A cache that grows between steps (tls_offload_append: 1-63 rows before
+    each step, across block boundaries and into new blocks) against the
+    oracle's schedule over the same lengths, made to follow the GPU's own
+    selections: every M_t (band rule on the block scores of the prefix), T_t
+    bit-exact, token sets by the band rule, outputs within 2e-3 of attention
+    over the GPU's tokens; afterwards the index (summaries, codes, scales) is
+    bit-exact against the oracle's build of the grown cache and the host cache
+    holds the appended rows. Device planning (2) and both host-planned modes."""
+    import two_level_sparse_amd as T
+    from gpu_common import bf16_bits, unpack_summaries
+    from two_level_sparse_amd.runtime import GrowingCache, StaggeredDecoder, bf16
+    steps, cap, N0 = 24, 6144, 3000
+    s_cap = W.small_shape(B=2, Hq=8, Hkv=2, N=cap, bs=64, Kb=8, Kt=200, n_outlier=4, seed=41)
+    q0 = W.gen_q(s_cap)
+    kv = W.gen_kv(s_cap)
+    lab = W.label_channels(s_cap, kv[0])
+    rng = np.random.default_rng(41)
+    adds = rng.integers(1, 64, steps)
+    adds[5] = 64  # a whole block at once
+    lens = np.cumsum(np.r_[N0, adds]).astype(np.int64)
+    assert lens[-1] <= cap
+    qs = W.drift_queries(s_cap, q0, steps)
+    s0 = s_cap.with_(N=N0)
+    gc = GrowingCache(s0, kv[:, :, :N0], lab, cap).build()
+    host = torch.zeros((s_cap.B, s_cap.Hkv, cap, s_cap.row), dtype=torch.bfloat16).pin_memory()
+    host[:, :, :N0] = torch.from_numpy(kv[:, :, :N0].view(np.int16)).view(torch.bfloat16)
+    sd = StaggeredDecoder(s0, gc, host, bf16(q0), copy_mode=mode)
+    assert sd.copy_mode == mode
+    pro = to_np(sd.selection(-1)).reshape(s_cap.pairs, -1).copy()
+    gM, gcounts, gblocks, gtok, gout = [], [], [], [], []
+    for t in range(steps):
+        sd.append(bf16(np.ascontiguousarray(kv[:, :, lens[t]:lens[t + 1]])))
+        out = sd.step(bf16(qs[t]))
+        torch.cuda.synchronize()
+        counts, blocks = sd.last_delta()
+        gM.append(to_np(sd.selection(t)).reshape(s_cap.pairs, -1).copy())
+        gcounts.append(counts.copy())
+        gblocks.append(blocks.copy())
+        gtok.append(to_np(sd.dec.token_idx).reshape(s_cap.pairs, -1).copy())
+        gout.append(to_np(out).reshape(s_cap.pairs, s_cap.G, s_cap.DV).copy())
+    assert sd.n == lens[-1]
+    sd.close()
+    gM = np.stack(gM)
+    built = oracle.decode(s_cap, q0, kv, lab)  # codes and scales of every token
+    ref = oracle.staggered(s_cap, qs, kv, lab, built, force_prologue=pro, force_M=gM, lens=lens)
+
+    def prefix(n):
+        return s_cap.with_(N=int(n)), np.ascontiguousarray(kv[:, :, :n])
+
+    sp, kvp = prefix(lens[0])
+    S0 = oracle.decode(sp, q0, kvp, lab).S
+    for p in range(s_cap.pairs):
+        band_check(pro[p], np.arange(sp.NB), S0[p], s_cap.Kb)
+    prev_blocks = pro
+    new_blocks = 0
+    for t in range(steps):
+        sp, kvp = prefix(lens[t + 1])
+        one = oracle.decode(sp, qs[t], kvp, lab)
+        for p in range(s_cap.pairs):
+            band_check(gM[t, p], np.arange(sp.NB), one.S[p], s_cap.Kb)
+            assert gblocks[t][p, : gcounts[t][p]].tolist() == ref.T[t, p, : ref.nT[t, p]].tolist(), (t, p)
+            b, h = divmod(p, s_cap.Hkv)
+            qp = qs[t, b, h * s_cap.G:(h + 1) * s_cap.G]
+            ti = gtok[t][p]
+            _, cand, cs = oracle.select_tokens_pair(sp, qp, lab[h], one.codes[p], one.scale[p], prev_blocks[p])
+            band_check(ti, cand, cs, s_cap.Kt)
+            assert ti.max() < lens[t + 1]
+            o_ref, _ = oracle.attend_pair(sp, qp, kv[b, h], ti[ti >= 0])
+            assert float(np.max(np.abs(gout[t][p] - o_ref))) <= 2e-3, (t, p)
+        new_blocks += int(np.sum(gM[t] >= (lens[0] + s_cap.bs - 1) // s_cap.bs))
+        prev_blocks = gM[t]
+    assert new_blocks > 0  # blocks that did not exist at the start were selected and moved
+    # the index of the grown cache and the host rows
+    n = int(lens[-1])
+    sn, kvn = prefix(n)
+    fin = oracle.decode(sn, q0, kvn, lab)
+    summ = unpack_summaries(gc.summ, s_cap, sn.NB)
+    for p in range(s_cap.pairs):
+        np.testing.assert_array_equal(W.bf16_bits_to_f64(summ[p, :, 0]), fin.kmax[p])
+        np.testing.assert_array_equal(W.bf16_bits_to_f64(summ[p, :, 1]), fin.kmin[p])
+    codes = to_np(gc.codes).reshape(s_cap.pairs, cap, -1)[:, :n]
+    scale = to_np(gc.scale).reshape(s_cap.pairs, cap)[:, :n]
+    for p in range(s_cap.pairs):
+        np.testing.assert_array_equal(codes[p], oracle.pack_codes(fin.codes[p]))
+        np.testing.assert_array_equal(scale[p].view(np.uint32), fin.scale[p].view(np.uint32))
+    np.testing.assert_array_equal(host.view(torch.int16).numpy().view(np.uint16)[:, :, :n], kv[:, :, :n])
+
+
 @pytest.mark.parametrize("helper,mode", [(False, 1), (True, 1), (False, 0), (True, 0), (False, 2), (True, 2), (False, 3)])
 def test_staggered_small(helper, mode):
     s = W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=21)

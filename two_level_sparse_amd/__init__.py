@@ -34,7 +34,7 @@ TLS_NOALLOC_SCRATCH_BYTES = 40 << 20  # the device array of tls_sparse_decode_no
 
 EXPORTED = ["tls_workspace_size", "tls_build_summaries", "tls_select_blocks", "tls_select_tokens", "tls_select",
             "tls_sparse_decode", "tls_sparse_decode_noalloc", "tls_decode_step", "tls_decode_step_status", "tls_append_kv", "tls_offload_create", "tls_offload_slot_map", "tls_prefetch_delta",
-            "tls_offload_set_copy_mode", "tls_offload_get_copy_mode", "tls_offload_last_delta",
+            "tls_offload_set_copy_mode", "tls_offload_append", "tls_offload_get_copy_mode", "tls_offload_last_delta",
             "tls_offload_total_copied", "tls_offload_destroy", "tls_profile_events",
             "tls_last_error", "tls_version"]
 
@@ -83,6 +83,7 @@ def load_library(path: Path | str | None = None) -> C.CDLL:
         "tls_offload_slot_map": (vp, [vp, i32]),
         "tls_prefetch_delta": (C.c_int, [vp, i32, vp, vp, vp, C.POINTER(i64)]),
         "tls_offload_last_delta": (C.c_int, [vp, vp, vp]),
+        "tls_offload_append": (C.c_int, [vp, vp, i32, vp, vp, vp, vp, vp]),
         "tls_offload_set_copy_mode": (C.c_int, [vp, C.c_int]),
         "tls_offload_get_copy_mode": (C.c_int, [vp]),
         "tls_offload_total_copied": (C.c_int, [vp, C.POINTER(i64)]),
@@ -206,6 +207,11 @@ def tls_prefetch_delta(ctx, step, dev_block_idx, side_stream, copies_done_event)
     _check(load_library().tls_prefetch_delta(ctx, step, _ptr(dev_block_idx), _stream(side_stream),
                                              copies_done_event.cuda_event, C.byref(n)))
     return n.value
+
+
+def tls_offload_append(ctx, new_kv, n_new, label_ch, summ, codes, scale, stream=None):
+    _check(load_library().tls_offload_append(ctx, _ptr(new_kv), int(n_new), _ptr(label_ch), _ptr(summ), _ptr(codes),
+                                             _ptr(scale), _stream(stream)))
 
 
 def tls_offload_set_copy_mode(ctx, mode):

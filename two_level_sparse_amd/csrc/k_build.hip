@@ -15,6 +15,41 @@
 
 namespace tls {
 
+// INT4 label codes of one token row: symmetric absmax over the label channels
+// (a == 0: scale 0, codes 0; otherwise scale = float(a / 7) and code_i =
+// clamp(rint(K[c_i] / scale), -7, 7), both divisions in double), packed two
+// per byte (channel i in byte i/2, low nibble for even i).
+template <int RMAX>
+__device__ __forceinline__ void quantize_row(const uint16_t* rowp, const int32_t* lab, int r, uint8_t* cp,
+                                             float* sc_out) {
+  float v[RMAX];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    v[i] = i < r ? bf2f(rowp[lab[i]]) : 0.0f;
+    a = fmaxf(a, fabsf(v[i]));
+  }
+  float sc = 0.0f;
+  int code[RMAX];
+  if (a == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) code[i] = 0;
+  } else {
+    sc = (float)((double)a / 7.0);
+    const double dsc = (double)sc;
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) {
+      double qv = rint((double)v[i] / dsc);
+      qv = qv > 7.0 ? 7.0 : (qv < -7.0 ? -7.0 : qv);
+      code[i] = (int)qv;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RMAX; i += 2)
+    if (i < r) cp[i / 2] = (uint8_t)((code[i] & 0xF) | ((code[i + 1] & 0xF) << 4));
+  *sc_out = sc;
+}
+
 template <int RMAX>
 __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, const int32_t* __restrict__ label_ch,
                                                uint16_t* __restrict__ summ, uint8_t* __restrict__ codes,
@@ -52,37 +87,70 @@ __global__ __launch_bounds__(256) void k_build(const uint16_t* __restrict__ kv, 
 
   // INT4 label cache: symmetric absmax per token over the label channels.
   const int64_t t = t0 + lane;
-  if (lane < bs && t < N) {
-    const uint16_t* rowp = base + t * row;
-    const int32_t* lab = label_ch + (int64_t)h * r;
-    float v[RMAX];
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
-      v[i] = i < r ? bf2f(rowp[lab[i]]) : 0.0f;
-      a = fmaxf(a, fabsf(v[i]));
+  if (lane < bs && t < N)
+    quantize_row<RMAX>(base + t * row, label_ch + (int64_t)h * r, r, codes + ((int64_t)p * Ns + t) * (r / 2),
+                       scale + (int64_t)p * Ns + t);
+}
+
+// Incremental index update for n new rows appended at N0 (rows [pairs, n,
+// row] on the device): workgroup (i, p) = one wave for the i-th block that the
+// new rows touch. A block's max / min over its valid tokens is the max / min
+// of its previous summary (when it already held tokens) and of its new rows,
+// exactly, so only the new rows are read -- in particular not the rows already
+// offloaded to host memory. The new tokens are quantised as in k_build.
+template <int RMAX>
+__global__ __launch_bounds__(64) void k_append_index(const uint16_t* __restrict__ rows, int n,
+                                                     const int32_t* __restrict__ label_ch, uint16_t* __restrict__ summ,
+                                                     uint8_t* __restrict__ codes, float* __restrict__ scale, int Hkv,
+                                                     int D, int row, int bs, int r, int64_t N0, int64_t Ns,
+                                                     int64_t NBs) {
+  const int lane = threadIdx.x, p = blockIdx.y;
+  const int64_t j = N0 / bs + blockIdx.x;
+  const int64_t t0 = j * bs, ta = t0 > N0 ? t0 : N0, tb = min(t0 + bs, N0 + n);  // new rows of block j
+  const bool had = t0 < N0;                                                       // block held tokens before
+  const uint16_t* src = rows + (int64_t)p * n * row;
+  uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
+  const int KC = D / 32;
+  for (int c = 2 * lane; c < D; c += 128) {
+    uint32_t* pmx = reinterpret_cast<uint32_t*>(sp + summ_elem(j, c, 0, KC));
+    uint32_t* pmn = reinterpret_cast<uint32_t*>(sp + summ_elem(j, c, 1, KC));
+    float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
+    if (had) {
+      const uint32_t wx = *pmx, wn = *pmn;
+      mx0 = bf_lo(wx);
+      mx1 = bf_hi(wx);
+      mn0 = bf_lo(wn);
+      mn1 = bf_hi(wn);
     }
-    float sc = 0.0f;
-    int code[RMAX];
-    if (a == 0.0f) {
-#pragma unroll
-      for (int i = 0; i < RMAX; ++i) code[i] = 0;
-    } else {
-      sc = (float)((double)a / 7.0);
-      const double dsc = (double)sc;
-#pragma unroll
-      for (int i = 0; i < RMAX; ++i) {
-        double qv = rint((double)v[i] / dsc);
-        qv = qv > 7.0 ? 7.0 : (qv < -7.0 ? -7.0 : qv);
-        code[i] = (int)qv;
-      }
+    for (int64_t t = ta; t < tb; ++t) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (t - N0) * row + c);
+      const float a = bf_lo(w), b = bf_hi(w);
+      mx0 = fmaxf(mx0, a);
+      mn0 = fminf(mn0, a);
+      mx1 = fmaxf(mx1, b);
+      mn1 = fminf(mn1, b);
     }
-    uint8_t* cp = codes + ((int64_t)p * Ns + t) * (r / 2);
-#pragma unroll
-    for (int i = 0; i < RMAX; i += 2)
-      if (i < r) cp[i / 2] = (uint8_t)((code[i] & 0xF) | ((code[i + 1] & 0xF) << 4));
-    scale[(int64_t)p * Ns + t] = sc;
+    *pmx = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xFFFF0000u);
+    *pmn = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xFFFF0000u);
   }
+  const int64_t t = t0 + lane;
+  if (lane < bs && t >= ta && t < tb)
+    quantize_row<RMAX>(src + (t - N0) * row, label_ch + (int64_t)(p % Hkv) * r, r,
+                       codes + ((int64_t)p * Ns + t) * (r / 2), scale + (int64_t)p * Ns + t);
+}
+
+hipError_t launch_append_index(const uint16_t* rows, int n, const int32_t* label_ch, uint16_t* summ, uint8_t* codes,
+                               float* scale, int pairs, int Hkv, int D, int row, int bs, int r, int64_t N0,
+                               int64_t Ns, int64_t NBs, hipStream_t st) {
+  const int64_t nblk = (N0 + n - 1) / bs - N0 / bs + 1;
+  dim3 grid((unsigned)nblk, (unsigned)pairs);
+  if (r <= 16)
+    hipLaunchKernelGGL(k_append_index<16>, grid, dim3(64), 0, st, rows, n, label_ch, summ, codes, scale, Hkv, D,
+                       row, bs, r, N0, Ns, NBs);
+  else
+    hipLaunchKernelGGL(k_append_index<32>, grid, dim3(64), 0, st, rows, n, label_ch, summ, codes, scale, Hkv, D,
+                       row, bs, r, N0, Ns, NBs);
+  return hipGetLastError();
 }
 
 // Appended rows: workgroup (i, p) copies new row i of pair p (row*2 bytes, a

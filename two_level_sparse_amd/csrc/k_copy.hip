@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
   __syncthreads();
   for (int i = tid; i < kb; i += 256) {
     const int b = M[i], bp = prev[i];
-    if ((unsigned)b >= (unsigned)NB) {
+    if ((unsigned)b >= (unsigned)a.NBv) {
       bad_sh = 1u;
       continue;
     }
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_delta_plan(DeltaArgs a) {
     atomicOr(&inm[bp >> 5], 1u << (bp & 31));
   }
   __syncthreads();
-  if (bad_sh) {  // M_t holds a block number outside [0, NB): nothing is changed
+  if (bad_sh) {  // M_t holds a block number outside [0, NBv): nothing is changed
     if (tid == 0) {
       *a.err = 2;
       a.counts[p] = 0;
@@ -246,9 +246,9 @@ __global__ __launch_bounds__(256) void k_full_plan(DeltaArgs a) {
   copy_map(a.map_cur + (int64_t)p * NB, map_next, NB, tid);
   __syncthreads();
   for (int i = tid; i < kb; i += 256)
-    if ((unsigned)M[i] >= (unsigned)NB) bad_sh = 1u;
+    if ((unsigned)M[i] >= (unsigned)a.NBv) bad_sh = 1u;
   __syncthreads();
-  if (bad_sh) {  // M_t holds a block number outside [0, NB): the map stays that of M_{t-1}
+  if (bad_sh) {  // M_t holds a block number outside [0, NBv): the map stays that of M_{t-1}
     if (tid == 0) {
       *a.err = 2;
       a.counts[p] = 0;
@@ -332,6 +332,30 @@ hipError_t launch_device_delta(const DeltaArgs& a, const uint16_t* host_kv_dev, 
   e = hipGetLastError();
   if (prof_end) (void)hipEventRecord(prof_end, st);
   return e;
+}
+
+// Rows appended to an offloaded cache: workgroup (i, p) writes new row i of
+// pair p (token N0 + i) into the resident slot of its block, when the block is
+// resident in slot_map (the map the next attention uses); a block that is not
+// resident is read from host memory, which holds the row, when it is next
+// transferred.
+__global__ __launch_bounds__(64) void k_patch_slots(const uint16_t* __restrict__ rows, int n, int64_t N0,
+                                                    const int32_t* __restrict__ slot_map, int64_t NBs,
+                                                    uint16_t* __restrict__ dev_cache, int cap, int bs, int row) {
+  const int i = blockIdx.x, p = blockIdx.y;
+  const int64_t t = N0 + i;
+  const int slot = slot_map[(int64_t)p * NBs + t / bs];
+  if (slot < 0 || slot >= cap) return;
+  const u32x4* s = reinterpret_cast<const u32x4*>(rows + ((int64_t)p * n + i) * row);
+  u32x4* d = reinterpret_cast<u32x4*>(dev_cache + (((int64_t)p * cap + slot) * bs + t % bs) * row);
+  for (int k = threadIdx.x; k < row / 8; k += 64) d[k] = s[k];
+}
+
+hipError_t launch_patch_slots(const uint16_t* rows, int n, int pairs, int64_t N0, const int32_t* slot_map,
+                              int64_t NBs, uint16_t* dev_cache, int cap, int bs, int row, hipStream_t st) {
+  hipLaunchKernelGGL(k_patch_slots, dim3((unsigned)n, (unsigned)pairs), dim3(64), 0, st, rows, n, N0, slot_map, NBs,
+                     dev_cache, cap, bs, row);
+  return hipGetLastError();
 }
 
 }  // namespace tls

@@ -44,7 +44,8 @@
 using namespace tls;
 
 struct tls_offload {
-  Derived d;
+  Derived d;                  // the shape at creation; per-block arrays are strided by d.NBs (capacity)
+  int64_t cur_N = 0;          // tokens per sequence now (grows with tls_offload_append)
   const uint16_t* host_kv = nullptr;
   uint16_t* dev_cache = nullptr;
   int32_t* dev_map[2] = {nullptr, nullptr};
@@ -99,7 +100,7 @@ constexpr int kCopyWorkgroups = 16;
 // Device copy of the planning state after the prologue (TLS_COPY_DEVICE).
 static hipError_t init_device_state(tls_offload* c) {
   const Derived& d = c->d;
-  const size_t P = d.pairs, kb = d.kb, cap = c->cap, NB = d.NB;
+  const size_t P = d.pairs, kb = d.kb, cap = c->cap, NB = d.NBs;
   auto up = [](size_t bytes) { return (bytes + 255) & ~(size_t)255; };
   const size_t o_items = 0, o_prev = o_items + up(P * kb * sizeof(CopyItem)), o_owner = o_prev + up(P * kb * 4),
                o_last = o_owner + up(P * cap * 4), o_counts = o_last + up(P * NB * 4),
@@ -119,12 +120,13 @@ static hipError_t init_device_state(tls_offload* c) {
   a.err = (int32_t*)(base + o_err);
   a.step_ctr = (int32_t*)(base + o_step);
   a.pairs = d.pairs;
-  a.NB = d.NB;
+  a.NB = d.NBs;
+  a.NBv = d.NB;
   a.kb = d.kb;
   a.cap = c->cap;
   a.bs = d.bs;
   a.row = d.row;
-  a.N = d.N;
+  a.N = d.Ns;
   a.block_elems = (int64_t)c->block_elems;
   a.copy_wgs = kCopyWorkgroups;
   if (const char* env = std::getenv("TLS_OFFLOAD_COPY_WGS")) {
@@ -172,21 +174,26 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   if (rc) return rc;
   if (!host_kv || !dev_cache || !dev_slot_map0 || !dev_slot_map1 || !initial_blocks)
     return set_error(TLS_ERR_INVALID_ARG, "NULL buffer");
-  if (d.N % d.bs != 0) return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_len to be a multiple of block_size");
-  if (d.Ns != d.N) return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_capacity equal to ctx_len (no appends)");
+  // blocks move whole: the host cache must hold every block of the capacity entirely
+  if (d.Ns % d.bs != 0)
+    return set_error(TLS_ERR_UNSUPPORTED, "offload needs ctx_capacity (ctx_len when 0) to be a multiple of block_size");
+  // a cache that will grow keeps Kb' = Kb (and so its slot count) from the start
+  if (d.Ns > d.N && d.NB < shape->top_kb)
+    return set_error(TLS_ERR_UNSUPPORTED, "a growing offloaded cache needs at least top_kb blocks from the start");
   tls_offload* c = new tls_offload;
   c->d = d;
+  c->cur_N = d.N;
   c->host_kv = (const uint16_t*)host_kv;
   c->dev_cache = (uint16_t*)dev_cache;
   c->dev_map[0] = dev_slot_map0;
   c->dev_map[1] = dev_slot_map1;
   c->cap = 2 * d.kb;
   c->block_elems = (size_t)d.bs * d.row;
-  c->slot_of.assign((size_t)d.pairs * d.NB, -1);
-  c->last_sel.assign((size_t)d.pairs * d.NB, -2);
+  c->slot_of.assign((size_t)d.pairs * d.NBs, -1);
+  c->last_sel.assign((size_t)d.pairs * d.NBs, -2);
   c->slot_owner.assign((size_t)d.pairs * c->cap, -1);
   c->prev.assign(initial_blocks, initial_blocks + (size_t)d.pairs * d.kb);
-  c->mark.assign((size_t)d.NB, 0u);
+  c->mark.assign((size_t)d.NBs, 0u);
   c->last_counts.assign(d.pairs, 0);
   c->last_blocks.assign((size_t)d.pairs * d.kb, -1);
   // the host-planned steps only clear and refill these, so they never allocate:
@@ -198,7 +205,7 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
   c->free_slots.reserve((size_t)c->cap);
   hipError_t e = hipHostMalloc((void**)&c->host_M, (size_t)d.pairs * d.kb * sizeof(int32_t), hipHostMallocDefault);
   for (int i = 0; i < 2 && e == hipSuccess; ++i)
-    e = hipHostMalloc((void**)&c->host_map[i], (size_t)d.pairs * d.NB * sizeof(int32_t), hipHostMallocDefault);
+    e = hipHostMalloc((void**)&c->host_map[i], (size_t)d.pairs * d.NBs * sizeof(int32_t), hipHostMallocDefault);
   if (e == hipSuccess)
     e = hipHostMalloc((void**)&c->items, (size_t)d.pairs * d.kb * sizeof(tls::CopyItem), hipHostMallocDefault);
   if (e == hipSuccess)
@@ -218,7 +225,7 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
       c->items_dev = (const tls::CopyItem*)di;
       c->map_items_dev = (const tls::MapItem*)dm;
       c->copy_mode = TLS_COPY_GATHER;
-      c->last_pos.assign((size_t)d.pairs * d.NB, -1);
+      c->last_pos.assign((size_t)d.pairs * d.NBs, -1);
     } else {
       (void)hipGetLastError();  // not device-mapped: per-block copies
     }
@@ -231,11 +238,11 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
         free_ctx(c);
         return set_error(TLS_ERR_INVALID_ARG, "initial_blocks must be ascending block numbers in [0, NB)");
       }
-      c->slot_of[(size_t)p * d.NB + blk] = i;
+      c->slot_of[(size_t)p * d.NBs + blk] = i;
       c->slot_owner[(size_t)p * c->cap + i] = blk;
-      c->last_sel[(size_t)p * d.NB + blk] = -1;
+      c->last_sel[(size_t)p * d.NBs + blk] = -1;
       e = hipMemcpy(c->dev_cache + ((size_t)p * c->cap + i) * c->block_elems,
-                    c->host_kv + ((size_t)p * d.N + (size_t)blk * d.bs) * d.row, c->block_elems * 2,
+                    c->host_kv + ((size_t)p * d.Ns + (size_t)blk * d.bs) * d.row, c->block_elems * 2,
                     hipMemcpyHostToDevice);
       if (e != hipSuccess) {
         free_ctx(c);
@@ -251,7 +258,7 @@ int tls_offload_create(const tls_shape_t* shape, const void* host_kv, void* dev_
     free_ctx(c);
     return hip_error(e, "initial slot map upload");
   }
-  if (c->host_kv_dev && c->cap <= kDeltaMaxCap && d.NB <= kDeltaMaxNB) {
+  if (c->host_kv_dev && c->cap <= kDeltaMaxCap && d.NBs <= kDeltaMaxNB) {
     e = init_device_state(c);
     if (e != hipSuccess) {
       free_ctx(c);
@@ -300,10 +307,11 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
 
   // every pair's M_t is checked before any state changes, so a rejected call
   // leaves the context as it was (and the same step can be retried)
+  const int64_t nb_now = (c->cur_N + d.bs - 1) / d.bs;  // blocks of the cache as it is now
   for (int p = 0; p < d.pairs; ++p) {
     const int32_t* cur = c->host_M + (size_t)p * d.kb;
     for (int i = 0; i < d.kb; ++i)
-      if (cur[i] < 0 || cur[i] >= d.NB || (i > 0 && cur[i] <= cur[i - 1]))
+      if (cur[i] < 0 || cur[i] >= nb_now || (i > 0 && cur[i] <= cur[i - 1]))
         return set_error(TLS_ERR_STATE, "M_t of pair %d is not ascending block numbers in [0, NB)", p);
   }
 
@@ -315,8 +323,8 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   for (int p = 0; p < d.pairs; ++p) {
     const int32_t* cur = c->host_M + (size_t)p * d.kb;
     int32_t* prv = c->prev.data() + (size_t)p * d.kb;
-    int32_t* slot_of = c->slot_of.data() + (size_t)p * d.NB;
-    int64_t* last = c->last_sel.data() + (size_t)p * d.NB;
+    int32_t* slot_of = c->slot_of.data() + (size_t)p * d.NBs;
+    int64_t* last = c->last_sel.data() + (size_t)p * d.NBs;
     int32_t* owner = c->slot_owner.data() + (size_t)p * c->cap;
     // mark M_{t-1} u M_t
     if (++c->stamp == 0) {
@@ -356,7 +364,7 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
         slot_of[blk] = -1;
         owner[sl] = -1;
         free_slots.push_back(sl);
-        c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NB + blk, -1, 0});
+        c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NBs + blk, -1, 0});
       }
       std::sort(free_slots.begin(), free_slots.end());
     }
@@ -365,8 +373,8 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
       const int32_t blk = T[i], sl = free_slots[i];
       slot_of[blk] = sl;
       owner[sl] = blk;
-      c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NB + blk, sl, 0});
-      const int64_t src = ((int64_t)p * d.N + (int64_t)blk * d.bs) * d.row;
+      c->cur_changes.push_back(tls::MapItem{(int64_t)p * d.NBs + blk, sl, 0});
+      const int64_t src = ((int64_t)p * d.Ns + (int64_t)blk * d.bs) * d.row;
       const int64_t dst = ((int64_t)p * c->cap + sl) * (int64_t)c->block_elems;
       if (c->copy_mode == TLS_COPY_GATHER) {
         c->items[nitems++] = tls::CopyItem{src, dst};
@@ -411,6 +419,38 @@ int tls_prefetch_delta(tls_offload_t* c, int32_t step, const int32_t* dev_block_
   c->next_step = step + 1;
   c->total_copied += total;
   if (n_copied_opt) *n_copied_opt = total;
+  return TLS_OK;
+}
+
+int tls_offload_append(tls_offload_t* c, const void* new_kv, int32_t n_new, const int32_t* label_ch, void* summ,
+                       uint8_t* codes, float* scale, void* stream) {
+  clear_error();
+  if (!c || !new_kv || !label_ch || !summ || !codes || !scale) return set_error(TLS_ERR_INVALID_ARG, "NULL argument");
+  const Derived& d = c->d;
+  if (n_new < 1) return set_error(TLS_ERR_INVALID_ARG, "n_new must be >= 1");
+  if (c->cur_N + n_new > d.Ns)
+    return set_error(TLS_ERR_INVALID_ARG, "the cache length after the append (%lld) exceeds ctx_capacity (%lld)",
+                     (long long)(c->cur_N + n_new), (long long)d.Ns);
+  if (!aligned(new_kv, 16) || !aligned(summ, 4) || !aligned(scale, 4) || !aligned(label_ch, 4))
+    return set_error(TLS_ERR_INVALID_ARG, "new_kv must be 16-byte aligned, summ, scale and label_ch 4-byte");
+  if (!c->host_kv_dev)
+    return set_error(TLS_ERR_UNSUPPORTED, "host_kv has no device mapping (allocate it with hipHostMalloc)");
+  hipStream_t st = (hipStream_t)stream;
+  const uint16_t* rows = (const uint16_t*)new_kv;
+  // the rows into the host cache, written through its device mapping
+  hipError_t e = launch_append_rows(rows, const_cast<uint16_t*>(c->host_kv_dev), d.pairs, n_new, d.row, c->cur_N,
+                                    d.Ns, st);
+  // the summaries of the blocks they fall in and their codes and scales
+  if (e == hipSuccess)
+    e = launch_append_index(rows, n_new, label_ch, (uint16_t*)summ, codes, scale, d.pairs, d.Hkv, d.D, d.row, d.bs,
+                            d.r, c->cur_N, d.Ns, d.NBs, st);
+  // the resident copies of those blocks, in the map the next attention reads
+  if (e == hipSuccess)
+    e = launch_patch_slots(rows, n_new, d.pairs, c->cur_N, c->dev_map[c->next_step & 1], d.NBs, c->dev_cache, c->cap,
+                           d.bs, d.row, st);
+  if (e != hipSuccess) return hip_error(e, "append launch");
+  c->cur_N += n_new;
+  c->da.NBv = (int)((c->cur_N + d.bs - 1) / d.bs);
   return TLS_OK;
 }
 

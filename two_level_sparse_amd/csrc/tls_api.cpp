@@ -449,7 +449,7 @@ static int sparse_decode(const tls_shape_t* shape, const void* q, const void* kv
   }
   DecodeArgs a{(const uint16_t*)q, (const uint16_t*)kv_cache, slot_map, token_idx, part, out, lse_opt,
                d.pairs, d.B, d.Hq, d.Hkv, d.G, d.D, d.DV, d.row, d.v_off, d.bs, d.kt,
-               slot_map ? slots_per_pair : 0, d.N, d.NB, d.Ns, d.sm,
+               slot_map ? slots_per_pair : 0, d.N, d.NBs, d.Ns, d.sm,  // (NBs: the slot map's per-pair stride)
                g_prof_start[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed),
                g_prof_end[TLS_PROFILE_ATTENTION].load(std::memory_order_relaxed)};
   hipError_t e = launch_decode(a, pl, (hipStream_t)stream);

@@ -18,6 +18,11 @@ struct BuildArgs {
   int64_t j_first;   // first block to build (blocks j_first .. NB-1)
 };
 hipError_t launch_build(const BuildArgs& a, hipStream_t st);
+// Summaries, codes and scales after n new rows (rows [pairs, n, row]) were
+// appended at N0, from the new rows and the previous summaries only.
+hipError_t launch_append_index(const uint16_t* rows, int n, const int32_t* label_ch, uint16_t* summ, uint8_t* codes,
+                               float* scale, int pairs, int Hkv, int D, int row, int bs, int r, int64_t N0,
+                               int64_t Ns, int64_t NBs, hipStream_t st);
 // Copies n_new rows per pair from src [pairs, n_new, row] to positions N0.. of kv (stride Ns tokens).
 hipError_t launch_append_rows(const uint16_t* src, uint16_t* kv, int pairs, int n_new, int row, int64_t N0,
                               int64_t Ns, hipStream_t st);
@@ -107,14 +112,20 @@ struct DeltaArgs {
   unsigned long long* total;  // blocks moved since creation
   int32_t* err;               // set when a step cannot be planned
   int32_t* step_ctr;          // steps planned so far (the LRU clock), advanced by the copy kernel
-  int pairs, NB, kb, cap, bs, row;
+  int pairs, NB, kb, cap, bs, row;  // NB: the per-pair stride of last and the maps (blocks of the capacity)
+  int NBv;                    // blocks that exist now (a valid M_t holds block numbers below it)
   int copy_wgs;               // workgroups of the copy kernel
   int full;                   // 1: transfer every block of M_t (no reuse)
-  int64_t N, block_elems;
+  int64_t N, block_elems;     // N: the per-pair stride of the host cache in tokens (the capacity)
 };
 // prof_start/prof_end (may be null) are recorded around the copy kernel.
 hipError_t launch_device_delta(const DeltaArgs& a, const uint16_t* host_kv_dev, uint16_t* dev_cache, hipStream_t st,
                                hipEvent_t prof_start, hipEvent_t prof_end);
+
+// New rows [pairs, n, row] of tokens N0.. into the resident slots of their
+// blocks (where slot_map [pairs, NBs] has one).
+hipError_t launch_patch_slots(const uint16_t* rows, int n, int pairs, int64_t N0, const int32_t* slot_map,
+                              int64_t NBs, uint16_t* dev_cache, int cap, int bs, int row, hipStream_t st);
 
 hipError_t launch_gather_blocks(const uint16_t* host_kv_dev, uint16_t* dev_cache, const CopyItem* items, int nitems,
                                 const MapItem* map_items, int nmap, int32_t* slot_map, int64_t block_elems,

@@ -185,22 +185,30 @@ class StaggeredDecoder:
     started.
 
     `cache` holds the summaries and label cache on the device (its `kv` is not
-    read); `host_kv` is the full cache [B,Hkv,N,row] bf16 in pinned memory.
+    read); `host_kv` is the full cache [B,Hkv,Ns,row] bf16 in pinned memory, Ns
+    >= s.N its allocated length. With Ns > s.N the cache can grow:
+    `append(rows)` adds tokens between steps (host rows, index, resident
+    slots); `cache` then holds its index at the capacity's strides (a
+    GrowingCache).
     """
 
     def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None, stagger=True):
         self.s = s
+        self.capacity = int(host_kv.shape[2])
+        self.n = s.N
+        s_cap = s.with_(N=self.capacity)
         # stagger=False: the baseline without staggering -- each step selects
         # M_t, moves T_t and then attends over tokens of M_t, in order on the
         # caller's stream (the transfers are the same; their time is not hidden)
         self.stagger = stagger
         self.cache = cache
         self.host_kv = host_kv
-        self.dec = Decoder(s, device)
+        # buffers and workspaces for the largest length (Kb' and Kt' do not change as it grows)
+        self.dec = Decoder(s_cap, device)
         self.kb = self.dec.kb
         self.cap = 2 * self.kb
         self.dev_cache = torch.empty((s.B, s.Hkv, self.cap, s.bs, s.row), dtype=torch.bfloat16, device=device)
-        self.maps = [torch.full((s.B, s.Hkv, s.NB), -1, dtype=torch.int32, device=device) for _ in range(2)]
+        self.maps = [torch.full((s.B, s.Hkv, s_cap.NB), -1, dtype=torch.int32, device=device) for _ in range(2)]
         # M_t lives in mbuf[t % 3]; M_{-1} (the prologue's selection) in mbuf[2]
         self.mbuf = [torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device) for _ in range(3)]
         self.stage = torch.cuda.Stream(device=device)
@@ -215,10 +223,10 @@ class StaggeredDecoder:
         for ev in self.events + [self.m_ready]:
             ev.record()  # materialise the HIP events
         # prologue: M_{-1} = stage 1 of q_0, loaded synchronously
-        self.dec.select_blocks(q0, cache, block_idx=self.mbuf[2])
+        self.dec.select_blocks(q0, cache, block_idx=self.mbuf[2], shape=self.shape)
         torch.cuda.synchronize()
         init = self.mbuf[2].cpu().numpy().astype(np.int32)
-        self.ctx = tls_offload_create_ctx(self.dec.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
+        self.ctx = tls_offload_create_ctx(self.shape, host_kv, self.dev_cache, self.maps[0], self.maps[1], init)
         from . import TLS_COPY_DEVICE, TLS_COPY_FULL, tls_offload_get_copy_mode, tls_offload_set_copy_mode
         if copy_mode is not None:
             tls_offload_set_copy_mode(self.ctx, copy_mode)
@@ -227,9 +235,29 @@ class StaggeredDecoder:
         self.t = 0
         self.copied = []
 
+    @property
+    def shape(self):
+        """The calls' shape: the current length, strided by the capacity."""
+        return shape_of(self.s.with_(N=self.n), self.capacity)
+
     def selection(self, t):
         """Device buffer holding M_t (valid for three steps after step t)."""
         return self.mbuf[t % 3]
+
+    def append(self, rows):
+        """Append rows [B, Hkv, n, row] bf16 (device) to the cache before the
+        next step: tls_offload_append on the current stream, after the copies of
+        the last prefetch."""
+        from . import tls_offload_append
+        n = int(rows.shape[2])
+        main = torch.cuda.current_stream()
+        if self.t > 0:
+            main.wait_event(self.events[(self.t - 1) % 2])
+        c = self.cache
+        tls_offload_append(self.ctx, rows.contiguous(), n, c.label_ch, c.summ, c.codes, c.scale, main)
+        self.n += n
+        if isinstance(c, GrowingCache):
+            c.n = self.n
 
     def step(self, q_t, helper=None):
         """Enqueue step t; returns the output buffer [B, Hq, DV] (valid after sync).
@@ -247,9 +275,10 @@ class StaggeredDecoder:
         t = self.t
         main = torch.cuda.current_stream()
         mt = self.selection(t)
+        sh = self.shape
         self.stage.wait_stream(main)
         with torch.cuda.stream(self.stage):
-            self.dec.select_blocks(q_t, self.cache, stream=self.stage, block_idx=mt)
+            self.dec.select_blocks(q_t, self.cache, stream=self.stage, block_idx=mt, shape=sh)
         self.m_ready.record(self.stage)
         self.side.wait_stream(main)
         self.side.wait_event(self.m_ready)
@@ -265,8 +294,8 @@ class StaggeredDecoder:
             prefetch()
         if t > 0:
             main.wait_event(self.events[(t - 1) % 2])
-        self.dec.select_tokens(q_t, self.cache, block_idx=self.selection(t - 1))
-        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t), slots=self.cap)
+        self.dec.select_tokens(q_t, self.cache, block_idx=self.selection(t - 1), shape=sh)
+        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t), slots=self.cap, shape=sh)
         if th:
             th.join()
         self.copied.append(res.get("n", 0))
@@ -278,11 +307,12 @@ class StaggeredDecoder:
         t = self.t
         main = torch.cuda.current_stream()
         mt = self.selection(t)
-        self.dec.select_blocks(q_t, self.cache, block_idx=mt)
+        sh = self.shape
+        self.dec.select_blocks(q_t, self.cache, block_idx=mt, shape=sh)
         self.copied.append(tls_prefetch_delta(self.ctx, t, mt, main, self.events[t % 2]))
-        self.dec.select_tokens(q_t, self.cache, block_idx=mt)
+        self.dec.select_tokens(q_t, self.cache, block_idx=mt, shape=sh)
         # the map written by this step's transfer (that of step t+1) holds M_t
-        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t + 1), slots=self.cap)
+        self.dec.decode(q_t, self.dev_cache, slot_map=tls_offload_slot_map(self.ctx, t + 1), slots=self.cap, shape=sh)
         self.t += 1
         return self.dec.out
 
