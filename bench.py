@@ -261,6 +261,9 @@ def main():
                          "full = every selected block every step, the baseline without reuse)")
     ap.add_argument("--no-stagger", action="store_true",
                     help="offloaded workload: the baseline without staggering (select, transfer, attend in order)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="offloaded workload: layers stepped as one model, each its own offloaded cache and queries "
+                         "(layer l's transfer runs under the attention of the layers after it)")
     ap.add_argument("--mode", default="tls", choices=["tls", "quest", "ds", "dense"],
                     help="tls: the two-level step; quest: block stage only (every token of the kept blocks); "
                          "ds: token stage only (Kt tokens selected over the whole cache); "
@@ -279,6 +282,8 @@ def main():
     T.load_library()
     s = W.CONFIGS[args.config]
     if s.steps:
+        if args.layers > 1:
+            return bench_offload_layers(args, s)
         return bench_offload(args, s)
     s_data = s  # the cache and queries; s below is the shape the calls run with
     if args.mode == "quest":
@@ -614,6 +619,120 @@ def bench_offload(args, s):
     if not args.no_cpu and not args.no_stagger and used != "full":
         log("[bench] oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline_staggered(s, qs, kv, lab, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def bench_offload_layers(args, s):
+    """L layers of the offloaded workload stepped as one model (LayeredDecoder):
+    layer l's token stage and attention run after layer l-1's, its stage 1 and
+    transfer on the shared side streams, so a layer's transfer runs under the
+    attention of the layers after it. Every layer has its own device index
+    (summaries, label cache), resident cache and query sequence (its own
+    seed); the layers share one pinned host cache, whose contents only set the
+    selections (host reads are never cached on the device). A step = step t of
+    every layer; timed as one graph replay of all steps (device planning),
+    staggered and, for comparison, in order (select, transfer, attend per
+    layer); the host-copy kernels are timed alone with the library's events."""
+    import torch
+
+    import two_level_sparse_amd as T
+    from two_level_sparse_amd.runtime import Cache, LayeredDecoder, bf16
+
+    L, steps = args.layers, s.steps
+    log(f"[bench] {s.name} x {L} layers: generating inputs")
+    kv = W.gen_kv(s)
+    lab = W.label_channels(s, kv[0])
+    base = Cache(s, kv, lab).build()
+    torch.cuda.synchronize()
+    base.kv = None
+    caches = [base]
+    for _ in range(1, L):
+        c = Cache.__new__(Cache)
+        c.s, c.shape, c.kv, c.label_ch = s, base.shape, None, base.label_ch
+        c.summ, c.codes, c.scale = base.summ.clone(), base.codes.clone(), base.scale.clone()
+        caches.append(c)
+    torch.cuda.empty_cache()
+    host = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory()
+    del kv
+    q0s = [W.gen_q(s.with_(seed=s.seed + 101 * l)) for l in range(L)]
+    qd = [[bf16(q) for q in W.drift_queries(s, q0s[l], steps)] for l in range(L)]
+    stream = torch.cuda.current_stream()
+
+    def run(stagger):
+        ld = LayeredDecoder(s, caches, [host] * L, [qd[l][0] for l in range(L)], stagger=stagger)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            main = torch.cuda.current_stream()
+            for t in range(steps):
+                ld.step([qd[l][t] for l in range(L)])
+            main.wait_stream(ld.stage)
+            main.wait_stream(ld.side)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        moved = ld.total_copied()
+        ld.close()
+        del g
+        return a.elapsed_time(b) / steps, moved
+
+    log("[bench] warmup")
+    run(True)
+    reps = 3
+    log(f"[bench] timing {reps} x {steps} steps of {L} layers, staggered and in order")
+    t0 = time.perf_counter()
+    pipe = sorted(run(True)[0] for _ in range(reps))
+    serial = sorted(run(False)[0] for _ in range(reps))
+    wall = time.perf_counter() - t0
+    ms_pipe, ms_serial = pipe[len(pipe) // 2], serial[len(serial) // 2]
+    moved = run(True)[1]
+
+    # the host-copy kernels alone (events around each launch, eager steps behind a spin kernel)
+    ld = LayeredDecoder(s, caches, [host] * L, [qd[l][0] for l in range(L)])
+    torch.cuda.synchronize()
+    n_ev = min(steps, 16)
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(n_ev * L)]
+    torch.cuda._sleep(int(6e7))
+    for t in range(n_ev):
+        for l, d in enumerate(ld.layers):
+            T.tls_profile_events(T.TLS_PROFILE_HOST_COPY, *evs[t * L + l])
+            d.step(qd[l][t], helper=False)
+    T.tls_profile_events(T.TLS_PROFILE_HOST_COPY)
+    torch.cuda.synchronize()
+    copy_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ld.close()
+
+    block_bytes = s.bs * s.row * 2
+    h2d_step = moved * block_bytes / steps
+    hidden = (ms_serial - ms_pipe) / (L * copy_ms) if copy_ms > 0 else None
+    res = {
+        "metric": METRIC,
+        "value": round(s.B / (ms_pipe / 1e3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": steps,
+        "ms_per_step": round(ms_pipe, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} x {L} layers: batch {s.B}, {s.Hq} q heads / {s.Hkv} kv heads, head dim "
+                               f"{s.D}, context {s.N} per layer, block {s.bs}, Kb={s.Kb}, Kt={s.Kt}, full KV in pinned "
+                               f"host memory, {steps} staggered steps of every layer with query drift 0.1",
+                   "batch": s.B, "ctx_len": s.N, "layers": L, "offload": True, "graph": True, "repetitions": reps},
+        "layers": {"ms_per_step_staggered": round(ms_pipe, 5), "ms_per_step_in_order": round(ms_serial, 5),
+                   "ms_per_layer_step_staggered": round(ms_pipe / L, 5),
+                   "copy_kernel_ms_per_layer_step": round(copy_ms, 5),
+                   "copy_time_hidden_fraction": None if hidden is None else round(min(max(hidden, 0.0), 1.0), 4),
+                   "blocks_copied_per_step": round(moved / steps, 1), "h2d_bytes_per_step": int(h2d_step),
+                   "note": "hidden fraction = (in-order - staggered step time) / (L x copy-kernel time)"},
+        "roofline": None,
+        "wall_s": round(wall, 3),
+    }
     print(json.dumps(res), flush=True)
 
 

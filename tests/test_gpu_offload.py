@@ -57,6 +57,13 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None, qs=None):
             print(f"[gpu] staggered: {t + 1} of {steps} steps run", flush=True)
     total = sd.total_copied()
     sd.close()
+    return check_staggered(s, qs, kv, lab, built, pro, gM, gcounts, gblocks, gtok, gout, total, copy_mode)
+
+
+def check_staggered(s, qs, kv, lab, built, pro, gM, gcounts, gblocks, gtok, gout, total, copy_mode=None):
+    """The checks of run_staggered on one layer's recorded run (per step: M_t,
+    T_t, the token set, the output; total = blocks moved)."""
+    steps = len(gM)
     gM = np.stack(gM)
     own = oracle.staggered(s, qs, kv, lab, built)
     ref = oracle.staggered(s, qs, kv, lab, built, force_prologue=pro, force_M=gM)
@@ -93,6 +100,65 @@ def run_staggered(s, q0, kv, lab, steps, helper, copy_mode=None, qs=None):
         prev_blocks = gM[t]
     assert total == stats["moved"]
     return stats
+
+
+@pytest.mark.parametrize("mode", [2, 1])
+def test_layered_staggered_decode(mode):
+    """Three layers, each its own offloaded cache and query sequence, stepped
+    as one model (LayeredDecoder: shared stage and copy streams, layer l+1's
+    selection after layer l's attention): every layer against the oracle's
+    schedule for its own inputs, as in run_staggered. Device planning is also
+    captured as one graph of all layers' steps and replayed, with the same
+    outputs."""
+    from two_level_sparse_amd.runtime import Cache, LayeredDecoder, bf16
+    L, steps = 3, 12
+    shapes = [W.small_shape(B=2, Hq=8, Hkv=2, N=8192, bs=64, Kb=8, Kt=200, n_outlier=4, seed=60 + l) for l in range(L)]
+    q0s = [W.gen_q(sl) for sl in shapes]
+    kvs = [W.gen_kv(sl) for sl in shapes]
+    labs = [W.label_channels(sl, kv[0]) for sl, kv in zip(shapes, kvs)]
+    qss = [W.drift_queries(sl, q0, steps) for sl, q0 in zip(shapes, q0s)]
+    s = shapes[0]
+    caches = [Cache(sl, kv, lab).build() for sl, kv, lab in zip(shapes, kvs, labs)]
+    hosts = [torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).pin_memory() for kv in kvs]
+    ld = LayeredDecoder(s, caches, hosts, [bf16(q0) for q0 in q0s], copy_mode=mode)
+    pros = [to_np(d.selection(-1)).reshape(s.pairs, -1).copy() for d in ld.layers]
+    rec = [dict(M=[], counts=[], blocks=[], tok=[], out=[]) for _ in range(L)]
+    for t in range(steps):
+        outs = ld.step([bf16(qss[l][t]) for l in range(L)])
+        torch.cuda.synchronize()
+        for l, d in enumerate(ld.layers):
+            counts, blocks = d.last_delta()
+            rec[l]["M"].append(to_np(d.selection(t)).reshape(s.pairs, -1).copy())
+            rec[l]["counts"].append(counts.copy())
+            rec[l]["blocks"].append(blocks.copy())
+            rec[l]["tok"].append(to_np(d.dec.token_idx).reshape(s.pairs, -1).copy())
+            rec[l]["out"].append(to_np(outs[l]).reshape(s.pairs, s.G, s.DV).copy())
+    totals = [d.total_copied() for d in ld.layers]
+    ld.close()
+    for l in range(L):
+        built = oracle.decode(shapes[l], q0s[l], kvs[l], labs[l])
+        r = rec[l]
+        check_staggered(shapes[l], qss[l], kvs[l], labs[l], built, pros[l], r["M"], r["counts"], r["blocks"],
+                        r["tok"], r["out"], totals[l], mode)
+    if mode == 2:  # the same steps as one graph of every layer
+        ld = LayeredDecoder(s, caches, hosts, [bf16(q0) for q0 in q0s], copy_mode=mode)
+        qd = [[bf16(qss[l][t]) for l in range(L)] for t in range(steps)]
+        outs = [torch.empty((s.B, s.Hq, s.DV), dtype=torch.float32, device="cuda") for _ in range(L)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            main = torch.cuda.current_stream()
+            for t in range(steps):
+                res = ld.step(qd[t])
+                if t == steps - 1:
+                    for l in range(L):
+                        outs[l].copy_(res[l])
+            main.wait_stream(ld.stage)
+            main.wait_stream(ld.side)
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            np.testing.assert_array_equal(to_np(outs[l]).reshape(s.pairs, s.G, s.DV), rec[l]["out"][-1])
+        ld.close()
 
 
 @pytest.mark.parametrize("mode", [2, 0, 1])

@@ -192,7 +192,9 @@ class StaggeredDecoder:
     GrowingCache).
     """
 
-    def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None, stagger=True):
+    def __init__(self, s, cache, host_kv, q0, device="cuda", copy_mode=None, stagger=True, streams=None):
+        """streams: (stage, copy) streams to use instead of two of its own (the
+        layers of a LayeredDecoder share theirs)."""
         self.s = s
         self.capacity = int(host_kv.shape[2])
         self.n = s.N
@@ -211,8 +213,9 @@ class StaggeredDecoder:
         self.maps = [torch.full((s.B, s.Hkv, s_cap.NB), -1, dtype=torch.int32, device=device) for _ in range(2)]
         # M_t lives in mbuf[t % 3]; M_{-1} (the prologue's selection) in mbuf[2]
         self.mbuf = [torch.empty((s.B, s.Hkv, self.kb), dtype=torch.int32, device=device) for _ in range(3)]
-        self.stage = torch.cuda.Stream(device=device)
-        self.side = torch.cuda.Stream(device=device)
+        if streams is None:
+            streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))
+        self.stage, self.side = streams
         # the first launch on a new stream sets up its hardware queue, which
         # takes milliseconds: do it here rather than in the first step
         for st in (self.stage, self.side):
@@ -357,6 +360,55 @@ class StaggeredDecoder:
         if self.ctx:
             tls_offload_destroy(self.ctx)
             self.ctx = None
+
+
+class LayeredDecoder:
+    """Staggered decode of L layers, each with its own offloaded cache
+    (AsyncTLS pages, section 2B, across the layers of a model).
+
+    Layer l of step t runs as one StaggeredDecoder step: its token stage and
+    attention on the main stream, after layer l-1's attention (the data
+    dependency of a model: layer l's query comes from layer l-1's output);
+    its stage 1 for M^l_t on the shared stage stream, which waits for that
+    same point; its transfer T^l_t on the shared copy stream. So layer l's
+    transfer runs under the attention of the layers after it, and it has until
+    layer l of step t+1 -- a whole pass over the other layers -- to land. All
+    layers share the two side streams (no more hardware queues than one layer
+    uses)."""
+
+    def __init__(self, s, caches, host_kvs, q0s, device="cuda", copy_mode=None, stagger=True):
+        streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))
+        for st in streams:
+            with torch.cuda.stream(st):
+                torch.zeros(1, device=device)
+        self.layers = [StaggeredDecoder(s, c, h, q, device, copy_mode, stagger, streams=streams)
+                       for c, h, q in zip(caches, host_kvs, q0s)]
+        self.stage, self.side = streams
+
+    def step(self, q_layers):
+        """Step t of every layer in order; returns the layers' output buffers."""
+        return [d.step(q, helper=False) for d, q in zip(self.layers, q_layers)]
+
+    def capture(self, q_steps):
+        """One HIP graph of len(q_steps) steps of every layer (q_steps[t][l]);
+        planning must be on the GPU (see StaggeredDecoder.capture)."""
+        if not all(d.device_planned for d in self.layers):
+            raise RuntimeError("graph capture needs planning on the GPU (TLS_COPY_DEVICE or TLS_COPY_FULL)")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            main = torch.cuda.current_stream()
+            for qs in q_steps:
+                self.step(qs)
+            main.wait_stream(self.stage)
+            main.wait_stream(self.side)
+        return g
+
+    def total_copied(self):
+        return sum(d.total_copied() for d in self.layers)
+
+    def close(self):
+        for d in self.layers:
+            d.close()
 
 
 def tls_offload_create_ctx(shape, host_kv, dev_cache, map0, map1, init):
