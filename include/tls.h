@@ -33,8 +33,10 @@
  *   - Index outputs are sets, written in ascending order. Ties in a top-k go to
  *     the lower index.
  *   - Workspaces: `ws` must be at least tls_workspace_size(shape, which) bytes
- *     (256-byte aligned). Their contents on entry do not matter. Calls that
- *     share one workspace must not overlap in time.
+ *     (256-byte aligned). Their contents on entry do not matter, except for
+ *     the first 64 KiB of a TLS_WS_DECODE workspace and for TLS_WS_STEP
+ *     (see tls_sparse_decode and tls_decode_step). Calls that share one
+ *     workspace must not overlap in time.
  *
  * Layouts (row-major)
  *   q          [B, Hq, D]            bf16
@@ -173,7 +175,15 @@ int tls_select(const tls_shape_t *shape, const void *q, const void *summ, const 
  *   slot_map [B,Hkv,NBs] (int32 slot of each block, -1 = not resident; NBs =
  *   blocks of ctx_capacity, NB when the capacity is the length); every
  *   block holding a kept token must be resident.
- * Entries -1 in token_idx are skipped. lse_opt: NULL or [B,Hq] float. */
+ * Entries -1 in token_idx are skipped. lse_opt: NULL or [B,Hq] float.
+ * ws: tls_workspace_size(shape, TLS_WS_DECODE) bytes: 64 KiB of counters,
+ *   then the splits' partial results. The counters must be zero before the
+ *   first call (zero-fill the workspace once, e.g. one hipMemset); every call
+ *   that completes leaves them zero, so later calls need no clearing, and
+ *   calls of different shapes may share the workspace. A workspace written
+ *   by anything else in between must be cleared again. (With 128-channel K
+ *   and V rows the last workgroup of each (pair, head tile) merges the
+ *   splits, counting the workgroups done in these counters.) */
 int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_cache, const int32_t *slot_map,
                       int32_t slots_per_pair, const int32_t *token_idx, float *out, float *lse_opt, void *ws,
                       size_t ws_bytes, void *stream);
@@ -186,8 +196,9 @@ int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_ca
  * a caller workspace; the caller passes only inputs and outputs. A shape whose
  * partials need more (tls_workspace_size(shape, TLS_WS_DECODE) above
  * TLS_NOALLOC_SCRATCH_BYTES) returns TLS_ERR_WORKSPACE before anything is
- * launched. Nothing in the array needs clearing between calls (every partial
- * is written before it is read). Every call on one GPU shares that GPU's
+ * launched. Nothing in the array needs clearing: it starts zeroed, and every
+ * call that completes leaves its counters zero (every partial is written
+ * before it is read). Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (other streams, other threads)
  * race on it, and the caller must order them. The first call on each device
  * looks the array's device address up (hipGetSymbolAddress, which may load

@@ -242,6 +242,32 @@ def test_workspace_too_small_is_rejected():
     assert e.value.code == T.TLS_ERR_WORKSPACE
 
 
+def test_decode_workspace_counters_return_to_zero_across_shapes():
+    """The attention's per-group counters (first 64 KiB of the decode
+    workspace) are zero after every call, and calls of different shapes can
+    share one workspace: shapes A, B, A on one zero-filled workspace give, bit
+    for bit, the outputs of each shape's own workspace."""
+    import two_level_sparse_amd as T
+    runs = []
+    for name, seed in (("gqa4", 5), ("many_splits", 6)):
+        s = SMALL[name]
+        q, kv, lab = inputs(s, seed=seed)
+        run = GpuRun(s, q, kv, lab)
+        run.dec.step(run.qd, run.cache)
+        torch.cuda.synchronize()
+        runs.append((run, to_np(run.dec.out).copy(), to_np(run.dec.lse).copy()))
+    size = max(run.dec.ws_sizes[T.TLS_WS_DECODE] for run, _, _ in runs)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for run, ref_out, ref_lse in (runs[0], runs[1], runs[0]):
+        d = run.dec
+        d.out.zero_(); d.lse.zero_()
+        T.tls_sparse_decode(d.shape, run.qd, run.cache.kv, None, 0, d.token_idx, d.out, d.lse, ws, size)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(d.out), ref_out)
+        np.testing.assert_array_equal(to_np(d.lse), ref_lse)
+        assert not ws[:65536].any().item()
+
+
 def test_graph_replay_matches_eager():
     """The three calls captured in a HIP graph: every replay equals the eager step."""
     s = SMALL["gqa4"]

@@ -18,9 +18,16 @@
 //     token per 16-byte load, so one wave load covers 64/(DV/8) whole rows; the
 //     probabilities cross from the MFMA layout through LDS.
 // The 4 waves merge their (m, l, o) in LDS and the workgroup writes one
-// partial. k_merge then combines the splits of every head. (A fused
-// last-workgroup merge would need an agent-scope release per workgroup, which
-// on this part writes back the XCD's whole L2; a second launch is cheaper.)
+// partial. k_merge then combines the splits of every head -- except after
+// k_attend_pv, whose last workgroup of each (pair, head tile) merges the
+// splits itself: every workgroup stores its partial with agent-scope atomic
+// stores, waits for them and counts itself in with an agent-scope atomic add
+// (a counter per group at the start of the workspace); the workgroup that
+// completes the count loads the partials with agent-scope atomic loads,
+// merges them and sets the counter back to zero. Those accesses are coherent
+// across the XCDs' L2 caches without writing any of them back (an
+// agent-scope release fence would write back the XCD's whole L2, which costs
+// more than the second launch it saves).
 #include <type_traits>
 
 #include "tls_attn_dev.h"
@@ -500,14 +507,67 @@ __global__ __launch_bounds__(256, 2) void k_attend_gqa(const uint16_t* __restric
   }
 }
 
+constexpr int kMaxSplits = 64;      // split limit of the general attention kernels
+constexpr int kMlaMaxSplits = 128;  // of the latent attention (512 tokens per split at most)
+constexpr int kMergePre = 8;
+// The log-sum-exp merge of one head's nsplit partials on value channels
+// c .. c+3 (hd: the head in split 0; splits SP floats apart): M = max of the
+// splits' m, L = sum of l_s 2^(m_s - M), o = sum of o_s 2^(m_s - M).
+// kMergePre splits per round, all their loads in flight together; the running
+// max and sums are rescaled when a round raises the max. COHERENT: the
+// partials are read with agent-scope atomic loads (written in this launch).
+template <bool COHERENT>
+__device__ __forceinline__ void merge_splits(const float* hd, int64_t SP, int nsplit, int c, float& M, float& L,
+                                             f32x4& o) {
+  M = -INFINITY;
+  L = 0.0f;
+  o = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += kMergePre) {
+    float2 ml[kMergePre];
+    f32x4 ov[kMergePre];
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+      const int64_t off = (int64_t)min(s0 + u, nsplit - 1) * SP;
+      if constexpr (COHERENT) {
+        ml[u] = load_agent2(hd + off);
+        const float2 o01 = load_agent2(hd + off + kPartHdr + c), o23 = load_agent2(hd + off + kPartHdr + c + 2);
+        ov[u] = f32x4{o01.x, o01.y, o23.x, o23.y};
+      } else {
+        ml[u] = *reinterpret_cast<const float2*>(hd + off);
+        ov[u] = *reinterpret_cast<const f32x4*>(hd + off + kPartHdr + c);
+      }
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) cm = fmaxf(cm, ml[u].x);  // clamped repeats leave the max as it is
+    if (cm != M) {
+      const float r = M == -INFINITY ? 0.0f : exp2f(M - cm);
+      L *= r;
+      o *= r;
+      M = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u)
+      if (s0 + u < nsplit) {
+        const float w = ml[u].x == -INFINITY ? 0.0f : exp2f(ml[u].x - M);
+        L += ml[u].y * w;
+        o += ov[u] * w;
+      }
+  }
+}
+
 // k_attend_pv: attend_pv_range over split blockIdx.x (tps tokens) of head tile
-// blockIdx.y of pair blockIdx.z.
+// blockIdx.y of pair blockIdx.z; the last workgroup of each (pair, head tile)
+// to finish merges the splits into out and lse (cnt: one counter per group,
+// zero before the launch and again after it).
 template <int HT, bool SMAP>
 __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                       const int32_t* __restrict__ slot_map,
                                                       const int32_t* __restrict__ token_idx, float* __restrict__ part,
-                                                      int Hq, int Hkv, int G, int64_t N, int64_t Ns, int bs, int64_t NB,
-                                                      int slots, int kt, int tps, int nsplit, int nht, float qk_scale) {
+                                                      int* __restrict__ cnt, float* __restrict__ out,
+                                                      float* __restrict__ lse, int Hq, int Hkv, int G, int64_t N,
+                                                      int64_t Ns, int bs, int64_t NB, int slots, int kt, int tps,
+                                                      int nsplit, int nht, float qk_scale) {
   __shared__ __attribute__((aligned(1024))) uint8_t tA[4][kPvTile * kPvRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t tB[4][kPvTile * kPvRowBytes];
   __shared__ int32_t rows[4][kPvMaxTps / 4];  // wave w: its tiles' rows, tile m at [16m, 16m+16)
@@ -516,10 +576,34 @@ __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict
   const int split = blockIdx.x, ht = blockIdx.y, p = blockIdx.z;
   const int t_begin = split * tps;
   const int t_end = min(t_begin + tps, kt);
-  float* dst = part + (((int64_t)p * nht + ht) * nsplit + split) * HT * (128 + kPartHdr);
-  attend_pv_range<HT, SMAP, kPvMaxTps / 4>(q, kv, slot_map, token_idx + (int64_t)p * kt + t_begin,
-                                           max(t_end - t_begin, 0), dst, Hq, Hkv, G, N, Ns, bs, NB, slots, p, ht,
-                                           qk_scale, tA, tB, rows, c_lds, ml_lds);
+  constexpr int PS = 128 + kPartHdr, SP = HT * PS;
+  float* grp = part + ((int64_t)p * nht + ht) * nsplit * SP;
+  attend_pv_range<HT, SMAP, kPvMaxTps / 4, true>(q, kv, slot_map, token_idx + (int64_t)p * kt + t_begin,
+                                                 max(t_end - t_begin, 0), grp + (int64_t)split * SP, Hq, Hkv, G, N,
+                                                 Ns, bs, NB, slots, p, ht, qk_scale, tA, tB, rows, c_lds, ml_lds);
+  // count this workgroup in once all of its partial is stored
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int s_last;
+  int* ctr = cnt + (int64_t)p * nht + ht;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // the last one: merge the group's splits, as k_merge does
+  const int b = p / Hkv, h = p % Hkv;
+  for (int e = threadIdx.x; e < HT * 32; e += 256) {
+    const int hh = e >> 5, c = (e & 31) * 4, g = ht * HT + hh;
+    if (g >= G) continue;
+    float M, L;
+    f32x4 o;
+    merge_splits<true>(grp + (int64_t)hh * PS, SP, nsplit, c, M, L, o);
+    const int64_t row = (int64_t)b * Hq + (int64_t)h * G + g;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (lse && c == 0) lse[row] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    *reinterpret_cast<f32x4*>(out + row * 128 + c) = o * inv;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // k_attend_mla: the latent-attention shape (K rows of 576, V = their first
@@ -783,9 +867,6 @@ __global__ __launch_bounds__(256, 2) void k_attend_mla(const uint16_t* __restric
 // thread forms its head's split weights 2^(m_s - M) itself from the splits'
 // (m, l), loaded together with its float4 of o, kMergePre splits per round:
 // no LDS and no barrier.
-constexpr int kMaxSplits = 64;      // split limit of the general attention kernels
-constexpr int kMlaMaxSplits = 128;  // of the latent attention (512 tokens per split at most)
-constexpr int kMergePre = 8;
 template <int DV, int HT>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, float* __restrict__ out,
                                                float* __restrict__ lse, int Hq, int Hkv, int G, int nht, int nsplit) {
@@ -800,36 +881,9 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part, f
   const bool active = e < HT * (DV / 4) && g < G;
   // head hh of split 0: (m, l, -, -, o[DV])
   const float* hd = part + ((int64_t)p * nht + ht) * nsplit * SP + (int64_t)hh * PS;
-  // kMergePre splits per round, all their loads in flight together; the
-  // running max and sums are rescaled when a round raises the max
-  float M = -INFINITY, L = 0.0f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit; s0 += kMergePre) {
-    float2 ml[kMergePre];
-    f32x4 ov[kMergePre];
-#pragma unroll
-    for (int u = 0; u < kMergePre; ++u) {
-      const int64_t off = (int64_t)min(s0 + u, nsplit - 1) * SP;
-      ml[u] = *reinterpret_cast<const float2*>(hd + off);
-      ov[u] = *reinterpret_cast<const f32x4*>(hd + off + kPartHdr + c);
-    }
-    float cm = M;
-#pragma unroll
-    for (int u = 0; u < kMergePre; ++u) cm = fmaxf(cm, ml[u].x);  // clamped repeats leave the max as it is
-    if (cm != M) {
-      const float r = M == -INFINITY ? 0.0f : exp2f(M - cm);
-      L *= r;
-      o *= r;
-      M = cm;
-    }
-#pragma unroll
-    for (int u = 0; u < kMergePre; ++u)
-      if (s0 + u < nsplit) {
-        const float w = ml[u].x == -INFINITY ? 0.0f : exp2f(ml[u].x - M);
-        L += ml[u].y * w;
-        o += ov[u] * w;
-      }
-  }
+  float M, L;
+  f32x4 o;
+  merge_splits<false>(hd, SP, nsplit, c, M, L, o);
   if (!active) return;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   if (lse && c == 0) lse[(int64_t)b * Hq + (int64_t)h * G + g] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
@@ -910,11 +964,17 @@ static void prof_mark(hipEvent_t ev, hipStream_t st) {
   if (ev) (void)hipEventRecord(ev, st);
 }
 
+// The decode workspace: the group counters, then the partials.
+static int* ws_counters(const DecodeArgs& a) { return reinterpret_cast<int*>(a.part); }
+static float* ws_partials(const DecodeArgs& a) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(a.part) + kDecodeCntBytes);
+}
+
 template <int DV, int HT>
 static hipError_t launch_merge(const DecodeArgs& a, const DecodePlan& pl, hipStream_t st) {
   dim3 mgrid((unsigned)((HT * DV / 4 + 255) / 256), (unsigned)pl.nht, (unsigned)a.pairs);
-  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)a.part, a.out, a.lse, a.Hq, a.Hkv,
-                     a.G, pl.nht, pl.nsplit);
+  hipLaunchKernelGGL((k_merge<DV, HT>), mgrid, dim3(256), 0, st, (const float*)ws_partials(a), a.out, a.lse, a.Hq,
+                     a.Hkv, a.G, pl.nht, pl.nsplit);
   return hipGetLastError();
 }
 
@@ -925,28 +985,29 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
   prof_mark(a.prof_start, st);
   if constexpr (D == 128 && DV == 128) {
     if (pl.pv) {
+      // (the split merge runs inside the kernel)
       if (a.slot_map)
         hipLaunchKernelGGL((k_attend_pv<HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                           (float*)a.part, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit,
-                           pl.nht, a.sm_scale * kLog2e);
+                           ws_partials(a), ws_counters(a), a.out, a.lse, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB,
+                           a.slots, a.kt, pl.tps, pl.nsplit, pl.nht, a.sm_scale * kLog2e);
       else
         hipLaunchKernelGGL((k_attend_pv<HT, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                           (float*)a.part, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit,
-                           pl.nht, a.sm_scale * kLog2e);
+                           ws_partials(a), ws_counters(a), a.out, a.lse, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB,
+                           a.slots, a.kt, pl.tps, pl.nsplit, pl.nht, a.sm_scale * kLog2e);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       prof_mark(a.prof_end, st);
-      return launch_merge<DV, HT>(a, pl, st);
+      return hipSuccess;
     }
   }
   if constexpr (D <= 128) {  // wider rows: the per-lane buffers of k_attend_gqa would spill
     if (a.slot_map)
       hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         ws_partials(a), a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                          pl.nsplit, pl.nht, a.sm_scale * kLog2e);
     else
       hipLaunchKernelGGL((k_attend_gqa<D, DV, HT, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                         (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                         ws_partials(a), a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                          pl.nsplit, pl.nht, a.sm_scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -955,11 +1016,11 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
   }
   if (a.slot_map)
     hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       ws_partials(a), a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   else
     hipLaunchKernelGGL((k_attend<D, DV, HT, PRE, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                       (float*)a.part, a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
+                       ws_partials(a), a.Hq, a.Hkv, a.G, a.row, a.v_off, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps,
                        pl.nsplit, pl.nht, a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -983,11 +1044,11 @@ static hipError_t go_decode_mla(const DecodeArgs& a, const DecodePlan& pl, hipSt
   dim3 grid((unsigned)pl.nsplit, (unsigned)pl.nht, (unsigned)a.pairs);
   prof_mark(a.prof_start, st);
   if (a.slot_map)
-    hipLaunchKernelGGL(k_attend_mla<true>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
+    hipLaunchKernelGGL(k_attend_mla<true>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, ws_partials(a),
                        a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
                        a.sm_scale * kLog2e);
   else
-    hipLaunchKernelGGL(k_attend_mla<false>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, (float*)a.part,
+    hipLaunchKernelGGL(k_attend_mla<false>, grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx, ws_partials(a),
                        a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, a.kt, pl.tps, pl.nsplit, pl.nht,
                        a.sm_scale * kLog2e);
   hipError_t e = hipGetLastError();

@@ -107,7 +107,7 @@ size_t ws_bytes(const Derived& d, int which) {
     case TLS_WS_DECODE: {
       DecodePlan pl;
       plan_decode(d.pairs, d.G, d.D, d.DV, d.v_off == 0, d.kt, &pl);
-      return round_up(pl.part_bytes);
+      return kDecodeCntBytes + round_up(pl.part_bytes);  // group counters, then the partials
     }
     case TLS_WS_STEP: {
       if (!step_supported(d.G, d.D, d.DV, d.v_off == 0, d.bs, d.r, d.NB, d.kb, d.kt)) return 0;

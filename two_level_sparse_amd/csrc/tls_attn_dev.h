@@ -45,8 +45,9 @@ __device__ __forceinline__ int pv_swz(int r) { return 2 * (r & 7) | ((r >> 3) & 
 // dst. LDS (separate objects, so that reading one tile buffer does not wait
 // for the loads into the other): tA and tB the wave-private tile buffers, rows
 // the waves' token rows, c_lds and ml_lds the rescale factors and (m, l) of
-// the four waves.
-template <int HT, bool SMAP, int RPW>
+// the four waves. COHERENT: the partial is stored with agent-scope atomic
+// stores (store_agent), for a reader in another workgroup of the same launch.
+template <int HT, bool SMAP, int RPW, bool COHERENT = false>
 __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map, const int32_t* tix, int ntok,
                                                 float* __restrict__ dst, int Hq, int Hkv, int G, int64_t N,
@@ -234,7 +235,10 @@ __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, 
       const float mw = ml_lds[w][tid][0];
       l += mw == -INFINITY ? 0.0f : ml_lds[w][tid][1] * exp2f(mw - ms);
     }
-    *reinterpret_cast<f32x4*>(dst + tid * (DV + kPartHdr)) = f32x4{ms, l, 0.0f, 0.0f};
+    if constexpr (COHERENT)
+      store_agent2(dst + tid * (DV + kPartHdr), ms, l);
+    else
+      *reinterpret_cast<f32x4*>(dst + tid * (DV + kPartHdr)) = f32x4{ms, l, 0.0f, 0.0f};
   }
   // thread (channel c, heads 8*(tid/128) ..): the sum over the four waves
   {
@@ -248,7 +252,13 @@ __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, 
       for (int w = 1; w < 4; ++w) acc += reinterpret_cast<const f32x4*>(tA[w])[c * 4 + g4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * g4 + i < HT) dst[(4 * g4 + i) * (DV + kPartHdr) + kPartHdr + c] = acc[i];
+        if (4 * g4 + i < HT) {
+          float* d = &dst[(4 * g4 + i) * (DV + kPartHdr) + kPartHdr + c];
+          if constexpr (COHERENT)
+            store_agent(d, acc[i]);
+          else
+            *d = acc[i];
+        }
     }
   }
 }

@@ -189,6 +189,25 @@ __device__ __forceinline__ void load_row_f32(const float* row, int n, int first,
   }
 }
 
+// Relaxed atomic accesses at agent scope (global_store / global_load with
+// sc1): coherent between the workgroups of one launch whatever XCDs they run
+// on, without writing back or invalidating any L2. One workgroup publishes
+// data this way, waits for its stores (s_waitcnt) and then counts with an
+// agent-scope atomic; the workgroup that reads the final count loads the data
+// the same way.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent2(float* p, float a, float b) {  // p 8-byte aligned
+  const uint64_t w = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {  // p 8-byte aligned
+  const uint64_t w = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32))};
+}
+
 // s_waitcnt vmcnt(N): at most N vector memory loads of this wave in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -68,7 +68,7 @@ struct DecodeArgs {
   const uint16_t* kv;
   const int32_t* slot_map;  // NULL = identity
   const int32_t* token_idx;
-  void* part;               // workspace: partial results of the splits
+  void* part;               // workspace: group counters, then the partial results of the splits
   float* out;
   float* lse;               // may be NULL
   int pairs, B, Hq, Hkv, G, D, DV, row, v_off, bs, kt, slots;
@@ -76,11 +76,17 @@ struct DecodeArgs {
   float sm_scale;
   hipEvent_t prof_start, prof_end;  // recorded around the attention kernel when not null
 };
+// Decode workspace: kDecodeCntBytes of per-group counters (the fused merge
+// of k_attend_pv; zero before a launch, zero after it), then the partials.
+// The region has the same size and place for every shape, so calls of
+// different shapes can share one workspace.
+constexpr size_t kDecodeCntBytes = (size_t)64 << 10;
+constexpr int kDecodeMaxGroups = (int)(kDecodeCntBytes / sizeof(int));
 struct DecodePlan {
   int HT, nht, tps, nsplit;
   int mla;            // 1: the MFMA latent-attention kernel (D 576, DV 512, HT 32)
-  int pv;             // 1: the MFMA kernel for 128-channel K and V rows (k_attend_pv)
-  size_t part_bytes;  // partial results (m, l, o) per split
+  int pv;             // 1: the MFMA kernel for 128-channel K and V rows (k_attend_pv, merge fused)
+  size_t part_bytes;  // partial results (m, l, o) per split (after the counters)
 };
 // Always succeeds for the shapes the API accepts.
 void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, DecodePlan* plan);

@@ -109,7 +109,8 @@ class Decoder:
             raise ValueError(f"invalid shape for libtls: {s}")
         # (a zero TOKENS/SELECT size: more candidates than the token stage takes; select_tokens then fails;
         # a zero STEP size: a shape the one-launch step does not cover)
-        # zero-filled: the one-launch step's workspace must start cleared
+        # zero-filled: the one-launch step's workspace, and the counters at the start of the
+        # attention's, must start cleared (every call leaves them so)
         self.ws = {w: torch.zeros(max(n, 256), dtype=torch.uint8, device=device) for w, n in self.ws_sizes.items()}
         self.one_launch = self.ws_sizes[TLS_WS_STEP] > 0
 
