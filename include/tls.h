@@ -42,7 +42,7 @@
  *   q          [B, Hq, D]            bf16
  *   kv         [B, Hkv, N, row]      bf16; row = D + DV (K then V) or, when
  *                                    v_is_k_prefix, row = D and V[t] = K[t, 0:DV]
- *   label_ch   [Hkv, r]              int32, ascending channel numbers
+ *   label_ch   [Hkv, r]              int32, ascending channel numbers in [0, D)
  *   summ       [B, Hkv, NT, D/32, 2, 4, 16, 8]  bf16, NT = ceil(NBs / 16) with
  *                                    NBs = ceil(ctx_capacity / bs) (NB when the
  *                                    capacity is the length): the
