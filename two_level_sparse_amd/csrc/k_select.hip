@@ -854,10 +854,17 @@ static void go_score_tokens_sel_ut(const TokenSelectArgs& a, const float* S, int
 template <int MT, int RB>
 static void go_score_tokens_sel(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx, float* A,
                                 hipStream_t st) {
-  if constexpr (MT >= 4)
+  if constexpr (MT >= 4) {
     go_score_tokens_sel_ut<MT, RB, 4>(a, S, NB, block_idx, A, st);
-  else
-    go_score_tokens_sel_ut<MT, RB, 16>(a, S, NB, block_idx, A, st);
+  } else {
+    // 1024 candidates per workgroup, or 512 where that leaves CUs without a
+    // workgroup (each workgroup selects the pair's blocks itself first)
+    const int64_t wgs = (int64_t)((a.kb * a.bs + 1023) / 1024) * a.pairs;
+    if (wgs < 256)
+      go_score_tokens_sel_ut<MT, RB, 8>(a, S, NB, block_idx, A, st);
+    else
+      go_score_tokens_sel_ut<MT, RB, 16>(a, S, NB, block_idx, A, st);
+  }
 }
 
 template <int MT>
