@@ -446,10 +446,47 @@ def main():
         "index_build": build_time(s_data, base) if args.mode != "dense" else None,
         "wall_s": round(wall, 3),
     }
+    res["peaks_measured"] = measured_peaks()
     if not args.no_cpu and args.mode == "tls":
         log("[bench] oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline(s, q0, kv, lab, args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def measured_peaks():
+    """What this GPU reaches on plain work, beside the published peaks that the
+    roofline fractions use: a 1 GiB device-to-device copy (2 GiB of HBM
+    traffic, torch's copy kernel) and an 8192^3 bf16 GEMM (hipBLASLt through
+    torch), best of six each."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(fn):
+        t = []
+        for _ in range(6):
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        return min(t)
+
+    src = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = best_ms(lambda: dst.copy_(src))
+    copy_gbs = 2 * src.numel() * 4 / (copy_ms / 1e3) / 1e9
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    gemm_ms = best_ms(lambda: torch.mm(x, y))
+    tflops = 2.0 * n ** 3 / (gemm_ms / 1e3) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "bf16_gemm_TFLOPs": round(tflops, 1), "bf16_gemm_frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "how": "best of 6: a 1 GiB device-to-device copy (read + write) and an 8192^3 bf16 torch.mm, "
+                   "after the timed region"}
 
 
 PCIE5_X16_GBS = 64.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b coding
