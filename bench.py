@@ -446,7 +446,8 @@ def main():
         "index_build": build_time(s_data, base) if args.mode != "dense" else None,
         "wall_s": round(wall, 3),
     }
-    res["peaks_measured"] = measured_peaks()
+    if not args.calibrate_copy:  # (a counter run keeps its calibration copy the last copy)
+        res["peaks_measured"] = measured_peaks()
     if not args.no_cpu and args.mode == "tls":
         log("[bench] oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline(s, q0, kv, lab, args.cpu_budget)
