@@ -268,6 +268,32 @@ def test_decode_workspace_counters_return_to_zero_across_shapes():
         assert not ws[:65536].any().item()
 
 
+def test_split_merge_reads_this_calls_partials():
+    """The split merge inside the 128-channel attention hands the partials from
+    workgroup to workgroup (on any XCDs) within the launch: calls on one
+    workspace alternating between two queries each give, bit for bit, the
+    first output of their query -- a merge that read a partial left by the
+    previous call would mix them."""
+    from two_level_sparse_amd.runtime import bf16
+    s = SMALL["many_splits"]
+    q, kv, lab = inputs(s, seed=8)
+    run = GpuRun(s, q, kv, lab)
+    d = run.dec
+    d.step(run.qd, run.cache)
+    q2 = bf16(W.gen_q(s.with_(seed=s.seed + 50)))
+    torch.cuda.synchronize()
+    refs = []
+    for qq in (run.qd, q2):
+        d.decode(qq, run.cache.kv)
+        torch.cuda.synchronize()
+        refs.append(to_np(d.out).copy())
+    assert np.abs(refs[0] - refs[1]).max() > 1e-3  # the two outputs differ
+    for i in range(60):
+        d.decode((run.qd, q2)[i % 2], run.cache.kv)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(d.out), refs[i % 2])
+
+
 def test_graph_replay_matches_eager():
     """The three calls captured in a HIP graph: every replay equals the eager step."""
     s = SMALL["gqa4"]
