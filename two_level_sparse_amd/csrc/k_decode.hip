@@ -557,10 +557,11 @@ __device__ __forceinline__ void merge_splits(const float* hd, int64_t SP, int ns
 }
 
 // k_attend_pv: attend_pv_range over split blockIdx.x (tps tokens) of head tile
-// blockIdx.y of pair blockIdx.z; the last workgroup of each (pair, head tile)
-// to finish merges the splits into out and lse (cnt: one counter per group,
-// zero before the launch and again after it).
-template <int HT, bool SMAP>
+// blockIdx.y of pair blockIdx.z. FUSED: the last workgroup of each (pair,
+// head tile) to finish merges the splits into out and lse (cnt: one counter
+// per group, zero before the launch and again after it); otherwise k_merge
+// does, in a launch of its own.
+template <int HT, bool SMAP, bool FUSED>
 __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                       const int32_t* __restrict__ slot_map,
                                                       const int32_t* __restrict__ token_idx, float* __restrict__ part,
@@ -578,9 +579,10 @@ __global__ __launch_bounds__(256, 2) void k_attend_pv(const uint16_t* __restrict
   const int t_end = min(t_begin + tps, kt);
   constexpr int PS = 128 + kPartHdr, SP = HT * PS;
   float* grp = part + ((int64_t)p * nht + ht) * nsplit * SP;
-  attend_pv_range<HT, SMAP, kPvMaxTps / 4, true>(q, kv, slot_map, token_idx + (int64_t)p * kt + t_begin,
-                                                 max(t_end - t_begin, 0), grp + (int64_t)split * SP, Hq, Hkv, G, N,
-                                                 Ns, bs, NB, slots, p, ht, qk_scale, tA, tB, rows, c_lds, ml_lds);
+  attend_pv_range<HT, SMAP, kPvMaxTps / 4, FUSED>(q, kv, slot_map, token_idx + (int64_t)p * kt + t_begin,
+                                                  max(t_end - t_begin, 0), grp + (int64_t)split * SP, Hq, Hkv, G, N,
+                                                  Ns, bs, NB, slots, p, ht, qk_scale, tA, tB, rows, c_lds, ml_lds);
+  if constexpr (!FUSED) return;
   // count this workgroup in once all of its partial is stored
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -912,6 +914,7 @@ void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, De
     if (tps > kMlaMaxTps) tps = kMlaMaxTps;  // kt <= kMlaMaxSplits * kMlaMaxTps keeps nsplit in range
     plan->mla = 1;
     plan->pv = 0;
+    plan->fused = 0;
     plan->HT = kMlaHeads;
     plan->nht = nht;
     plan->tps = tps;
@@ -941,6 +944,11 @@ void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, De
     plan->nht = nht;
     plan->tps = tps;
     plan->nsplit = (kt + tps - 1) / tps;
+    // the split merge inside the launch pays when every workgroup is resident
+    // at once (two per CU): with more, each workgroup's wait for its stores and
+    // its count would recur round after round (the dense 128k launch, 4096
+    // workgroups: 818 us fused against 734 with k_merge)
+    plan->fused = (int64_t)units * plan->nsplit <= kFuseMaxWorkgroups;
     plan->part_bytes = (size_t)pairs * nht * plan->nsplit * HT * (DV + kPartHdr) * sizeof(float);
     return;
   }
@@ -952,6 +960,7 @@ void plan_decode(int pairs, int G, int D, int DV, bool v_is_k_prefix, int kt, De
   const int nsplit = (kt + tps - 1) / tps;
   plan->mla = 0;
   plan->pv = 0;
+  plan->fused = 0;
   plan->HT = HT;
   plan->nht = nht;
   plan->tps = tps;
@@ -985,19 +994,20 @@ static hipError_t go_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream
   prof_mark(a.prof_start, st);
   if constexpr (D == 128 && DV == 128) {
     if (pl.pv) {
-      // (the split merge runs inside the kernel)
-      if (a.slot_map)
-        hipLaunchKernelGGL((k_attend_pv<HT, true>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                           ws_partials(a), ws_counters(a), a.out, a.lse, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB,
-                           a.slots, a.kt, pl.tps, pl.nsplit, pl.nht, a.sm_scale * kLog2e);
-      else
-        hipLaunchKernelGGL((k_attend_pv<HT, false>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,
-                           ws_partials(a), ws_counters(a), a.out, a.lse, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB,
-                           a.slots, a.kt, pl.tps, pl.nsplit, pl.nht, a.sm_scale * kLog2e);
+#define TLS_PV(SM, FU)                                                                                          \
+  hipLaunchKernelGGL((k_attend_pv<HT, SM, FU>), grid, dim3(256), 0, st, a.q, a.kv, a.slot_map, a.token_idx,       \
+                     ws_partials(a), ws_counters(a), a.out, a.lse, a.Hq, a.Hkv, a.G, a.N, a.Ns, a.bs, a.NB, a.slots, \
+                     a.kt, pl.tps, pl.nsplit, pl.nht, a.sm_scale * kLog2e)
+      if (a.slot_map) {
+        if (pl.fused) TLS_PV(true, true); else TLS_PV(true, false);
+      } else {
+        if (pl.fused) TLS_PV(false, true); else TLS_PV(false, false);
+      }
+#undef TLS_PV
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       prof_mark(a.prof_end, st);
-      return hipSuccess;
+      return pl.fused ? hipSuccess : launch_merge<DV, HT>(a, pl, st);  // (fused: merged inside the kernel)
     }
   }
   if constexpr (D <= 128) {  // wider rows: the per-lane buffers of k_attend_gqa would spill

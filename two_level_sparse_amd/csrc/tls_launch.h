@@ -82,10 +82,12 @@ struct DecodeArgs {
 // different shapes can share one workspace.
 constexpr size_t kDecodeCntBytes = (size_t)64 << 10;
 constexpr int kDecodeMaxGroups = (int)(kDecodeCntBytes / sizeof(int));
+constexpr int64_t kFuseMaxWorkgroups = 512;  // the fused merge: one round of workgroups (two per CU)
 struct DecodePlan {
   int HT, nht, tps, nsplit;
   int mla;            // 1: the MFMA latent-attention kernel (D 576, DV 512, HT 32)
-  int pv;             // 1: the MFMA kernel for 128-channel K and V rows (k_attend_pv, merge fused)
+  int pv;             // 1: the MFMA kernel for 128-channel K and V rows (k_attend_pv)
+  int fused;          // 1: k_attend_pv merges the splits itself (at most kFuseMaxWorkgroups workgroups)
   size_t part_bytes;  // partial results (m, l, o) per split (after the counters)
 };
 // Always succeeds for the shapes the API accepts.
