@@ -182,8 +182,9 @@ int tls_select(const tls_shape_t *shape, const void *q, const void *summ, const 
  *   that completes leaves them zero, so later calls need no clearing, and
  *   calls of different shapes may share the workspace. A workspace written
  *   by anything else in between must be cleared again. (With 128-channel K
- *   and V rows the last workgroup of each (pair, head tile) merges the
- *   splits, counting the workgroups done in these counters.) */
+ *   and V rows and at most 512 attention workgroups, the last workgroup of
+ *   each (pair, head tile) merges the splits, counting the workgroups done in
+ *   these counters; otherwise a merge kernel follows the attention.) */
 int tls_sparse_decode(const tls_shape_t *shape, const void *q, const void *kv_cache, const int32_t *slot_map,
                       int32_t slots_per_pair, const int32_t *token_idx, float *out, float *lse_opt, void *ws,
                       size_t ws_bytes, void *stream);

@@ -19,8 +19,9 @@
 //     probabilities cross from the MFMA layout through LDS.
 // The 4 waves merge their (m, l, o) in LDS and the workgroup writes one
 // partial. k_merge then combines the splits of every head -- except after
-// k_attend_pv, whose last workgroup of each (pair, head tile) merges the
-// splits itself: every workgroup stores its partial with agent-scope atomic
+// k_attend_pv launched as a single round of workgroups (at most two per CU),
+// whose last workgroup of each (pair, head tile) merges the splits itself
+// instead: every workgroup stores its partial with agent-scope atomic
 // stores, waits for them and counts itself in with an agent-scope atomic add
 // (a counter per group at the start of the workspace); the workgroup that
 // completes the count loads the partials with agent-scope atomic loads,
