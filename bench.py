@@ -69,15 +69,43 @@ def attention_kernel(s):
     return "k_attend_gqa" if s.D <= 128 else "k_attend"
 
 
+def source_code(text):
+    """C/C++ source text without its comments, every run of white space
+    shown as one blank (string and character literals otherwise kept): what
+    a counter summary depends on."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha():
-    """Digest of every kernel source (the .hip files and their device headers):
-    a counter summary is valid only for the sources it was taken with."""
+    """Digest of every kernel source (the .hip files, their device headers and
+    the launch header), comments and layout aside: a counter summary is valid
+    only for the code it was taken with."""
     import hashlib
     h = hashlib.sha256()
     csrc = ROOT / "two_level_sparse_amd" / "csrc"
-    for f in sorted(list(csrc.glob("*.hip")) + list(csrc.glob("*_dev.h")) + [csrc / "tls_dev.h"]):
+    files = list(csrc.glob("*.hip")) + list(csrc.glob("*_dev.h")) + [csrc / "tls_dev.h", csrc / "tls_launch.h"]
+    for f in sorted(set(files)):
         h.update(f.name.encode())
-        h.update(f.read_bytes())
+        h.update(source_code(f.read_text()).encode())
     return h.hexdigest()[:16]
 
 
