@@ -547,6 +547,23 @@ __device__ __forceinline__ void score_unit(float (&val)[UT / 4], int (&cand)[UT 
   }
 }
 
+// Pair and unit group of a workgroup of a (unit groups, pairs) grid.
+// Workgroups are dealt to the 8 XCDs in turn (linear id mod 8); when the pair
+// count allows, all of pair p's workgroups land on XCD p mod 8, so that its
+// block-score row, label channels and q are fetched into one L2 only.
+__device__ __forceinline__ void pair_and_unit(int& p, int& ux) {
+  const int nx = (int)gridDim.x;
+  if (gridDim.y % 8 == 0) {
+    const int l = (int)blockIdx.y * nx + (int)blockIdx.x;
+    const int slot = l / 8;
+    p = l % 8 + 8 * (slot / nx);
+    ux = slot % nx;
+  } else {
+    p = (int)blockIdx.y;
+    ux = (int)blockIdx.x;
+  }
+}
+
 template <int MT, int RB, int UT, bool FOLD>
 __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict__ q,
                                                       const int32_t* __restrict__ label_ch,
@@ -555,11 +572,12 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
                                                       const int32_t* __restrict__ block_idx, float* __restrict__ A,
                                                       int Hq, int Hkv, int G, int D, int64_t N, int64_t Ns, int bs,
                                                       int bsh, int r, int kb) {
-  const int p = blockIdx.y;
+  int p, ux;
+  pair_and_unit(p, ux);
   const int b = p / Hkv, h = p % Hkv;
   const int wave = threadIdx.x >> 6;
   const int ncand = kb * bs, rb = r / 2;
-  const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  const int c0 = ux * (4 * UT * 16) + wave * (UT * 16);
   const int32_t* lab = label_ch + (int64_t)h * r;
   const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
   __shared__ __align__(16) uint16_t sq[MT * 16 * kLabRow];
@@ -599,7 +617,9 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   __shared__ TopkLds<256> sh;
   __shared__ uint32_t stage[256 * PERB];
   __shared__ int32_t sblk[kSelMaxBlocks];
-  const int p = blockIdx.y, tid = threadIdx.x;
+  int p, ux;
+  pair_and_unit(p, ux);
+  const int tid = threadIdx.x;
   const int b = p / Hkv, h = p % Hkv;
   const int wave = tid >> 6;
   const int ncand = kb * bs, rb = r / 2;
@@ -626,9 +646,9 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
     block_topk<PERB, 256>(key, id, (uint32_t)kb, sblk, kb, sh, stage);
   }
   lds_sync();
-  if (blockIdx.x == 0)
+  if (ux == 0)
     for (int i = tid; i < kb; i += 256) block_idx[(int64_t)p * kb + i] = sblk[i];
-  const int c0 = blockIdx.x * (4 * UT * 16) + wave * (UT * 16);
+  const int c0 = ux * (4 * UT * 16) + wave * (UT * 16);
   u32x4 qa[MT];
   label_q_finish<MT, FOLD>(qa, hl, sq, r);
   float val[UT / 4];
