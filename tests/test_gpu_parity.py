@@ -92,6 +92,11 @@ SMALL = {
     # latent attention on MFMA: a half-empty second head group, 16 splits of one tile
     "mla_g48": W.small_shape(B=1, Hq=48, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=3000, bs=32, r=32,
                              Kb=20, Kt=500, n_outlier=0),
+    # pair counts that are a multiple of 8: the token scorers place all of a
+    # pair's workgroups on one XCD (their pair/unit mapping is permuted)
+    "pairs8_gqa": W.small_shape(B=4, Hq=16, Hkv=2, N=3000, bs=64, Kb=10, Kt=300),
+    "pairs8_mla": W.small_shape(B=8, Hq=128, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=1000, bs=64, r=32,
+                                Kb=6, Kt=200, n_outlier=0),
     # few heads on the 576-wide rows: the vector attention kernel
     "mla_g8": W.small_shape(B=2, Hq=8, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=1500, bs=64, r=32,
                             Kb=6, Kt=200, n_outlier=0),
