@@ -175,8 +175,14 @@ def block_scorer_mfma(s, dec, qs, caches, stream, reps=20):
     import two_level_sparse_amd as T
     flops = 2.0 * s.G * s.NB * 2 * s.D * s.pairs
     summ_bytes = s.pairs * s.NB * 2 * s.D * 2
+    # the GEMM's roofline: with its operands (summaries, q) and scores moved
+    # through HBM at the peak rate, the products keep MFMA busy at most
+    # (flop per byte) / (peak flop/s / peak byte/s) of the launch
+    per_byte = flops / (summ_bytes + s.B * s.Hq * s.D * 2 + s.pairs * s.NB * 4)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     out = {"kernel": "k_score_blocks_lds" if s.G > 48 else "k_score_blocks", "flops": flops,
-           "bytes": summ_bytes, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+           "bytes": summ_bytes, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "flop_per_byte": round(per_byte, 1),
+           "mfma_util_bound_at_hbm_peak": round(min(1.0, per_byte / ridge), 4)}
     for mode in ("cold", "warm"):
         evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         torch.cuda._sleep(int(2e7))  # the host queues every call before the GPU starts them
