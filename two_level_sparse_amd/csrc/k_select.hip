@@ -33,32 +33,22 @@ namespace tls {
 
 // ----------------------------------------------------------- block scores --
 
-// Streaming scorer for small head groups (G <= 48): every summary byte is used
-// by at most three 16-row MFMA tiles, so the kernel is a plain HBM stream.
-// Each wave scores 16*NSUB consecutive blocks; the channel loop runs in groups
-// of UNR chunks of 32 channels whose loads (summaries and q fragments) are all
-// issued before the group's MFMAs. KC = D/32 when known at compile time (0:
-// from D at run time, with UNR = 1).
+// The scores of NSUB consecutive 16-block tiles of one pair, from tile T0
+// (a tile past the last is the last again): best[s] is block 16*(T0+s) + n's
+// score in the lanes with kq == 0. The channel loop runs in groups of UNR
+// chunks of 32 channels whose loads (summaries and q fragments) are all issued
+// before the group's MFMAs. qp: the pair's first head row; sp: its summaries.
 template <int MT, int NSUB, int KC, int UNR>
-__global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ summ, float* __restrict__ S,
-                                                      int Hq, int Hkv, int G, int D, int64_t NB, int64_t NBs) {
-  const int p = blockIdx.y;
-  const int b = p / Hkv, h = p % Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void block_tile_scores(float (&best)[NSUB], const uint16_t* qp, const uint16_t* sp,
+                                                  int64_t T0, int64_t NB, int G, int D) {
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, kq = lane >> 4;
-  const int64_t jbase = ((int64_t)blockIdx.x * 4 + wave) * (16 * NSUB);
-  if (jbase >= NB) return;
-  const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
   const int kc = KC > 0 ? KC : D / 32;
-  const uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
-
-  // the wave's tiles in tile-fragment order (a tile past the last is the last
-  // again; its scores are not stored): lane L reads elements 8L .. 8L+7 of a unit
+  // the tiles in tile-fragment order: lane L reads elements 8L .. 8L+7 of a unit
   const uint16_t* brow[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    const int64_t T = min(jbase / 16 + s, summ_tiles(NB) - 1);
+    const int64_t T = min(T0 + s, summ_tiles(NB) - 1);
     brow[s] = sp + summ_unit(T, 0, 0, kc) + 8 * lane;
   }
   const uint16_t* qrow[MT];
@@ -100,15 +90,38 @@ __global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict
   }
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    float best = -INFINITY;
+    float b = -INFINITY;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (m * 16 + 4 * kq + i < G) best = fmaxf(best, acc[m][s][i]);
-    best = max_rows(best);
+        if (m * 16 + 4 * kq + i < G) b = fmaxf(b, acc[m][s][i]);
+    best[s] = max_rows(b);
+  }
+}
+
+// Streaming scorer for small head groups (G <= 48): every summary byte is used
+// by at most three 16-row MFMA tiles, so the kernel is a plain HBM stream.
+// Each wave scores 16*NSUB consecutive blocks (block_tile_scores). KC = D/32
+// when known at compile time (0: from D at run time, with UNR = 1).
+template <int MT, int NSUB, int KC, int UNR>
+__global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ summ, float* __restrict__ S,
+                                                      int Hq, int Hkv, int G, int D, int64_t NB, int64_t NBs) {
+  const int p = blockIdx.y;
+  const int b = p / Hkv, h = p % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, kq = lane >> 4;
+  const int64_t jbase = ((int64_t)blockIdx.x * 4 + wave) * (16 * NSUB);
+  if (jbase >= NB) return;
+  const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
+  const uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
+  float best[NSUB];
+  block_tile_scores<MT, NSUB, KC, UNR>(best, qp, sp, jbase / 16, NB, G, D);
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
     const int64_t j = jbase + s * 16 + n;
-    if (kq == 0 && j < NB) S[(int64_t)p * NB + j] = best;
+    if (kq == 0 && j < NB) S[(int64_t)p * NB + j] = best[s];
   }
 }
 
@@ -604,19 +617,32 @@ __global__ __launch_bounds__(256) void k_score_tokens(const uint16_t* __restrict
 // is repeated by the pair's few scoring workgroups instead of costing a launch
 // of its own, which would keep all but one workgroup per pair of the chip idle.
 constexpr int kSelMaxBlocks = 4096;  // block-score row per workgroup: 16 per thread
+// BSC: the workgroups compute their pair's block scores themselves from the
+// summaries (block_tile_scores, the arithmetic of k_score_blocks, so the same
+// scores) instead of reading them from S: one head tile, 128 channels, at most
+// kSelScoreMaxBlocks blocks, kSelScoreTiles tiles per wave and round. Every
+// scoring workgroup of a pair then reads all of the pair's summaries, which
+// pays while they are few: graph-replayed steps of 4 x 8 pairs (G = 4, Kb =
+// NB/8) took 26.5 / 29.5 / 33.8 / 36.6 us at 128 / 256 / 384 / 512 blocks
+// against 29.5 / 31.7 / 34.2 / 35.7 us with the block scorer's launch.
+constexpr int kSelScoreMaxBlocks = 384;
+constexpr int kSelScoreTiles = 4;
 
-template <int MT, int RB, int UT, int PERB, bool FOLD>
+template <int MT, int RB, int UT, int PERB, bool FOLD, bool BSC>
 __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ label_ch,
                                                           const uint8_t* __restrict__ codes,
                                                           const float* __restrict__ scale,
-                                                          const float* __restrict__ S, int NB,
+                                                          const float* __restrict__ S,
+                                                          const uint16_t* __restrict__ summ, int NB, int64_t NBs,
                                                           int32_t* __restrict__ block_idx, float* __restrict__ A,
                                                           int Hq, int Hkv, int G, int D, int64_t N, int64_t Ns, int bs,
                                                           int bsh, int r, int kb) {
+  static_assert(!BSC || (MT == 1 && PERB * 256 >= kSelScoreMaxBlocks), "block scores inside: one head tile");
   __shared__ TopkLds<256> sh;
   __shared__ uint32_t stage[256 * PERB];
   __shared__ int32_t sblk[kSelMaxBlocks];
+  __shared__ float srow[BSC ? kSelScoreMaxBlocks : 1];
   int p, ux;
   pair_and_unit(p, ux);
   const int tid = threadIdx.x;
@@ -631,10 +657,32 @@ __global__ __launch_bounds__(256) void k_score_tokens_sel(const uint16_t* __rest
   {
     const int per = (NB + 255) / 256;
     float v[PERB];
-    load_row_f32<PERB>(S + (int64_t)p * NB, NB, tid * per, v);
     const int32_t* lab = label_ch + (int64_t)h * r;
     const uint16_t* qp = q + ((int64_t)b * Hq + (int64_t)h * G) * D;
-    label_q_issue<MT>(hl, lab, qp, G, D, r);
+    if constexpr (BSC) {
+      label_q_issue<MT>(hl, lab, qp, G, D, r);
+      // wave w scores tiles 4w .. 4w+3, then 16 further on, ...
+      const uint16_t* sp = summ + (int64_t)p * summ_pair_elems(NBs, D);
+      const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), ntiles = (NB + 15) / 16;
+      for (int t0 = wv * kSelScoreTiles; t0 < ntiles; t0 += 4 * kSelScoreTiles) {
+        float best[kSelScoreTiles];
+        block_tile_scores<1, kSelScoreTiles, 4, 4>(best, qp, sp, t0, NB, G, D);
+#pragma unroll
+        for (int s = 0; s < kSelScoreTiles; ++s) {
+          const int j = (t0 + s) * 16 + (tid & 15);
+          if ((tid & 63) < 16 && j < NB) srow[j] = best[s];
+        }
+      }
+      lds_sync();
+#pragma unroll
+      for (int e = 0; e < PERB; ++e) {
+        const int c = tid * per + e;
+        v[e] = (e < per && c < NB) ? srow[c] : 0.0f;
+      }
+    } else {
+      load_row_f32<PERB>(S + (int64_t)p * NB, NB, tid * per, v);
+      label_q_issue<MT>(hl, lab, qp, G, D, r);
+    }
     uint32_t key[PERB];
     int32_t id[PERB];
 #pragma unroll
@@ -852,9 +900,9 @@ static void go_score_tokens_sel_ut(const TokenSelectArgs& a, const float* S, int
   const int ncand = a.kb * a.bs;
   dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
 #define TLS_GO(PB, F)                                                                                               \
-  hipLaunchKernelGGL((k_score_tokens_sel<MT, RB, UT, PB, F>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes,    \
-                     a.scale, S, NB, block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, log2_or_neg(a.bs), a.r, \
-                     a.kb)
+  hipLaunchKernelGGL((k_score_tokens_sel<MT, RB, UT, PB, F, false>), grid, dim3(256), 0, st, a.q, a.label_ch,      \
+                     a.codes, a.scale, S, nullptr, NB, (int64_t)0, block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs, \
+                     log2_or_neg(a.bs), a.r, a.kb)
   if constexpr (MT == 1 && (RB == 4 || RB == 8)) {
     if (fold_ok<MT, RB>(a)) {
       if (NB <= 256 * 8)
@@ -941,6 +989,53 @@ hipError_t launch_select_fused(const TokenSelectArgs& a, const float* S, int NB,
     case 7: go_score_tokens_sel_rb<7>(a, S, NB, block_idx, A, st); break;
     case 8: go_score_tokens_sel_rb<8>(a, S, NB, block_idx, A, st); break;
     default: return hipErrorInvalidValue;
+  }
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_topk_tokens(a, A, st);
+}
+
+bool select_scores_inside_ok(int G, int D, int NB, int kb) {
+  return G <= 16 && D == 128 && NB <= kSelScoreMaxBlocks && kb <= NB;
+}
+
+template <int RB, int UT>
+static void go_select_from_summaries(const TokenSelectArgs& a, const uint16_t* summ, int NB, int64_t NBs,
+                                     int32_t* block_idx, float* A, hipStream_t st) {
+  const int ncand = a.kb * a.bs;
+  dim3 grid((unsigned)((ncand + 64 * UT - 1) / (64 * UT)), (unsigned)a.pairs);
+#define TLS_GO(F)                                                                                                  \
+  hipLaunchKernelGGL((k_score_tokens_sel<1, RB, UT, 8, F, true>), grid, dim3(256), 0, st, a.q, a.label_ch, a.codes, \
+                     a.scale, nullptr, summ, NB, NBs, block_idx, A, a.Hq, a.Hkv, a.G, a.D, a.N, a.Ns, a.bs,         \
+                     log2_or_neg(a.bs), a.r, a.kb)
+  if constexpr (RB == 4 || RB == 8) {
+    if (fold_ok<1, RB>(a)) {
+      TLS_GO(true);
+      return;
+    }
+  }
+  TLS_GO(false);
+#undef TLS_GO
+}
+
+template <int RB>
+static void go_select_from_summaries_ut(const TokenSelectArgs& a, const uint16_t* summ, int NB, int64_t NBs,
+                                        int32_t* block_idx, float* A, hipStream_t st) {
+  // the unit size of go_score_tokens_sel for one head tile
+  const int64_t wgs = (int64_t)((a.kb * a.bs + 1023) / 1024) * a.pairs;
+  if (wgs < 256)
+    go_select_from_summaries<RB, 8>(a, summ, NB, NBs, block_idx, A, st);
+  else
+    go_select_from_summaries<RB, 16>(a, summ, NB, NBs, block_idx, A, st);
+}
+
+hipError_t launch_select_from_summaries(const TokenSelectArgs& a, const uint16_t* summ, int NB, int64_t NBs,
+                                        int32_t* block_idx, float* A, hipStream_t st) {
+  if (!select_scores_inside_ok(a.G, a.D, NB, a.kb)) return hipErrorInvalidValue;
+  switch (a.r) {
+    case 8: go_select_from_summaries_ut<4>(a, summ, NB, NBs, block_idx, A, st); break;
+    case 16: go_select_from_summaries_ut<8>(a, summ, NB, NBs, block_idx, A, st); break;
+    case 32: go_select_from_summaries_ut<16>(a, summ, NB, NBs, block_idx, A, st); break;
+    default: go_select_from_summaries_ut<0>(a, summ, NB, NBs, block_idx, A, st); break;
   }
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : launch_topk_tokens(a, A, st);

@@ -273,15 +273,20 @@ int tls_select(const tls_shape_t* shape, const void* q, const void* summ, const 
   hipStream_t st = (hipStream_t)stream;
   float* S = (float*)ws;
   float* A = (float*)((char*)ws + ws_bytes(d, TLS_WS_BLOCKS));
+  TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
+                    d.bs, d.r, d.kb, d.kt, d.N, d.Ns};
+  hipError_t e;
+  if (select_scores_inside_ok(d.G, d.D, (int)d.NB, d.kb)) {  // few blocks: no block-scorer launch
+    e = launch_select_from_summaries(a, (const uint16_t*)summ, (int)d.NB, d.NBs, block_idx, A, st);
+    return e == hipSuccess ? TLS_OK : hip_error(e, "select (block scores in the token stage) launch");
+  }
   BlockScoreArgs sa{(const uint16_t*)q, (const uint16_t*)summ, S, d.pairs, d.Hq, d.Hkv, d.G, d.D, d.NB, d.NBs};
   const hipEvent_t pb = g_prof_start[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
   const hipEvent_t pe = g_prof_end[TLS_PROFILE_BLOCK_SCORES].load(std::memory_order_relaxed);
   if (pb) (void)hipEventRecord(pb, st);
-  hipError_t e = launch_score_blocks(sa, st);
+  e = launch_score_blocks(sa, st);
   if (pe) (void)hipEventRecord(pe, st);
   if (e != hipSuccess) return hip_error(e, "score_blocks launch");
-  TokenSelectArgs a{(const uint16_t*)q, label_ch, codes, scale, block_idx, token_idx, d.pairs, d.Hq, d.Hkv, d.G, d.D,
-                    d.bs, d.r, d.kb, d.kt, d.N, d.Ns};
   if (select_fused_ok((int)d.NB, d.kb)) {
     e = launch_select_fused(a, S, (int)d.NB, block_idx, A, st);
     return e == hipSuccess ? TLS_OK : hip_error(e, "select (fused token stage) launch");

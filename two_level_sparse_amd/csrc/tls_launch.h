@@ -59,6 +59,14 @@ hipError_t launch_select_tokens(const TokenSelectArgs& a, float* ws /* token_ws_
 bool select_fused_ok(int NB, int kb);
 hipError_t launch_select_fused(const TokenSelectArgs& a, const float* S, int NB, int32_t* block_idx,
                                float* ws /* token_ws_bytes */, hipStream_t st);
+// The same with the block scores computed by the token-scoring workgroups
+// themselves from the summaries (the arithmetic of launch_score_blocks, so the
+// same block sets): for few blocks per pair, where every workgroup reading its
+// pair's summaries again costs less than a launch of the block scorer. Only
+// where select_scores_inside_ok(G, D, NB, kb).
+bool select_scores_inside_ok(int G, int D, int NB, int kb);
+hipError_t launch_select_from_summaries(const TokenSelectArgs& a, const uint16_t* summ, int NB, int64_t NBs,
+                                        int32_t* block_idx, float* ws /* token_ws_bytes */, hipStream_t st);
 
 // Exact top-K per row of S ([rows, n] float); ids are column numbers.
 hipError_t launch_topk_blocks(const float* S, int rows, int n, int K, int32_t* out, hipStream_t st);
