@@ -92,6 +92,11 @@ SMALL = {
     # latent attention on MFMA: a half-empty second head group, 16 splits of one tile
     "mla_g48": W.small_shape(B=1, Hq=48, Hkv=1, D=576, DV=512, v_is_k_prefix=True, N=3000, bs=32, r=32,
                              Kb=20, Kt=500, n_outlier=0),
+    # tls_select scoring the blocks inside the token stage at its limit (384
+    # blocks per pair), and one token past it (385 blocks, the last holding
+    # one token: the separate block scorer)
+    "nb_384_inside": W.small_shape(B=1, Hq=16, Hkv=2, N=384 * 64, bs=64, Kb=40, Kt=1000),
+    "nb_385_ragged": W.small_shape(B=1, Hq=16, Hkv=2, N=384 * 64 + 1, bs=64, Kb=40, Kt=1000),
     # pair counts that are a multiple of 8: the token scorers place all of a
     # pair's workgroups on one XCD (their pair/unit mapping is permuted)
     "pairs8_gqa": W.small_shape(B=4, Hq=16, Hkv=2, N=3000, bs=64, Kb=10, Kt=300),
