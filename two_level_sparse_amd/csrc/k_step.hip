@@ -277,7 +277,7 @@ __device__ __attribute__((noinline)) void item_cut(ArgsP a0, int p) {
   uint32_t mine = 0u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) mine += hb[j][0] + hb[j][1] + hb[j][2] + hb[j][3];
-  const uint32_t pre = block_exclusive_scan(mine, s_scan);
+  const uint32_t pre = block_exclusive_scan<4>(mine, s_scan);
   if (tid == 255) bc[0] = pre + mine;  // every kept-able key
   lds_sync();
   const uint32_t total = bc[0];
@@ -307,7 +307,7 @@ __device__ __attribute__((noinline)) void item_cut(ArgsP a0, int p) {
         ++nmine;
         kmin = min(kmin, kr[e]);
       }
-    uint32_t at = block_exclusive_scan(nmine, s_scan);
+    uint32_t at = block_exclusive_scan<4>(nmine, s_scan);
 #pragma unroll
     for (int e = 0; e < PERT; ++e)
       if (kr[e] != 0u && (kr[e] >> kHistShift) == d) list[at++] = kr[e];
@@ -384,7 +384,7 @@ __device__ __attribute__((noinline)) void item_attend(ArgsP a0, int p, int v) {
     gt += k[e] > thr ? 1u : 0u;
     eq += (k[e] == thr && k[e] != 0u) ? 1u : 0u;
   }
-  const uint32_t pre = block_exclusive_scan(gt | (eq << 16), s_scan);
+  const uint32_t pre = block_exclusive_scan<4>(gt | (eq << 16), s_scan);
   uint32_t eq_before = eqb + (pre >> 16);
   uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem) - min(eqb, krem);
   int32_t* ti = a->token_idx + (int64_t)p * kt + off;

@@ -25,42 +25,71 @@ __device__ __forceinline__ void split_sign(u32x4 raw, u32x4& pos, u32x4& neg) {
 constexpr int kTopkThreads = 1024;  // the largest workgroup: 16 keys per thread up to 16384
 constexpr int kTopkChunk = 16384;   // the most keys one workgroup selects from
 
+// Bins of the first (linear) pass: 1024 for the large rows of 512- and
+// 1024-thread workgroups, so that the bin holding the cut keeps few keys.
+template <int NT>
+constexpr int topk_bins1() { return NT >= 512 ? 1024 : 256; }
+constexpr int kTopkFew = 64;  // a bin of at most this many keys is resolved by every wave alone
+
 template <int NT>
 struct alignas(16) TopkLds {
-  uint32_t hist[3][256];  // pass i counts into hist[i % 3]
+  uint32_t hist0[topk_bins1<NT>()];  // first pass; later passes rotate hist0, hist[0], hist[1]
+  uint32_t hist[2][256];
   uint32_t red[3][NT / 64];
-  uint32_t scan[NT / 64];
+  alignas(16) uint32_t scan[NT / 64];
+  uint32_t few[kTopkFew];  // keys of a bin with few keys
+  uint32_t nfew;
+  __device__ __forceinline__ uint32_t* buf(int i) { return i == 0 ? hist0 : hist[i - 1]; }
 };
 
-// Block-wide exclusive scan of one uint32 per thread; returns the prefix.
+// Block-wide exclusive scan of one uint32 per thread of NW waves; returns
+// the prefix. Every wave reads all NW wave totals at once and adds those of
+// the waves before it (a loop up to the wave's own index would make the last
+// wave wait for NW-1 LDS round trips in turn).
+template <int NW>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh /* one per wave */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wave] = x;
   lds_sync();
+  uint32_t tot[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot[w] = sh[w];
   uint32_t before = 0u;
-  for (int w = 0; w < wave; ++w) before += sh[w];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) before += w < wave ? tot[w] : 0u;
   return before + x - v;
 }
 
-// The bin of a 256-bin histogram that holds the krem-th largest key: every
-// wave reads the whole histogram and finds it on its own (wave-uniform
-// results, no LDS round trip). Lane l holds bins 255-4l .. 252-4l, so an
-// exclusive prefix scan over lanes counts the keys in the bins above.
+// The bin of an NBINS-bin histogram (NBINS = 256 or 1024) that holds the
+// krem-th largest key: every wave reads the whole histogram and finds it on
+// its own (wave-uniform results, no LDS round trip). Lane l holds the NBINS/64
+// bins below NBINS - NBINS/64*l, so an exclusive prefix scan over lanes counts
+// the keys in the bins above.
 struct BinPick {
   uint32_t bin, above, count;
 };
+template <int NBINS = 256>
 __device__ __forceinline__ BinPick pick_bin(const uint32_t* hist, uint32_t krem) {
+  constexpr int PB = NBINS / 64;
   const int lane = threadIdx.x & 63;
-  const int b0 = 252 - 4 * lane;
-  const u32x4 hb = *reinterpret_cast<const u32x4*>(&hist[b0]);
-  const uint32_t mine = hb[0] + hb[1] + hb[2] + hb[3];
+  const int b0 = NBINS - PB * (lane + 1);
+  uint32_t hb[PB];
+#pragma unroll
+  for (int i = 0; i < PB; i += 4) {
+    const u32x4 h4 = *reinterpret_cast<const u32x4*>(&hist[b0 + i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hb[i + e] = h4[e];
+  }
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int i = 0; i < PB; ++i) mine += hb[i];
   const uint32_t above = wave_incl_scan(mine) - mine;
   const uint64_t hit = __ballot(above < krem && krem <= above + mine);
-  const int L = __builtin_ctzll(hit);  // the lane whose 4 bins hold it (one exists: krem <= keys in range)
+  const int L = __builtin_ctzll(hit);  // the lane whose bins hold it (one exists: krem <= keys in range)
   uint32_t bin = 0u, ab = 0u, cnt = 0u, run = above;
 #pragma unroll
-  for (int i = 3; i >= 0; --i) {
+  for (int i = PB - 1; i >= 0; --i) {
     if (run < krem && krem <= run + hb[i]) {  // true for exactly one bin of lane L
       bin = (uint32_t)(b0 + i);
       ab = run;
@@ -111,15 +140,20 @@ struct TopkCut {
 // Radix select. The first pass bins the keys' float values linearly between
 // the smallest and the largest (a monotone map, so a bin holds one interval
 // of keys; binning the raw keys instead would put every float of one binade
-// into a single bin). The later passes histogram (key - lo) >> shift, the next
-// 8 bits below the top set bit of (hi - lo), over the keys left in [lo, hi].
-// The search stops as soon as the chosen bin is taken whole, with the
-// threshold at the bin's lower edge and every key equal to it kept. One
-// barrier per pass: the histograms rotate over three buffers (a buffer is
-// cleared two passes after its last read), and every wave picks the bin.
+// into a single bin). When the bin holding the cut has at most kTopkFew keys,
+// one more pass gathers them into LDS, where the waves share out the search
+// for the cut among them: for gathered key i, gt counts the keys above it and
+// ge those not below it, and the key with gt < krem <= ge is the threshold.
+// Otherwise the
+// later passes histogram (key - lo) >> shift, the next 8 bits below the top
+// set bit of (hi - lo), over the keys left in [lo, hi], and stop as soon as
+// the chosen bin is taken whole, with the threshold at the bin's lower edge
+// and every key equal to it kept. One barrier per pass: the histograms rotate
+// over three buffers (a buffer is cleared two passes after its last read),
+// and every wave picks the bin.
 template <int PER, int NT, class Src>
 __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
-  constexpr int kWaves = NT / 64, NJ = (PER + 3) / 4;
+  constexpr int kWaves = NT / 64, NJ = (PER + 3) / 4, NB1 = topk_bins1<NT>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nval = 0u;
 #pragma unroll
@@ -141,7 +175,11 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
     sh.red[1][wave] = kmax;
     sh.red[2][wave] = nval;
   }
-  for (int i = tid; i < 512; i += NT) sh.hist[i >> 8][i & 255] = 0u;  // buffers 0 and 1
+  for (int i = tid; i < NB1 + 256; i += NT) {  // buffers 0 and 1
+    if (i < NB1) sh.hist0[i] = 0u;
+    else sh.hist[0][i - NB1] = 0u;
+  }
+  if (tid == 0) sh.nfew = 0u;
   lds_sync();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, total = 0u;
 #pragma unroll
@@ -157,62 +195,92 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
     bool done = false;
     int pass = 0;  // histogram buffer = pass % 3; pass p clears buffer (p + 1) % 3
     const float vlo = key_float(lo), vhi = key_float(hi);
-    const float sc = 256.0f / (vhi - vlo);
+    const float sc = (float)NB1 / (vhi - vlo);
     if (hi > lo && sc > 0.0f && sc < INFINITY) {
-      auto bin_of = [&](uint32_t k) { return min((uint32_t)((key_float(k) - vlo) * sc), 255u); };  // in [0, 256]
+      auto bin_of = [&](uint32_t k) { return min((uint32_t)((key_float(k) - vlo) * sc), (uint32_t)(NB1 - 1)); };
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const u32x4 v = src.get4(j);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (v[i] != 0u) atomicAdd(&sh.hist[0][bin_of(v[i])], 1u);
+          if (v[i] != 0u) atomicAdd(&sh.hist0[bin_of(v[i])], 1u);
       }
-      if (tid < 256) sh.hist[2][tid] = 0u;  // (buffer 1 was cleared at the start)
+      if (tid < 256) sh.hist[1][tid] = 0u;  // (buffer 1 was cleared at the start)
       lds_sync();
-      const BinPick pk = pick_bin(sh.hist[0], krem);
+      const BinPick pk = pick_bin<NB1>(sh.hist0, krem);
       pass = 1;
       const uint32_t d = pk.bin;
       krem -= pk.above;
-      // keys of bin d: one interval [lo, hi] (a block reduction; its barrier
-      // also orders this pass's histogram reads before buffer 0 is cleared)
-      kmin = 0xFFFFFFFFu;
-      kmax = 0u;
+      if (pk.count <= (uint32_t)kTopkFew) {
+        // gather the bin's keys (its count is known, so no slot overflows)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const u32x4 v = src.get4(j);
+        for (int j = 0; j < NJ; ++j) {
+          const u32x4 v = src.get4(j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v[i] != 0u && bin_of(v[i]) == d) {
-            kmin = min(kmin, v[i]);
-            kmax = max(kmax, v[i]);
+          for (int i = 0; i < 4; ++i)
+            if (v[i] != 0u && bin_of(v[i]) == d) sh.few[atomicAdd(&sh.nfew, 1u)] = v[i];
+        }
+        lds_sync();
+        // lane l holds gathered key l; wave w tests the keys w, w + kWaves, ..
+        // against all of them with two ballots each, and the wave holding the
+        // krem-th largest (1 <= krem <= c) publishes it
+        const uint32_t c = pk.count;
+        const uint32_t k = (uint32_t)lane < c ? sh.few[lane] : 0u;
+        for (uint32_t i = (uint32_t)wave; i < c; i += kWaves) {
+          const uint32_t ki = readlane(k, (int)i);
+          const uint32_t gt = (uint32_t)__builtin_popcountll(__ballot(k > ki));  // empty lanes hold 0 < ki
+          const uint32_t ge = (uint32_t)__builtin_popcountll(__ballot(k >= ki));
+          if (gt < krem && krem <= ge && lane == 0) {  // keys equal to ki all pass and store the same
+            sh.red[0][0] = ki;
+            sh.red[1][0] = krem - gt;  // keys equal to thr to keep, first in element order
           }
-      }
-      kmin = wave_umin(kmin);
-      kmax = wave_umax(kmax);
-      if (lane == 0) {
-        sh.red[0][wave] = kmin;
-        sh.red[1][wave] = kmax;
-      }
-      lds_sync();
-      lo = 0xFFFFFFFFu;
-      hi = 0u;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        lo = min(lo, sh.red[0][w]);
-        hi = max(hi, sh.red[1][w]);
-      }
-      if (krem == pk.count) {
-        // the whole bin is taken: the threshold is its smallest key
-        thr = lo;
-        krem = 0xFFFFFFFFu;
+        }
+        lds_sync();
+        thr = sh.red[0][0];
+        krem = sh.red[1][0];
         done = true;
+      } else {
+        // keys of bin d: one interval [lo, hi] (a block reduction; its barrier
+        // also orders this pass's histogram reads before buffer 0 is cleared)
+        kmin = 0xFFFFFFFFu;
+        kmax = 0u;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const u32x4 v = src.get4(j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v[i] != 0u && bin_of(v[i]) == d) {
+              kmin = min(kmin, v[i]);
+              kmax = max(kmax, v[i]);
+            }
+        }
+        kmin = wave_umin(kmin);
+        kmax = wave_umax(kmax);
+        if (lane == 0) {
+          sh.red[0][wave] = kmin;
+          sh.red[1][wave] = kmax;
+        }
+        lds_sync();
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          lo = min(lo, sh.red[0][w]);
+          hi = max(hi, sh.red[1][w]);
+        }
+        if (krem == pk.count) {
+          // the whole bin is taken: the threshold is its smallest key
+          thr = lo;
+          krem = 0xFFFFFFFFu;
+          done = true;
+        }
       }
     }
     while (!done && hi > lo) {
       const uint32_t diff = hi - lo;
       const int nbits = 32 - __clz(diff);
       const int shift = nbits > 8 ? nbits - 8 : 0;
-      uint32_t* hcur = sh.hist[pass % 3];
+      uint32_t* hcur = sh.buf(pass % 3);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const u32x4 v = src.get4(j);
@@ -220,7 +288,7 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
         for (int i = 0; i < 4; ++i)
           if (v[i] >= lo && v[i] <= hi) atomicAdd(&hcur[(v[i] - lo) >> shift], 1u);
       }
-      if (tid < 256) sh.hist[(pass + 1) % 3][tid] = 0u;  // last read two barriers ago
+      if (tid < 256) sh.buf((pass + 1) % 3)[tid] = 0u;  // last read two barriers ago
       lds_sync();
       const BinPick pk = pick_bin(hcur, krem);
       ++pass;
@@ -267,7 +335,7 @@ __device__ void topk_place(const Src& src, const TopkCut& cut, Ids id, int32_t* 
       eq += (v[i] == thr && v[i] != 0u) ? 1u : 0u;
     }
   }
-  const uint32_t pre = block_exclusive_scan(gt | (eq << 16), sh.scan);
+  const uint32_t pre = block_exclusive_scan<NT / 64>(gt | (eq << 16), sh.scan);
   auto place = [&](bool ids) {
     uint32_t eq_before = pre >> 16;
     uint32_t pos = (pre & 0xFFFFu) + min(eq_before, krem);
