@@ -47,6 +47,48 @@ __device__ __forceinline__ int pv_swz(int r) { return 2 * (r & 7) | ((r >> 3) & 
 // the waves' token rows, c_lds and ml_lds the rescale factors and (m, l) of
 // the four waves. COHERENT: the partial is stored with agent-scope atomic
 // stores (store_agent), for a reader in another workgroup of the same launch.
+// The rows of a wave's tiles (see attend_pv_range), lane L those of its tiles
+// L/16, L/16 + 4, ..: every token (and slot) load of the lane is issued
+// before the first is used, so the list costs one memory round trip, not one
+// per group of four tiles. All MI groups are stored (-1 past the wave's
+// tiles): with the stores under a condition, the compiler made every
+// iteration of the tile loop after it wait for all loads in flight. Returns
+// the lane's smallest valid row (0xFFFFFFFF: none).
+template <bool SMAP, int MI>
+__device__ __forceinline__ uint32_t pv_resolve_rows(int32_t* rw, const int32_t* tix, int ntok, int mt_w,
+                                                 const int32_t* smap, int64_t N, int bs, int slots) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  int tok[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = (lane >> 4) + 4 * i;
+    const int k = (wave + 4 * m) * kPvTile + (lane & 15);
+    tok[i] = m < mt_w && k < ntok ? tix[k] : -1;
+  }
+  int slot[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    slot[i] = 0;
+    if constexpr (SMAP) slot[i] = tok[i] >= 0 && tok[i] < N ? smap[tok[i] / bs] : -1;
+  }
+  uint32_t vmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = (lane >> 4) + 4 * i;
+    int r = -1;
+    if (tok[i] >= 0 && tok[i] < N) {
+      if constexpr (SMAP) {
+        if (slot[i] >= 0 && slot[i] < slots) r = slot[i] * bs + tok[i] % bs;
+      } else {
+        r = tok[i];
+      }
+    }
+    rw[m * kPvTile + (lane & 15)] = r;
+    if (r >= 0) vmin = min(vmin, (uint32_t)r);
+  }
+  return vmin;
+}
+
 template <int HT, bool SMAP, int RPW, bool COHERENT = false>
 __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                 const int32_t* __restrict__ slot_map, const int32_t* tix, int ntok,
@@ -79,25 +121,8 @@ __device__ __forceinline__ void attend_pv_range(const uint16_t* __restrict__ q, 
   const int ntile_all = (ntok + kPvTile - 1) / kPvTile;
   const int mt_w = ntile_all > wave ? (ntile_all - wave + 3) / 4 : 0;  // this wave's tiles
   int32_t* rw = rows[wave];
-  uint32_t vmin = 0xFFFFFFFFu;
-  {
-    const int32_t* smap = SMAP ? slot_map + (int64_t)p * NB : nullptr;
-    for (int m = lane >> 4; m < mt_w; m += 4) {
-      const int k = (wave + 4 * m) * kPvTile + (lane & 15);
-      const int tok = k < ntok ? tix[k] : -1;
-      int r = -1;
-      if (tok >= 0 && tok < N) {
-        if constexpr (SMAP) {
-          const int slot = smap[tok / bs];
-          if (slot >= 0 && slot < slots) r = slot * bs + tok % bs;
-        } else {
-          r = tok;
-        }
-      }
-      rw[m * kPvTile + (lane & 15)] = r;
-      if (r >= 0) vmin = min(vmin, (uint32_t)r);
-    }
-  }
+  const uint32_t vmin = pv_resolve_rows<SMAP, RPW / kPvTile / 4>(rw, tix, ntok, mt_w, SMAP ? slot_map + (int64_t)p * NB : nullptr,
+                                                                 N, bs, slots);
   const uint32_t fbu = wave_umin(vmin);
   const int fb = fbu == 0xFFFFFFFFu ? -1 : (int)fbu;
   const int ntw = fb < 0 ? 0 : mt_w;  // a wave without a valid row has nothing to add
