@@ -199,6 +199,31 @@ def test_integer_ties_are_broken_by_lower_index(seed):
     log(f"[gpu] integer ties seed {seed}: {st}")
 
 
+@pytest.mark.parametrize("keys", ["few_values", "powers_of_two"])
+def test_integer_ties_in_wide_rows(keys):
+    """Exact ties in rows wide enough for the 1024-thread token selection (4800
+    candidates, 1024 first-pass bins). few_values: keys in {-2..2} leave about
+    50 distinct scores, so the bins holding the cuts hold hundreds of equal
+    keys and the radix passes after the first decide. powers_of_two: keys in
+    {0, +-1, +-2, +-4} and q in -6..6 leave 80-200 distinct scores per row;
+    the cut bins then hold 29-77 keys of one or a few values, resolved by the
+    few-key gather where they are at most 64 and by radix passes elsewhere.
+    In both, every label-channel scale is a power of two times 1/7, so equal
+    scores are equal in fp32 and in the oracle's fp64 alike, and the sets must
+    equal the oracle's exactly (lower index wins)."""
+    s = W.small_shape(B=1, Hq=8, Hkv=2, N=16000, bs=16, D=64, DV=64, r=4, Kb=300, Kt=2000)
+    if keys == "few_values":
+        q, kv, lab = inputs(s, int_range=2, seed=7)
+    else:
+        rng = np.random.default_rng(11)
+        q = W.f32_to_bf16_bits(rng.integers(-6, 7, (s.B, s.Hq, s.D)).astype(np.float32))
+        vals = np.array([-4, -2, -1, 0, 1, 2, 4], dtype=np.float32)
+        kv = W.f32_to_bf16_bits(rng.choice(vals, (s.B, s.Hkv, s.N, s.row)))
+        lab = np.stack([np.sort(rng.choice(s.D, s.r, replace=False)) for _ in range(s.Hkv)]).astype(np.int32)
+    st = check_all(s, q, kv, lab, expect_exact=True)
+    log(f"[gpu] integer ties, wide rows ({keys}): {st}")
+
+
 def test_build_exact_ties_round_half_to_even():
     """The label cache built on the GPU for keys whose quotients k / scale are exact
     half-way cases (label absmax 7 * 2^e, so the scale is 2^e): codes round half to
