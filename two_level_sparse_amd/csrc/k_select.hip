@@ -104,8 +104,15 @@ __device__ __forceinline__ void block_tile_scores(float (&best)[NSUB], const uin
 // by at most three 16-row MFMA tiles, so the kernel is a plain HBM stream.
 // Each wave scores 16*NSUB consecutive blocks (block_tile_scores). KC = D/32
 // when known at compile time (0: from D at run time, with UNR = 1).
+// Waves per SIMD the streaming scorer asks of the compiler: one head tile on
+// 128 channels fits in 64 registers, so eight workgroups share a CU and the
+// 128k launch (2048 workgroups) runs as one round instead of seven per CU
+// and a tail; the larger tiles keep the compiler's own choice.
+template <int MT, int KC>
+constexpr int score_blocks_waves() { return MT == 1 && KC > 0 && KC <= 4 ? 8 : 1; }
+
 template <int MT, int NSUB, int KC, int UNR>
-__global__ __launch_bounds__(256) void k_score_blocks(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, (score_blocks_waves<MT, KC>())) void k_score_blocks(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ summ, float* __restrict__ S,
                                                       int Hq, int Hkv, int G, int D, int64_t NB, int64_t NBs) {
   const int p = blockIdx.y;
