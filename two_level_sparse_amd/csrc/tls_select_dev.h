@@ -198,12 +198,15 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
     const float sc = (float)NB1 / (vhi - vlo);
     if (hi > lo && sc > 0.0f && sc < INFINITY) {
       auto bin_of = [&](uint32_t k) { return min((uint32_t)((key_float(k) - vlo) * sc), (uint32_t)(NB1 - 1)); };
+      uint32_t bn[NJ * 4];  // each key's first-pass bin (NB1: no key), kept for the gather below
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const u32x4 v = src.get4(j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v[i] != 0u) atomicAdd(&sh.hist0[bin_of(v[i])], 1u);
+        for (int i = 0; i < 4; ++i) {
+          bn[4 * j + i] = v[i] != 0u ? bin_of(v[i]) : (uint32_t)NB1;
+          if (v[i] != 0u) atomicAdd(&sh.hist0[bn[4 * j + i]], 1u);
+        }
       }
       if (tid < 256) sh.hist[1][tid] = 0u;  // (buffer 1 was cleared at the start)
       lds_sync();
@@ -218,7 +221,7 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
           const u32x4 v = src.get4(j);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (v[i] != 0u && bin_of(v[i]) == d) sh.few[atomicAdd(&sh.nfew, 1u)] = v[i];
+            if (bn[4 * j + i] == d) sh.few[atomicAdd(&sh.nfew, 1u)] = v[i];
         }
         lds_sync();
         // lane l holds gathered key l; wave w tests the keys w, w + kWaves, ..
@@ -249,7 +252,7 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
           const u32x4 v = src.get4(j);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (v[i] != 0u && bin_of(v[i]) == d) {
+            if (bn[4 * j + i] == d) {
               kmin = min(kmin, v[i]);
               kmax = max(kmax, v[i]);
             }
@@ -359,6 +362,7 @@ __device__ void topk_place(const Src& src, const TopkCut& cut, Ids id, int32_t* 
   };
   place(true);
   lds_sync();
+#pragma unroll 4
   for (int i = tid; i < out_len; i += NT) out[i] = i < (int)kk ? (int32_t)stage[i] : -1;
   if (out_key) {
     lds_sync();
