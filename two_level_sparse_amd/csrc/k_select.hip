@@ -735,8 +735,15 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(const float* __restrict__ A,
     const int c = min(tid * PER + e, ncand - 1);
     bq[e] = bsh >= 0 ? (c >> bsh) : c / bs;
   }
+  if (bs % PER == 0) {
+    // the thread's elements lie in one block: one load of its number
+    const int b0 = bidx[bq[0]];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) bid[e] = bidx[bq[e]];
+    for (int e = 0; e < PER; ++e) bid[e] = b0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) bid[e] = bidx[bq[e]];
+  }
   uint32_t key[PER];
   int32_t id[PER];
 #pragma unroll
