@@ -829,7 +829,8 @@ static int log2_or_neg(int bs) { return (bs & (bs - 1)) == 0 ? __builtin_ctz((un
 // Workgroup size for a row of n keys: the fewest threads with at most 8 keys
 // each (up to 16 with 1024 threads). Measured on the 128k workload: 2048
 // block scores 5.1 us on 256 threads vs 5.4 on 1024; 8192 candidates 9.2 us
-// on 1024 vs 9.8 on 512.
+// on 1024 vs 9.8 on 512; 4096 candidates (the 32k and 64k latent steps) on
+// 1024 threads made those steps 0.3-1 us slower than on 512.
 static int topk_threads(int n) { return n <= 256 * 8 ? 256 : n <= 512 * 8 ? 512 : 1024; }
 #define TLS_PER_SWITCH(per, NT, MACRO) \
   if (per <= 1) MACRO(1, NT);          \
