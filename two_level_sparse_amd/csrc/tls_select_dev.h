@@ -29,7 +29,7 @@ constexpr int kTopkChunk = 16384;   // the most keys one workgroup selects from
 // 1024-thread workgroups, so that the bin holding the cut keeps few keys.
 template <int NT>
 constexpr int topk_bins1() { return NT >= 512 ? 1024 : 256; }
-constexpr int kTopkFew = 64;  // a bin of at most this many keys is resolved by every wave alone
+constexpr int kTopkFew = 64;  // a cut bin of at most this many keys is gathered and resolved in LDS
 
 template <int NT>
 struct alignas(16) TopkLds {
@@ -144,13 +144,12 @@ struct TopkCut {
 // one more pass gathers them into LDS, where the waves share out the search
 // for the cut among them: for gathered key i, gt counts the keys above it and
 // ge those not below it, and the key with gt < krem <= ge is the threshold.
-// Otherwise the
-// later passes histogram (key - lo) >> shift, the next 8 bits below the top
-// set bit of (hi - lo), over the keys left in [lo, hi], and stop as soon as
-// the chosen bin is taken whole, with the threshold at the bin's lower edge
-// and every key equal to it kept. One barrier per pass: the histograms rotate
-// over three buffers (a buffer is cleared two passes after its last read),
-// and every wave picks the bin.
+// Otherwise the later passes histogram (key - lo) >> shift, the next 8 bits
+// below the top set bit of (hi - lo), over the keys left in [lo, hi], and stop
+// as soon as the chosen bin is taken whole, with the threshold at the bin's
+// lower edge and every key equal to it kept. One barrier per pass: the
+// histograms rotate over three buffers (a buffer is cleared two passes after
+// its last read), and every wave picks the bin.
 template <int PER, int NT, class Src>
 __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
   constexpr int kWaves = NT / 64, NJ = (PER + 3) / 4, NB1 = topk_bins1<NT>();
@@ -208,7 +207,7 @@ __device__ TopkCut topk_cut(const Src& src, uint32_t K, TopkLds<NT>& sh) {
           if (v[i] != 0u) atomicAdd(&sh.hist0[bn[4 * j + i]], 1u);
         }
       }
-      if (tid < 256) sh.hist[1][tid] = 0u;  // (buffer 1 was cleared at the start)
+      if (tid < 256) sh.hist[1][tid] = 0u;  // buffer 2 (buffer 1 was cleared at the start)
       lds_sync();
       const BinPick pk = pick_bin<NB1>(sh.hist0, krem);
       pass = 1;
